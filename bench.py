@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the planned GEMM on one MI355X.
+
+One step is one dg_gemm call on the int8 4096^3 workload (plan from the
+handle's cache, the tiled MFMA kernel, the fused epilogue): the workload the
+headline throughput is quoted on.  The other workloads (fp16 4096^3, the bf16
+M = 1 and M = 16 long-K GEMMs, the GELU GEMM, the e2m1 GEMMs, the small alpha/beta
+GEMM) are timed after it and reported under "workloads".  Inputs are seeded
+synthetic data drawn on the GPU and resident in HBM before any timing starts.
+
+Timing: HIP events on the stream the kernels run on (torch's current stream),
+bracketing K back-to-back steps after W warm-up steps; ms_per_step is the
+average.  Small HBM-bound workloads rotate through copies of B (>= 576 MB in
+all, twice the L2 + MALL) so that every step reads HBM, and are also reported
+warm; workloads whose kernels are shorter than the host's launch cost are
+replayed from a captured HIP graph (checked against an eager run).
+
+The CPU baseline is the oracle (plain C, binary64 / int64) timed on a bounded
+sample of the headline workload on this host's cores.
+"""
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("TFLOP/s (TOPS int8) at 4096³ + GB/s at M=1 long-K, each as % of MI355X peak")
+PEAK = {"i8": 5033.2, "f16": 2516.6, "bf16": 2516.6, "e2m1": 2516.6}   # dense TOP/s / TFLOP/s
+HBM_PEAK = 8000.0                                                      # GB/s
+CACHE_BYTES = 576 * 10 ** 6       # 2 x (256 MB MALL + 32 MB L2)
+
+HEADLINE = "i8_4096x4096x4096"
+SECONDARY = ["f16_4096x4096x4096", "bf16_1x4096x131072", "bf16_16x4096x131072",
+             "f16_2048x2048x8192_bias_gelu", "e2m1_4096x4096x4096", "e2m1_1x4096x4096",
+             "bf16_1x256x12800", "f16_256x256x256_alpha_beta_d"]
+
+
+def algorithmic(w):
+    """(ops, bytes): 2*M*N*K, and every operand read once plus C written once."""
+    M, N, K = w.M, w.N, w.K
+    ops = 2 * M * N * K
+    ea = 1 if w.path == "i8" else 2
+    eb = {"i8": 1, "e2m1": 0.5}.get(w.path, 2)
+    eo = {"i32": 4, "f32": 4}.get(w.out, 2)
+    b = M * K * ea + K * N * eb + M * N * eo
+    if w.path == "e2m1":
+        b += N * (K // 32) * 2
+    if w.beta != 0:
+        b += M * N * eo
+    if "bias" in w.epilogue:
+        b += N * 2
+    return ops, int(b)
+
+
+class Prepared:
+    """Device operands of one workload and a pre-marshalled dg_gemm call."""
+
+    def __init__(self, h, name, dev, rotate):
+        import torch
+        from tile_planned_generator_amd import dg, synth
+        self.dg = dg
+        self.w = w = synth.make(name, device=dev)
+        t = w.tensors
+        self.torch_out = {"f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}[w.out]
+        self.A = t["A"].contiguous()
+        if w.path == "e2m1":
+            B0 = dg.pack_e2m1(t["codes"])
+            S0 = dg.scales_nk(t["scale"])
+            b_bytes = B0.numel() + S0.numel() * 2
+        else:
+            B0 = t["B"].contiguous()
+            S0 = None
+            b_bytes = B0.numel() * B0.element_size()
+        R = 1
+        if rotate and b_bytes < CACHE_BYTES:
+            R = -(-CACHE_BYTES // b_bytes)
+        self.R = R
+        self.Bs = [B0] + [B0.clone() for _ in range(R - 1)]
+        self.Ss = [S0] + [S0.clone() for _ in range(R - 1)] if S0 is not None else [None] * R
+        self.D = t.get("D") if w.beta != 0 else None
+        self.bias = t.get("bias")
+        self.C = torch.empty(w.M, w.N, dtype=self.torch_out, device=dev)
+        layout = dg.DG_COL_MAJOR if w.path == "e2m1" else dg.DG_ROW_MAJOR
+        a = {"i8": "i8", "e2m1": "f16"}.get(w.path, w.path)
+        b = w.path
+        self.info = h.plan(w.M, w.N, w.K, a, b, w.out, layout, w.epilogue)
+        self.ws = (torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=dev)
+                   if self.info.workspace_bytes else None)
+        self.dt, self.lay = dg.Handle.problem(a, b, w.out, layout)
+        if w.path == "i8":
+            self.al, self.be = C.c_int32(int(w.alpha)), C.c_int32(int(w.beta))
+        else:
+            self.al, self.be = C.c_float(w.alpha), C.c_float(w.beta)
+        self.epi = dg.dg_epilogue(dg.EPI[w.epilogue], dg.DTYPE[w.path if w.path != "e2m1" else "f16"]
+                                  if self.bias is not None else 0,
+                                  self.bias.data_ptr() if self.bias is not None else None, 1.0)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.lib = dg.load()
+        self.h = h
+        self.args = []
+        for i in range(R):
+            self.args.append((h.h, w.M, w.N, w.K, C.byref(self.dt), C.byref(self.lay),
+                              self.A.data_ptr(), self.Bs[i].data_ptr(),
+                              self.Ss[i].data_ptr() if self.Ss[i] is not None else None,
+                              32 if w.path == "e2m1" else 0,
+                              self.D.data_ptr() if self.D is not None else None,
+                              self.C.data_ptr(), C.byref(self.al), C.byref(self.be),
+                              C.byref(self.epi), None,
+                              self.ws.data_ptr() if self.ws is not None else None,
+                              self.ws.numel() if self.ws is not None else 0, self.stream))
+
+    def launch(self, i=0):
+        s = self.lib.dg_gemm(*self.args[i % self.R])
+        if s != 0:
+            self.dg.check(s)
+
+
+def time_steps(p, steps, warmup, use_graph):
+    """Average milliseconds per step over `steps` steps (HIP events)."""
+    import torch
+    if use_graph:
+        # a graph of L consecutive steps (cycling through the B copies)
+        L = max(p.R, 20)
+        p.launch(0)
+        torch.cuda.synchronize()
+        eager = p.C.clone()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            p.stream = s.cuda_stream
+            p.args = [a[:-1] + (s.cuda_stream,) for a in p.args]
+            with torch.cuda.graph(g, stream=s):
+                for i in range(L):
+                    p.launch(i)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(max(1, warmup // L)):
+            g.replay()
+        torch.cuda.synchronize()
+        # the graph's result must equal the eager result
+        if not torch.equal(p.C, eager):
+            raise RuntimeError(f"graph replay differs from eager run for {p.w.name}")
+        reps = max(1, -(-steps // L))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * L), reps * L
+    for i in range(warmup):
+        p.launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        p.launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, steps
+
+
+def report(p, ms):
+    ops, byts = algorithmic(p.w)
+    path = p.w.path
+    tflops = ops / (ms * 1e-3) / 1e12
+    gbps = byts / (ms * 1e-3) / 1e9
+    i = p.info
+    bound = "hbm" if p.w.M <= 16 else "mfma"
+    frac = gbps / HBM_PEAK if bound == "hbm" else tflops / PEAK[path]
+    return {"ms": round(ms, 6), "TFLOP/s" if path != "i8" else "TOP/s": round(tflops, 2),
+            "GB/s": round(gbps, 1), "bound": bound, "frac_of_peak": round(frac, 4),
+            "kernel": i.kernel_name.decode(), "split_k": i.split_k,
+            "tile": f"{i.m_tile}x{i.n_tile}", "algorithmic_bytes": byts, "ops": ops}
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle on leading rows of the int8 4096^3 workload; rows grow until
+    about `budget_s` seconds of CPU work."""
+    import oracle
+    from tile_planned_generator_amd import synth
+    w = synth.make(HEADLINE, M=4096)
+    A = w.tensors["A"].numpy()
+    B = w.tensors["B"].numpy()
+    rows, spent = 8, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_int(A[:rows], B)
+        dt = time.perf_counter() - t0
+        if dt * 4 > budget_s or rows >= 4096:
+            break
+        rows = min(4096, rows * 4)
+        spent += dt
+    ops = 2.0 * rows * w.N * w.K
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the int8 4096x4096x4096 GEMM "
+                      f"({rows}x4096x4096 multiply-adds, int64 accumulation), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU: the planned GEMM is a single-GPU kernel here; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tile_planned_generator_amd import dg
+    dev = "cuda:0"
+    torch.cuda.init()
+    h = dg.Handle(0)
+    props = torch.cuda.get_device_properties(0)
+
+    # ---- headline
+    p = Prepared(h, HEADLINE, dev, rotate=False)
+    ms, steps = time_steps(p, args.steps, args.warmup, use_graph=False)
+    head = report(p, ms)
+    ops, _ = algorithmic(p.w)
+    achieved = ops / (ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["i8"],
+                "unit": "TOP/s", "frac": round(achieved / PEAK["i8"], 4), "traffic": None}
+    del p
+    torch.cuda.empty_cache()
+
+    workloads = {HEADLINE: head}
+    if not args.only_headline:
+        for name in SECONDARY:
+            p = Prepared(h, name, dev, rotate=True)
+            small = p.info.est_us < 25
+            ms_w, _ = time_steps(p, max(50, args.steps // 2), args.warmup, use_graph=small)
+            r = report(p, ms_w)
+            if p.R > 1:
+                r["rotated_copies"] = p.R
+                pw = Prepared(h, name, dev, rotate=False)
+                ms_warm, _ = time_steps(pw, max(50, args.steps // 2), args.warmup, use_graph=small)
+                r["warm"] = report(pw, ms_warm)
+                del pw
+            r["graph"] = small
+            workloads[name] = r
+            del p
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC, "value": round(achieved, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "M": 4096, "N": 4096, "K": 4096,
+                   "a": "int8 row-major", "b": "int8 row-major (K x N)", "c": "int32",
+                   "kernel": head["kernel"], "tile": head["tile"], "split_k": head["split_k"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+    h.close()
+
+
+if __name__ == "__main__":
+    main()

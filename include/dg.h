@@ -1,0 +1,243 @@
+/*
+ * dg.h - C ABI of the planned dense GEMM for AMD MI355X (gfx950).
+ *
+ *   C = act( alpha * (A . B) + beta * D + bias )
+ *
+ * Page citations use two keys:
+ *   [overview]  the DeepGEMM overview article (lqnn.cn, mirrored at discosf.com)
+ *   [generator] the DeepGEMM generator article (kwkr.cn)
+ *
+ * The operation is the GEMM whose kernels the pages generate: the
+ * "alpha * C + beta * D" epilogue ([generator] section 3.2, step 3), a bias
+ * vector added in the epilogue ([generator] section 2.2, third layer), a fused
+ * GELU ([overview] section 6.1), 16-bit inputs accumulated in fp32 and cast to
+ * the output type ([overview] section 3.5, second lesson), int8 accumulated in
+ * int32 and converted with round-to-nearest ([overview] section 4.3), and 4-bit
+ * e2m1 weights with fp16 activations ([overview] section 2.2, second layer).
+ * The tile shape, the K schedule (a K step that may change along K) and the
+ * K split are chosen by a host-side constraint planner ([generator] section 2.2,
+ * first layer: shared-memory, register and occupancy inequalities and a
+ * Pareto-optimal set of tile shapes; here re-derived for gfx950's LDS, VGPR/AGPR
+ * budget and MFMA geometry).
+ *
+ * Conventions for every function:
+ *   - Every call returns a dg_status.  On failure, dg_last_error() returns a
+ *     message for the last failing call on the calling thread.  No C++
+ *     exception crosses this interface.  Nothing fails silently: a missing
+ *     operand is DG_ERR_INVALID_ARG (the pages' runtime fails silently when an
+ *     operand is left unbound, [overview] section 5.1, problem 3; this one
+ *     does not).
+ *   - Device buffers (A, B, scales, D, C, bias, workspace) belong to the
+ *     caller and must stay valid until the work enqueued on the stream has
+ *     finished.  The library never allocates device memory, never copies
+ *     between host and device and never synchronises: dg_gemm validates on
+ *     the host, enqueues its kernels on `stream` and returns.
+ *   - A handle is used by one thread at a time; distinct handles are
+ *     independent.  A handle holds only host state: the device description,
+ *     the plan cache.
+ *   - Sizes and leading dimensions are in elements (for e2m1, in 4-bit codes).
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dg_handle_s *dg_handle_t;
+typedef void *dg_stream_t; /* a hipStream_t; NULL is the null stream */
+
+/* Status codes.  The pages' failures map as: "No valid candidate found after
+ * pruning" -> DG_ERR_NO_CANDIDATE; "K dimension not aligned" -> DG_ERR_ALIGNMENT;
+ * "conflicting compute units" -> DG_ERR_CONFLICT; the runtime's
+ * DGMM_ERROR_INVALID_STATE (module/hardware mismatch) -> DG_ERR_INVALID_STATE
+ * ([overview] sections 3.5 and 5.1). */
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = 1,    /* null operand, negative size, bad enum      */
+    DG_ERR_UNSUPPORTED = 2,    /* dtype / layout / epilogue combination       */
+    DG_ERR_ALIGNMENT = 3,      /* K or a leading dimension or pointer alignment */
+    DG_ERR_NO_CANDIDATE = 4,   /* every tile candidate violates a constraint  */
+    DG_ERR_CONFLICT = 5,       /* options that cannot hold together           */
+    DG_ERR_INVALID_STATE = 6,  /* offline/destroyed handle, wrong device      */
+    DG_ERR_WORKSPACE = 7,      /* workspace missing or smaller than planned   */
+    DG_ERR_HIP = 8,            /* a HIP runtime call or kernel launch failed  */
+    DG_ERR_INTERNAL = 9
+} dg_status;
+
+typedef enum { DG_F16 = 0, DG_BF16 = 1, DG_F32 = 2, DG_I8 = 3, DG_I32 = 4, DG_E2M1 = 5 } dg_dtype;
+
+/* DG_ROW_MAJOR: for A, M x K with K contiguous; for B, K x N with N contiguous.
+ * DG_COL_MAJOR: for B only, stored N x K with K contiguous (the e2m1 layout). */
+typedef enum { DG_ROW_MAJOR = 0, DG_COL_MAJOR = 1 } dg_layout;
+
+typedef enum {
+    DG_EPI_NONE = 0,           /* v = alpha*acc + beta*D                         */
+    DG_EPI_BIAS = 1,           /* v = alpha*acc + beta*D + bias[j]               */
+    DG_EPI_GELU_ERF = 2,       /* GELU(alpha*acc + beta*D), erf form             */
+    DG_EPI_BIAS_GELU_ERF = 3,  /* GELU(alpha*acc + beta*D + bias[j])             */
+    DG_EPI_REQUANT_I8 = 4,     /* int path: clamp(rint(f32(acc)*scale + bias[j])) to int8 */
+    DG_EPI_REQUANT_F16 = 5     /* int path: fp16(f32(acc)*scale + bias[j]), nearest-even  */
+} dg_epi_kind;
+
+typedef enum { DG_UNIT_AUTO = 0, DG_UNIT_MFMA = 1, DG_UNIT_VALU = 2 } dg_unit;
+typedef enum { DG_PATH_AUTO = -1, DG_PATH_TILED = 0, DG_PATH_SKINNY = 1 } dg_path;
+
+/* Precision triple plus the accumulator type ([overview] section 2.2, second
+ * layer: a precision scheme {weight, activation, output} is declared, not
+ * guessed).  Supported:
+ *   a=F16  b=F16  c=F16|F32  compute=F32
+ *   a=BF16 b=BF16 c=BF16|F32 compute=F32
+ *   a=I8   b=I8   c=I32      compute=I32   (c=I8 / F16 with the requantise epilogues)
+ *   a=F16  b=E2M1 c=F16|F32  compute=F32   (b_scale: one fp16 per group_k codes)
+ * D, when read, has the type of C (I32 for the int path). */
+typedef struct {
+    int32_t a, b, c, compute; /* dg_dtype */
+} dg_dtypes;
+
+/* Leading dimensions in elements; 0 means tightly packed.  A: row-major only.
+ * B: row-major (f16, bf16, i8) or column-major (f16, bf16, i8, and e2m1, where
+ * it is the only layout).  C and D are row-major.  A, B rows (columns for a
+ * column-major B) must start on 16-byte boundaries: base pointers 16-byte
+ * aligned and lda, ldb multiples of 16 bytes. */
+typedef struct {
+    int32_t a, b;             /* dg_layout */
+    int64_t lda, ldb, ldc, ldd;
+} dg_layouts;
+
+/* Epilogue.  bias: device pointer to N elements of bias_type (F16, BF16 or F32;
+ * F32 for the requantise kinds), required by the kinds that name it and
+ * optional for the requantise kinds.  scale: the requantise multiplier. */
+typedef struct {
+    int32_t kind;             /* dg_epi_kind */
+    int32_t bias_type;        /* dg_dtype */
+    const void *bias;
+    float scale;
+} dg_epilogue;
+
+/* Planner options ([overview] section 3.2: constraints such as use_hmma and
+ * sm_mem_limit; section 5.3: use_hmma false for small GEMMs).  Zero-initialised
+ * options mean "planner decides". */
+typedef struct {
+    int32_t force_m_tile, force_n_tile, force_k_tile; /* tiled path tile (0 = free)   */
+    int32_t force_split_k;    /* number of K slices (0 = free)                      */
+    int32_t force_path;       /* dg_path; 0 (TILED) is a valid force, so set -1 for free */
+    int32_t unit;             /* dg_unit: MFMA (matrix cores) or VALU (vector FMA)  */
+    int32_t lds_limit_bytes;  /* LDS budget per workgroup (0 = device maximum)      */
+    float target_occupancy;   /* minimum waves per SIMD as a fraction of 8 (0 = 0.125) */
+    int32_t pad_k;            /* reserved: must be 0 (K tails must be MFMA-aligned) */
+} dg_plan_opts;
+
+/* Description of the device the planner plans for.  dg_create fills it from
+ * hipGetDeviceProperties; dg_default_device_desc gives the MI355X table
+ * (the analogue of the pages' per-GPU hardware JSON, [generator] section 3.2,
+ * step 1). */
+typedef struct {
+    char arch[32];            /* "gfx950" */
+    int32_t cu_count;         /* compute units (256)                    */
+    int32_t xcd_count;        /* accelerator dies sharing the CUs (8)   */
+    int32_t simd_per_cu;      /* 4                                      */
+    int32_t wave_size;        /* 64                                     */
+    int32_t lds_bytes_per_cu; /* 163840                                 */
+    int32_t lds_bytes_per_wg; /* largest LDS allocation of one workgroup */
+    int32_t vgpr_per_lane;    /* unified VGPR+AGPR file per SIMD lane (512) */
+    int32_t max_waves_per_simd; /* 8                                    */
+    double clock_ghz;         /* peak engine clock (2.4)                */
+    double hbm_gbps;          /* peak HBM bandwidth, GB/s (8000)        */
+    double l2_bytes_per_xcd;  /* 4 MiB                                  */
+} dg_device_desc;
+
+/* What the planner chose (the pages' "Solution": tile shape and the estimate
+ * behind the choice, [generator] section 3.2, step 2). */
+typedef struct {
+    int32_t path;             /* dg_path */
+    int32_t unit;             /* dg_unit */
+    int32_t mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape (0 on VALU) */
+    int32_t m_tile, n_tile;   /* workgroup tile (skinny path: M rows x N columns) */
+    int32_t k_main, n_main;   /* K schedule of the first K slice: n_main steps of k_main */
+    int32_t k_tail, n_tail;   /* then n_tail steps of k_tail (the smaller tail step) */
+    int32_t split_k;          /* K slices; partials reduced in ascending slice order */
+    int32_t k_slice;          /* K length of every slice but the last */
+    int32_t waves_per_wg;
+    int32_t lds_bytes;        /* LDS per workgroup */
+    int32_t vgpr_est, agpr_est;       /* registers per lane (estimate) */
+    int32_t waves_per_simd;   /* occupancy the estimate allows */
+    int32_t grid;             /* workgroups launched by the main kernel */
+    int64_t workspace_bytes;  /* workspace dg_gemm needs (0 if none) */
+    double est_us;            /* model estimate of the kernel time */
+    double est_roof_fraction; /* roofline time / estimate */
+    int32_t kernel_id;
+    char kernel_name[64];
+} dg_plan_info;
+
+/* Create a handle for HIP device `hip_device`: queries it and checks that it is
+ * a gfx950 (DG_ERR_UNSUPPORTED otherwise, DG_ERR_HIP if the query fails). */
+dg_status dg_create(dg_handle_t *out, int hip_device);
+
+/* Planner-only handle for a described device (no HIP call is made).  dg_gemm on
+ * it returns DG_ERR_INVALID_STATE.  `desc` is copied. */
+dg_status dg_create_offline(dg_handle_t *out, const dg_device_desc *desc);
+
+/* The MI355X description used by dg_create_offline callers and as the fallback
+ * for fields the HIP query does not report. */
+dg_status dg_default_device_desc(dg_device_desc *out);
+
+/* Release a handle (NULL is accepted). */
+dg_status dg_destroy(dg_handle_t h);
+
+/* Plan one problem: enumerate tile candidates, prune by the constraints, score
+ * with a roofline model, keep the Pareto set and pick the fastest estimate
+ * ([generator] section 2.2, first layer; [overview] section 4.1, stage 2).  The
+ * plan is cached in the handle.  `opts` and `out` may be NULL.  Errors:
+ * DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_ALIGNMENT, DG_ERR_CONFLICT,
+ * DG_ERR_NO_CANDIDATE. */
+dg_status dg_plan(dg_handle_t h, int64_t M, int64_t N, int64_t K,
+                  const dg_dtypes *dt, const dg_layouts *lay, int32_t group_k,
+                  int32_t epi_kind, const dg_plan_opts *opts, dg_plan_info *out);
+
+/* The Pareto-optimal candidates (estimated time, LDS bytes, registers), best
+ * first; at most `cap` are written, *count receives how many exist. */
+dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K,
+                             const dg_dtypes *dt, const dg_layouts *lay, int32_t group_k,
+                             int32_t epi_kind, const dg_plan_opts *opts,
+                             dg_plan_info *out, int32_t cap, int32_t *count);
+
+/* Enqueue C = act(alpha*(A.B) + beta*D + bias) on `stream` (the kernel argument
+ * list of the pages' launch, A, B, C, alpha, beta, m, n, k, [generator] section
+ * 3.2, step 4, plus the precision, layout and epilogue description).
+ *   A       device, M x K (lda)
+ *   B       device, K x N row-major (ldb) or N x K column-major (ldb); e2m1: two
+ *           codes per byte, even k in the low nibble, N x K column-major
+ *   b_scale e2m1 only: device fp16, [N][K/group_k] (column n's scales contiguous)
+ *   group_k e2m1 only: 32
+ *   D       device, M x N (ldd); read only when *beta != 0, may be NULL otherwise
+ *   C       device, M x N (ldc)
+ *   alpha, beta  host pointers to compute-type scalars (float for F32 compute,
+ *           int32_t for I32 compute; the requantise kinds need alpha == 1 and
+ *           beta == 0 and use epi->scale)
+ *   epi     NULL means DG_EPI_NONE
+ *   opts    the planner options (NULL: planner decides)
+ *   workspace, workspace_bytes   device scratch of at least the planned
+ *           workspace_bytes (may be NULL when the plan needs none)
+ * Returns after enqueueing; errors in the arguments are reported before
+ * anything is enqueued. */
+dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
+                  const dg_dtypes *dt, const dg_layouts *lay,
+                  const void *A, const void *B, const void *b_scale, int32_t group_k,
+                  const void *D, void *C, const void *alpha, const void *beta,
+                  const dg_epilogue *epi, const dg_plan_opts *opts,
+                  void *workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *dg_last_error(void);
+
+/* Name of a status code. */
+const char *dg_status_str(dg_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,384 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded bits.
+
+Every case draws its inputs with the shared generator, runs ``dg_gemm`` through
+the C ABI (ctypes binding), and compares with the oracle: bit for bit for int8
+-> int32 and the requantise epilogues, within the rule of ``tests/parity.py``
+for floating point.  Small cases span several tiles with ragged edges and
+padded leading dimensions and are checked on every output; the full-size
+workloads run in the launch configuration the benchmark times and are checked
+on sampled rows and columns (the oracle computes those outputs one by one).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import bits, check_fp, out_values, say, tol_for
+from tile_planned_generator_amd import dg, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def h():
+    torch.cuda.init()
+    hd = dg.Handle(0)
+    yield hd
+    hd.close()
+
+
+TORCH_OUT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32,
+             "i32": torch.int32, "i8": torch.int8}
+
+
+def to_dev(t, pad=0):
+    """2-D tensor on the GPU; with pad > 0 the rows are padded (leading dimension
+    = columns + pad) so the kernels see a non-tight leading dimension."""
+    t = t.to(DEV)
+    if pad:
+        buf = torch.zeros(t.shape[0], t.shape[1] + pad, dtype=t.dtype, device=DEV)
+        buf[:, : t.shape[1]] = t
+        return buf[:, : t.shape[1]]
+    return t.contiguous()
+
+
+def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, rows=None,
+        cols=None, requant_scale=1.0, rq_bias=None, alpha=None, beta=None):
+    """Run workload ``w`` through dg_gemm and check it against the oracle on
+    rows x cols (all by default).  Returns (plan info, error stats)."""
+    t = w.tensors
+    M, N, K = w.M, w.N, w.K
+    out = out or w.out
+    epilogue = epilogue or w.epilogue
+    alpha = w.alpha if alpha is None else alpha
+    beta = w.beta if beta is None else beta
+    say(f"[case] {w.name} M={M} N={N} K={K} seed={w.seed} out={out} epi={epilogue} "
+        f"colmajor={b_colmajor} pad={pad} opts={opts and {f: getattr(opts, f) for f, _ in opts._fields_}}")
+    A = to_dev(t["A"], pad)
+    scale = None
+    if w.path == "e2m1":
+        Bd = to_dev(dg.pack_e2m1(t["codes"]), pad)
+        scale = dg.scales_nk(t["scale"]).to(DEV)
+        layout = dg.DG_COL_MAJOR
+    elif b_colmajor:
+        Bd = to_dev(t["B"].t().contiguous(), pad)
+        layout = dg.DG_COL_MAJOR
+    else:
+        Bd = to_dev(t["B"], pad)
+        layout = dg.DG_ROW_MAJOR
+    Cd = to_dev(torch.full((M, N), 7, dtype=TORCH_OUT[out]), pad)
+    D = to_dev(t["D"], pad) if "D" in t and beta != 0 else None
+    bias = t.get("bias")
+    if epilogue in ("requant_i8", "requant_f16"):
+        bias = rq_bias
+    bias = bias.to(DEV) if bias is not None else None
+    info = h.gemm(A, Bd, Cd, alpha=alpha, beta=beta, D=D, bias=bias, epilogue=epilogue,
+                  b_scale=scale, b_layout=layout, opts=opts, requant_scale=requant_scale)
+    torch.cuda.synchronize()
+    say(f"       plan {info.kernel_name.decode()} S={info.split_k} tile={info.m_tile}x{info.n_tile}")
+
+    r_idx = torch.arange(M) if rows is None else torch.as_tensor(rows)
+    c_idx = torch.arange(N) if cols is None else torch.as_tensor(cols)
+    Csub = Cd.cpu()[r_idx][:, c_idx]
+    Ah = t["A"][r_idx.to(t["A"].device)].cpu()
+    if w.path == "i8":
+        Bh = t["B"][:, c_idx.to(t["B"].device)].cpu()
+        Dh = t["D"][r_idx][:, c_idx].cpu() if D is not None else None
+        R, Cw, ov = oracle.gemm_int(Ah.numpy(), Bh.numpy(), alpha=int(alpha), beta=int(beta),
+                                    D=bits(Dh) if Dh is not None else None)
+        if epilogue in ("requant_i8", "requant_f16"):
+            want = oracle.requant(Cw, alpha=requant_scale,
+                                  bias=rq_bias.numpy()[c_idx.numpy()] if rq_bias is not None else None,
+                                  out="i8" if epilogue == "requant_i8" else "f16")
+            got = bits(Csub)
+            assert np.array_equal(got, want), int((got != want).sum())
+            return info, {"bitexact": True}
+        got = Csub.numpy()
+        assert np.array_equal(got, Cw), int((got != Cw).sum())
+        return info, {"bitexact": True, "overflow": ov}
+    a_kind = "f16" if w.path in ("f16", "e2m1") else "bf16"
+    kw = {}
+    if w.path == "e2m1":
+        Bh = bits(t["codes"][:, c_idx.to(t["codes"].device)])
+        kw = dict(scale=bits(t["scale"][:, c_idx.to(t["scale"].device)]), group_k=32)
+        b_kind = "e2m1"
+    else:
+        Bh = bits(t["B"][:, c_idx.to(t["B"].device)])
+        b_kind = a_kind
+    if D is not None:
+        kw.update(D=bits(t["D"][r_idx][:, c_idx]), d_kind=out)
+    if bias is not None:
+        kw.update(bias=bits(t["bias"][c_idx.to(t["bias"].device)]), bias_kind=a_kind)
+    act = 1 if "gelu" in epilogue else 0
+    R = oracle.gemm_real(bits(Ah), Bh, a_kind=a_kind, b_kind=b_kind, alpha=alpha, beta=beta,
+                         act=act, **kw)
+    st = check_fp(Csub, R, tol_for(w.path, out))
+    say(f"       ok {st}")
+    return info, st
+
+
+# ------------------------------------------------------- exact special cases
+def test_identity_and_permutation_are_bit_exact(h):
+    # A . I = A and A . P permutes columns: one non-zero product per output,
+    # exact in fp32, exact in the output type - any operand-layout or
+    # output-layout slip in the MFMA fragments shows up as a wrong element.
+    for dt, kd in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
+        M, K = 96, 192
+        A = synth.to_storage(synth.normal(77, M * K), dt).view(M, K)
+        I = torch.eye(K, dtype=dt)
+        perm = torch.randperm(K, generator=torch.Generator().manual_seed(1))
+        P = I[:, perm].contiguous()          # (A.P)[:, j] = A[:, perm[j]]
+        for colmajor in (False, True):
+            for Bm, want in ((I, A), (P, A[:, perm])):
+                Bd = Bm.t().contiguous().to(DEV) if colmajor else Bm.to(DEV)
+                Cd = torch.empty(M, K, dtype=dt, device=DEV)
+                h.gemm(A.to(DEV), Bd, Cd, b_layout=dg.DG_COL_MAJOR if colmajor else dg.DG_ROW_MAJOR)
+                torch.cuda.synchronize()
+                assert torch.equal(Cd.cpu(), want), (kd, colmajor)
+    # int8: A . P with P a permutation gives A's columns exactly
+    M, K = 64, 256
+    A = synth.int8_uniform(78, M * K).view(M, K)
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(2))
+    P = torch.zeros(K, K, dtype=torch.int8)
+    P[perm, torch.arange(K)] = 1
+    for colmajor in (False, True):
+        Bd = P.t().contiguous().to(DEV) if colmajor else P.to(DEV)
+        Cd = torch.empty(M, K, dtype=torch.int32, device=DEV)
+        h.gemm(A.to(DEV), Bd, Cd, b_layout=dg.DG_COL_MAJOR if colmajor else dg.DG_ROW_MAJOR)
+        torch.cuda.synchronize()
+        assert torch.equal(Cd.cpu(), A[:, perm].to(torch.int32)), colmajor
+
+
+def test_e2m1_one_hot_decode_is_exact(h):
+    # A = one-hot rows selects single weights: C[i][j] = e2m1(code[k_i][j]) *
+    # scale[k_i/32][j]; with power-of-two scales every product is exact in fp16,
+    # so all 16 codes, both nibbles and the group index are checked bit for bit.
+    K, N = 64, 32
+    codes = (torch.arange(K * N, dtype=torch.int64) % 16).to(torch.uint8).view(K, N)
+    codes = codes[torch.randperm(K, generator=torch.Generator().manual_seed(3))]
+    G = K // 32
+    sc = torch.tensor([[2.0 ** (-(g + (j % 5))) for j in range(N)] for g in range(G)],
+                      dtype=torch.float16)
+    M = K
+    A = torch.eye(K, dtype=torch.float16)
+    gold = oracle.e2m1_values(codes.numpy()) * sc.double().numpy()[np.arange(K) // 32]
+    for opts in (dg.dg_plan_opts(force_path=dg.DG_PATH_TILED), None):
+        Cd = torch.empty(M, N, dtype=torch.float16, device=DEV)
+        h.gemm(A.to(DEV), dg.pack_e2m1(codes).to(DEV), Cd, b_scale=dg.scales_nk(sc).to(DEV),
+               opts=opts)
+        torch.cuda.synchronize()
+        assert np.array_equal(Cd.cpu().double().numpy(), gold)
+    # the skinny path (M = 1) on each row of the one-hot
+    for k in (0, 1, 33, 62):
+        Cd = torch.empty(1, N, dtype=torch.float32, device=DEV)
+        h.gemm(A[k:k + 1].contiguous().to(DEV), dg.pack_e2m1(codes).to(DEV), Cd,
+               b_scale=dg.scales_nk(sc).to(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(Cd.cpu().double().numpy()[0], gold[k])
+
+
+def test_rank_one_closed_form_exact(h):
+    # a[i][k] = x_i, b[k][j] = y_j: C = K x_i y_j, exact for small integers
+    M, N, K = 130, 70, 512
+    x = torch.tensor([(i % 7) - 3 for i in range(M)], dtype=torch.float16)
+    y = torch.tensor([(j % 5) - 2 for j in range(N)], dtype=torch.float16)
+    A = x[:, None].expand(M, K).contiguous()
+    B = y[None, :].expand(K, 80).contiguous()[:, :N]
+    Bp = torch.zeros(K, 80, dtype=torch.float16)
+    Bp[:, :N] = B
+    Cd = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    h.gemm(A.to(DEV), Bp.to(DEV)[:, :N], Cd)
+    torch.cuda.synchronize()
+    assert torch.equal(Cd.cpu(), (K * x.float()[:, None] * y.float()[None, :]))
+    # int8 extremes: 127 * -128 * 4096 and (-128)^2 * 4096 = 2^26
+    A = torch.full((40, 4096), 127, dtype=torch.int8)
+    A[20:] = -128
+    B = torch.full((4096, 48), -128, dtype=torch.int8)
+    Cd = torch.empty(40, 48, dtype=torch.int32, device=DEV)
+    h.gemm(A.to(DEV), B.to(DEV), Cd)
+    torch.cuda.synchronize()
+    assert int(Cd[0, 0]) == -66584576 and int(Cd[39, 47]) == 2 ** 26
+
+
+def test_fp16_subnormal_inputs_not_flushed(h):
+    # products of fp16 subnormals with 2^10 land in the normal range: flushing
+    # either operand to zero would give 0
+    M, N, K = 64, 64, 64
+    A = torch.zeros(M, K, dtype=torch.float16)
+    A[:, 0] = torch.tensor(2.0 ** -20, dtype=torch.float16)   # subnormal
+    B = torch.zeros(K, N, dtype=torch.float16)
+    B[0, :] = 1024.0
+    Cd = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    h.gemm(A.to(DEV), B.to(DEV), Cd)
+    torch.cuda.synchronize()
+    assert torch.all(Cd.cpu() == 2.0 ** -10)
+
+
+# --------------------------------------------------------- small full parity
+def test_f16_alpha_beta_d_full_size(h):
+    run(h, synth.make("f16_256x256x256_alpha_beta_d"))
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(257, 263, 272, 8), (300, 129, 1040, 0), (33, 65, 16, 16)])
+def test_f16_alpha_beta_d_ragged(h, M, N, K, pad):
+    w = synth.make("f16_256x256x256_alpha_beta_d", M=M, N=N, K=K)
+    if N % 8 and not pad:
+        pytest.skip("tight rows need 16-byte alignment")
+    run(h, w, pad=pad if pad else 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 384, 640), (300, 200, 96), (129, 257, 4160)])
+@pytest.mark.parametrize("colmajor", [False, True])
+def test_i8_bit_exact_small(h, M, N, K, colmajor):
+    w = synth.make("i8_4096x4096x4096", M=M, N=N, K=K)
+    run(h, w, b_colmajor=colmajor, pad=16 if N % 16 else 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(384, 320, 1024), (130, 200, 2112)])
+def test_f16_bias_gelu_small(h, M, N, K):
+    w = synth.make("f16_2048x2048x8192_bias_gelu", M=M, N=N, K=K)
+    run(h, w, pad=8 if N % 8 else 0)
+    run(h, w, out="f32", pad=8 if N % 8 else 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 1024), (100, 72, 320)])
+@pytest.mark.parametrize("colmajor", [False, True])
+def test_bf16_tiled_small(h, M, N, K, colmajor):
+    w = synth.make("bf16_16x4096x131072", M=M, N=N, K=K)
+    run(h, w, b_colmajor=colmajor)
+    run(h, w, b_colmajor=colmajor, epilogue="gelu_erf", out="f32")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (70, 96, 192)])
+def test_e2m1_tiled_small(h, M, N, K):
+    w = synth.make("e2m1_4096x4096x4096", M=M, N=N, K=K)
+    run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_TILED))
+
+
+def test_every_tiled_variant_on_a_ragged_problem(h):
+    # each compiled tile shape, forced in turn, on a problem with ragged M and N,
+    # a K tail (K = 3 full steps + a partial one) and a K split
+    for path, name, colm in (("f16", "f16_2048x2048x8192_bias_gelu", False),
+                             ("f16", "f16_2048x2048x8192_bias_gelu", True),
+                             ("bf16", "bf16_16x4096x131072", False),
+                             ("i8", "i8_4096x4096x4096", False),
+                             ("i8", "i8_4096x4096x4096", True),
+                             ("e2m1", "e2m1_4096x4096x4096", True)):
+        ktail = 3 * (128 if path == "i8" else 64) + (64 if path == "i8" else 32)
+        w = synth.make(name, M=290, N=272, K=ktail)
+        for bm, bn, occ in ((256, 256, 0.0), (256, 256, 0.25), (256, 128, 0.0), (128, 128, 0.0),
+                            (64, 64, 0.0)):
+            for s in (1, 2):
+                # target occupancy 2/8 selects the 8-wave 256 x 256 variant
+                o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
+                                    force_path=dg.DG_PATH_TILED, target_occupancy=occ)
+                run(h, w, b_colmajor=colm, opts=o)
+
+
+def test_split_k_and_schedule_tail(h):
+    o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_split_k=4)
+    run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=512, N=512, K=2048 + 48), opts=o)
+    run(h, synth.make("i8_4096x4096x4096", M=512, N=512, K=2048 + 96), opts=o)
+    # a K shorter than one full step: only a tail step
+    run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=64, K=16))
+
+
+# ------------------------------------------------------------- skinny paths
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("K", [1024, 2000])
+def test_skinny_valu(h, M, K):
+    for lpr_n in (4096, 1000, 256):
+        w = synth.make("bf16_1x4096x131072", M=M, N=lpr_n, K=K)
+        run(h, w, opts=dg.dg_plan_opts(unit=dg.DG_UNIT_VALU), pad=8 if lpr_n % 8 else 0)
+    w = synth.make("f16_256x256x256_alpha_beta_d", M=M, N=520, K=K)
+    run(h, w, opts=dg.dg_plan_opts(unit=dg.DG_UNIT_VALU, force_split_k=3))
+
+
+@pytest.mark.parametrize("M", [1, 9, 16])
+def test_skinny_mfma(h, M):
+    w = synth.make("bf16_16x4096x131072", M=M, N=1000, K=4128)
+    run(h, w, opts=dg.dg_plan_opts(unit=dg.DG_UNIT_MFMA, force_path=dg.DG_PATH_SKINNY), pad=8)
+    w = synth.make("f16_256x256x256_alpha_beta_d", M=M, N=512, K=1040)
+    run(h, w, opts=dg.dg_plan_opts(unit=dg.DG_UNIT_MFMA, force_path=dg.DG_PATH_SKINNY, force_split_k=5))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 7])
+def test_skinny_e2m1(h, M):
+    for K, S in ((4096, 1), (4096, 4), (1056, 0)):
+        w = synth.make("e2m1_1x4096x4096", M=M, N=300, K=K)
+        run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY, force_split_k=S))
+
+
+def test_config_bf16_1x256x12800_full(h):
+    run(h, synth.make("bf16_1x256x12800"))
+
+
+def test_config_e2m1_1x4096x4096_full(h):
+    run(h, synth.make("e2m1_1x4096x4096"))
+
+
+# ------------------------------------------------------------ epilogues
+def test_requantise_bit_exact(h):
+    w = synth.make("i8_4096x4096x4096", M=130, N=96, K=512)
+    rq_bias = synth.uniform(9, 96, -4, 4).to(torch.float32)
+    for epi in ("requant_i8", "requant_f16"):
+        for s_ in (1.0 / 4096, 3.1e-5):
+            run(h, w, epilogue=epi, out="i8" if epi == "requant_i8" else "f16",
+                requant_scale=s_, rq_bias=rq_bias if epi == "requant_i8" else None)
+        run(h, w, epilogue=epi, out="i8" if epi == "requant_i8" else "f16", requant_scale=1 / 8192,
+            opts=dg.dg_plan_opts(force_split_k=2, force_path=dg.DG_PATH_TILED))
+
+
+def test_int_alpha_beta_d(h):
+    w = synth.make("i8_4096x4096x4096", M=100, N=64, K=256)
+    w.tensors["D"] = synth.int8_uniform(11, 100 * 64).view(100, 64).to(torch.int32) * 1000
+    run(h, w, alpha=3, beta=-2)
+
+
+def test_k_zero_and_empty(h):
+    # K = 0: the sum is empty and C = act(alpha*0 + beta*D + bias)
+    run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=0))
+    run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=40, N=64, K=0))
+    # M = 0 or N = 0: nothing to do, nothing launched
+    Ce = torch.empty(0, 64, dtype=torch.float16, device=DEV)
+    h.gemm(torch.empty(0, 16, dtype=torch.float16, device=DEV),
+           torch.zeros(16, 64, dtype=torch.float16, device=DEV), Ce)
+    torch.cuda.synchronize()
+
+
+def test_errors_on_device_handle(h):
+    A = torch.zeros(64, 64, dtype=torch.float16, device=DEV)
+    B = torch.zeros(64, 64, dtype=torch.float16, device=DEV)
+    Cd = torch.zeros(64, 64, dtype=torch.float16, device=DEV)
+    with pytest.raises(dg.DGError) as e:
+        h.gemm(A, B, Cd, beta=1.0, D=None)
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
+    with pytest.raises(dg.DGError) as e:
+        h.gemm(A, B, Cd, epilogue="bias")
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
+    o = dg.dg_plan_opts(force_split_k=4, force_path=dg.DG_PATH_TILED)
+    with pytest.raises(dg.DGError) as e:
+        h.gemm(A, B, Cd, opts=o, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == dg.DG_ERR_WORKSPACE
+    with pytest.raises(dg.DGError) as e:
+        h.gemm(A[:, 1:], B[1:], Cd, K=63)
+    assert e.value.status == dg.DG_ERR_ALIGNMENT
+
+
+# ------------------------------------------------------ full-size workloads
+def _sample(n, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.randperm(n, generator=g)[:k].sort().values
+    # always include the first and last row/column (tile edges)
+    return torch.unique(torch.cat([idx, torch.tensor([0, n - 1])]))
+
+
+@pytest.mark.parametrize("name", ["i8_4096x4096x4096", "f16_4096x4096x4096",
+                                  "f16_2048x2048x8192_bias_gelu", "e2m1_4096x4096x4096",
+                                  "bf16_1x4096x131072", "bf16_16x4096x131072"])
+def test_full_size_sampled(h, name):
+    w = synth.make(name, device=DEV)
+    rows = _sample(w.M, 48, 5) if w.M > 16 else None
+    cols = _sample(w.N, 96, 6)
+    run(h, w, rows=rows, cols=cols)

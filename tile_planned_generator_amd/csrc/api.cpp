@@ -1,0 +1,457 @@
+// api.cpp - the C ABI (include/dg.h): validation, plan cache, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/dg.h"
+#include "catalogue.h"
+#include "dg_args.h"
+#include "launch.h"
+#include "planner.h"
+
+using namespace dg;
+
+struct dg_handle_s {
+    dg_device_desc desc;
+    int device;   // -1: offline (planner only)
+    std::unordered_map<std::string, Candidate> cache;
+};
+
+namespace {
+
+thread_local std::string g_err;
+std::mutex g_live_mu;
+std::set<const void *> g_live;
+
+dg_status fail(dg_status s, const std::string &msg)
+{
+    g_err = msg;
+    return s;
+}
+
+dg_status ok()
+{
+    return DG_OK;
+}
+
+bool is_live(dg_handle_t h)
+{
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    return h && g_live.count(h);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elt_of(int32_t t)
+{
+    switch (t) {
+    case DG_F16: return T_F16;
+    case DG_BF16: return T_BF16;
+    case DG_F32: return T_F32;
+    case DG_I32: return T_I32;
+    case DG_I8: return T_I8;
+    default: return -1;
+    }
+}
+
+int elt_size(int e) { return (e == T_F16 || e == T_BF16) ? 2 : (e == T_I8 ? 1 : 4); }
+
+// Validate a problem description and build the planner's view of it.
+dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
+                   int32_t group_k, int32_t epi_kind, int beta_nz, Problem &pr)
+{
+    if (!dt) return fail(DG_ERR_INVALID_ARG, "dtypes is NULL");
+    if (M < 0 || N < 0 || K < 0) return fail(DG_ERR_INVALID_ARG, "negative size");
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(DG_ERR_UNSUPPORTED, "sizes above 2^31-1 are not supported");
+    int path;
+    if (dt->a == DG_F16 && dt->b == DG_F16) path = P_F16;
+    else if (dt->a == DG_BF16 && dt->b == DG_BF16) path = P_BF16;
+    else if (dt->a == DG_I8 && dt->b == DG_I8) path = P_I8;
+    else if (dt->a == DG_F16 && dt->b == DG_E2M1) path = P_E2M1;
+    else return fail(DG_ERR_UNSUPPORTED, "unsupported (a, b) dtype pair");
+    const bool is_int = path == P_I8;
+    if (dt->compute != (is_int ? DG_I32 : DG_F32))
+        return fail(DG_ERR_UNSUPPORTED, is_int ? "int8 inputs accumulate in I32" : "16-bit and e2m1 inputs accumulate in F32");
+    if (epi_kind < DG_EPI_NONE || epi_kind > DG_EPI_REQUANT_F16)
+        return fail(DG_ERR_INVALID_ARG, "unknown epilogue kind");
+    const bool rq = epi_kind == DG_EPI_REQUANT_I8 || epi_kind == DG_EPI_REQUANT_F16;
+    if (is_int) {
+        const int want = epi_kind == DG_EPI_NONE ? DG_I32 : (epi_kind == DG_EPI_REQUANT_I8 ? DG_I8 : DG_F16);
+        if (!(epi_kind == DG_EPI_NONE || rq))
+            return fail(DG_ERR_UNSUPPORTED, "the int8 path supports the NONE and requantise epilogues");
+        if (dt->c != want) return fail(DG_ERR_UNSUPPORTED, "output dtype does not match the int8 epilogue");
+        if (rq && beta_nz) return fail(DG_ERR_INVALID_ARG, "requantise epilogues need beta == 0");
+    } else {
+        if (rq) return fail(DG_ERR_UNSUPPORTED, "requantise epilogues need the int8 path");
+        const int own = path == P_BF16 ? DG_BF16 : DG_F16;
+        if (dt->c != own && dt->c != DG_F32)
+            return fail(DG_ERR_UNSUPPORTED, "output dtype must be the input's 16-bit type or F32");
+    }
+    // layouts
+    dg_layouts L{};
+    if (lay) L = *lay;
+    else L.b = path == P_E2M1 ? DG_COL_MAJOR : DG_ROW_MAJOR;
+    if (L.a != DG_ROW_MAJOR) return fail(DG_ERR_UNSUPPORTED, "A must be row-major");
+    if (L.b != DG_ROW_MAJOR && L.b != DG_COL_MAJOR) return fail(DG_ERR_INVALID_ARG, "unknown B layout");
+    if (path == P_E2M1 && L.b != DG_COL_MAJOR)
+        return fail(DG_ERR_UNSUPPORTED, "e2m1 B must be column-major (N x K, K contiguous)");
+    const int64_t lda = L.lda ? L.lda : K;
+    const int64_t ldb = L.ldb ? L.ldb : (L.b == DG_ROW_MAJOR ? N : K);
+    const int64_t ldc = L.ldc ? L.ldc : N;
+    const int64_t ldd = L.ldd ? L.ldd : N;
+    if (lda < K || ldb < (L.b == DG_ROW_MAJOR ? N : K) || ldc < N || ldd < N)
+        return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
+    // alignment: K in whole MFMA steps, rows on 16-byte boundaries
+    const int ksub = (path == P_I8 || path == P_E2M1) ? 32 : 16;
+    if (K % ksub)
+        return fail(DG_ERR_ALIGNMENT, "K dimension not aligned to the MFMA depth (" + std::to_string(ksub) +
+                                          "); padding (pad_k) is not supported");
+    if (path == P_E2M1 && group_k != 32) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs group_k == 32");
+    const int esz = path == P_I8 ? 1 : 2;
+    if ((lda * esz) % 16) return fail(DG_ERR_ALIGNMENT, "lda is not a multiple of 16 bytes");
+    if (path == P_E2M1) {
+        if (ldb % 32) return fail(DG_ERR_ALIGNMENT, "ldb (codes) is not a multiple of 32");
+    } else if ((ldb * esz) % 16) {
+        return fail(DG_ERR_ALIGNMENT, "ldb is not a multiple of 16 bytes");
+    }
+    pr.M = M;
+    pr.N = N;
+    pr.K = K;
+    pr.path = path;
+    pr.b_kmajor = L.b == DG_COL_MAJOR;
+    pr.out_type = elt_of(dt->c);
+    pr.epi = epi_kind;
+    pr.beta_nz = beta_nz;
+    return DG_OK;
+}
+
+dg_plan_opts opts_or_default(const dg_plan_opts *o)
+{
+    dg_plan_opts d{};
+    d.force_path = DG_PATH_AUTO;
+    if (o) d = *o;
+    if (d.target_occupancy <= 0.f) d.target_occupancy = 0.125f;
+    return d;
+}
+
+std::string cache_key(const Problem &p, const dg_plan_opts &o)
+{
+    char k[256];
+    std::snprintf(k, sizeof k, "%lld,%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d",
+                  (long long)p.M, (long long)p.N, (long long)p.K, p.path, p.b_kmajor, p.out_type, p.epi,
+                  p.beta_nz, o.force_m_tile, o.force_n_tile, o.force_k_tile, o.force_split_k, o.force_path,
+                  o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k);
+    return k;
+}
+
+dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, Candidate &out)
+{
+    if (o.pad_k) return fail(DG_ERR_UNSUPPORTED, "pad_k is reserved and must be 0");
+    if (o.unit < DG_UNIT_AUTO || o.unit > DG_UNIT_VALU) return fail(DG_ERR_INVALID_ARG, "unknown unit");
+    if (o.force_path < DG_PATH_AUTO || o.force_path > DG_PATH_SKINNY)
+        return fail(DG_ERR_INVALID_ARG, "unknown path");
+    if (o.force_split_k < 0 || o.force_m_tile < 0 || o.force_n_tile < 0 || o.force_k_tile < 0 ||
+        o.lds_limit_bytes < 0 || o.target_occupancy > 1.0f)
+        return fail(DG_ERR_INVALID_ARG, "invalid planner option");
+    const std::string key = cache_key(pr, o);
+    auto it = h->cache.find(key);
+    if (it != h->cache.end()) {
+        out = it->second;
+        return DG_OK;
+    }
+    PlanResult r = plan_problem(pr, h->desc, o);
+    if (r.status != DG_OK) return fail(r.status, r.message);
+    out = r.pareto.front();
+    h->cache.emplace(key, out);
+    return DG_OK;
+}
+
+const char *status_names[] = {"DG_OK",
+                              "DG_ERR_INVALID_ARG",
+                              "DG_ERR_UNSUPPORTED",
+                              "DG_ERR_ALIGNMENT",
+                              "DG_ERR_NO_CANDIDATE",
+                              "DG_ERR_CONFLICT",
+                              "DG_ERR_INVALID_STATE",
+                              "DG_ERR_WORKSPACE",
+                              "DG_ERR_HIP",
+                              "DG_ERR_INTERNAL"};
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_default_device_desc(dg_device_desc *out)
+{
+    if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
+    std::memset(out, 0, sizeof *out);
+    std::snprintf(out->arch, sizeof out->arch, "gfx950");
+    out->cu_count = 256;
+    out->xcd_count = 8;
+    out->simd_per_cu = 4;
+    out->wave_size = 64;
+    out->lds_bytes_per_cu = 163840;
+    out->lds_bytes_per_wg = 163840;
+    out->vgpr_per_lane = 512;
+    out->max_waves_per_simd = 8;
+    out->clock_ghz = 2.4;
+    out->hbm_gbps = 8000.0;
+    out->l2_bytes_per_xcd = 4.0 * 1024 * 1024;
+    return DG_OK;
+}
+
+dg_status dg_create(dg_handle_t *out, int hip_device)
+{
+    try {
+        if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
+        *out = nullptr;
+        int n = 0;
+        hipError_t e = hipGetDeviceCount(&n);
+        if (e != hipSuccess || n <= 0) return fail(DG_ERR_HIP, "no HIP device visible");
+        if (hip_device < 0 || hip_device >= n) return fail(DG_ERR_INVALID_ARG, "device index out of range");
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, hip_device);
+        if (e != hipSuccess) return fail(DG_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail(DG_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
+        dg_handle_s *h = new dg_handle_s();
+        dg_default_device_desc(&h->desc);
+        h->desc.cu_count = prop.multiProcessorCount;
+        if (prop.clockRate > 0) h->desc.clock_ghz = prop.clockRate / 1e6;
+        if (prop.maxSharedMemoryPerMultiProcessor > 0)
+            h->desc.lds_bytes_per_cu = (int32_t)prop.maxSharedMemoryPerMultiProcessor;
+        h->device = hip_device;
+        {
+            std::lock_guard<std::mutex> lk(g_live_mu);
+            g_live.insert(h);
+        }
+        *out = h;
+        return DG_OK;
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_create");
+    }
+}
+
+dg_status dg_create_offline(dg_handle_t *out, const dg_device_desc *desc)
+{
+    try {
+        if (!out || !desc) return fail(DG_ERR_INVALID_ARG, "NULL argument");
+        *out = nullptr;
+        if (desc->cu_count <= 0 || desc->simd_per_cu <= 0 || desc->lds_bytes_per_cu <= 0 ||
+            desc->lds_bytes_per_wg <= 0 || desc->vgpr_per_lane <= 0 || desc->max_waves_per_simd <= 0 ||
+            desc->clock_ghz <= 0 || desc->hbm_gbps <= 0)
+            return fail(DG_ERR_INVALID_ARG, "device description has a non-positive field");
+        dg_handle_s *h = new dg_handle_s();
+        h->desc = *desc;
+        h->device = -1;
+        {
+            std::lock_guard<std::mutex> lk(g_live_mu);
+            g_live.insert(h);
+        }
+        *out = h;
+        return DG_OK;
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_create_offline");
+    }
+}
+
+dg_status dg_destroy(dg_handle_t h)
+{
+    if (!h) return DG_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        if (!g_live.erase(h)) return fail(DG_ERR_INVALID_STATE, "handle is not live");
+    }
+    delete h;
+    return DG_OK;
+}
+
+dg_status dg_plan(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
+                  int32_t group_k, int32_t epi_kind, const dg_plan_opts *opts, dg_plan_info *out)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        Problem pr;
+        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, pr);
+        if (s) return s;
+        Candidate c;
+        s = plan_cached(h, pr, opts_or_default(opts), c);
+        if (s) return s;
+        if (out) fill_info(c, out);
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_plan");
+    }
+}
+
+dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt,
+                             const dg_layouts *lay, int32_t group_k, int32_t epi_kind,
+                             const dg_plan_opts *opts, dg_plan_info *out, int32_t cap, int32_t *count)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (cap < 0 || (cap > 0 && !out)) return fail(DG_ERR_INVALID_ARG, "bad output array");
+        Problem pr;
+        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, pr);
+        if (s) return s;
+        dg_plan_opts o = opts_or_default(opts);
+        if (o.pad_k) return fail(DG_ERR_UNSUPPORTED, "pad_k is reserved and must be 0");
+        PlanResult r = plan_problem(pr, h->desc, o);
+        if (r.status != DG_OK) return fail(r.status, r.message);
+        if (count) *count = (int32_t)r.pareto.size();
+        for (int i = 0; i < cap && i < (int)r.pareto.size(); ++i) fill_info(r.pareto[i], &out[i]);
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_plan_candidates");
+    }
+}
+
+dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
+                  const void *A, const void *B, const void *b_scale, int32_t group_k, const void *D, void *C,
+                  const void *alpha, const void *beta, const dg_epilogue *epi, const dg_plan_opts *opts,
+                  void *workspace, size_t workspace_bytes, dg_stream_t stream)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: planning only");
+        if (!dt || !alpha || !beta) return fail(DG_ERR_INVALID_ARG, "dtypes, alpha and beta are required");
+        const bool is_int = dt->compute == DG_I32;
+        const int32_t ia = is_int ? *reinterpret_cast<const int32_t *>(alpha) : 0;
+        const int32_t ib = is_int ? *reinterpret_cast<const int32_t *>(beta) : 0;
+        const float fa = is_int ? 0.f : *reinterpret_cast<const float *>(alpha);
+        const float fb = is_int ? 0.f : *reinterpret_cast<const float *>(beta);
+        const int beta_nz = is_int ? ib != 0 : fb != 0.f;
+        dg_epilogue E{};
+        if (epi) E = *epi;
+        Problem pr;
+        dg_status s = describe(M, N, K, dt, lay, group_k, E.kind, beta_nz, pr);
+        if (s) return s;
+        const bool rq = E.kind == DG_EPI_REQUANT_I8 || E.kind == DG_EPI_REQUANT_F16;
+        if (rq && ia != 1) return fail(DG_ERR_INVALID_ARG, "requantise epilogues need alpha == 1 (use epi->scale)");
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+            return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
+        if (M == 0 || N == 0) return ok();
+        // operands
+        if (!C) return fail(DG_ERR_INVALID_ARG, "C is NULL");
+        if (K > 0 && (!A || !B)) return fail(DG_ERR_INVALID_ARG, "A or B is NULL");
+        if (pr.path == P_E2M1 && K > 0 && !b_scale) return fail(DG_ERR_INVALID_ARG, "e2m1 needs b_scale");
+        if (beta_nz && !D) return fail(DG_ERR_INVALID_ARG, "beta != 0 needs D");
+        const bool has_bias_kind = E.kind == DG_EPI_BIAS || E.kind == DG_EPI_BIAS_GELU_ERF;
+        if (has_bias_kind && !E.bias) return fail(DG_ERR_INVALID_ARG, "the epilogue needs a bias");
+        if (E.bias) {
+            if (rq && E.bias_type != DG_F32) return fail(DG_ERR_UNSUPPORTED, "requantise bias must be F32");
+            if (!rq && E.bias_type != DG_F16 && E.bias_type != DG_BF16 && E.bias_type != DG_F32)
+                return fail(DG_ERR_UNSUPPORTED, "bias must be F16, BF16 or F32");
+            if (!rq && E.kind != DG_EPI_BIAS && E.kind != DG_EPI_BIAS_GELU_ERF)
+                return fail(DG_ERR_CONFLICT, "a bias was given to an epilogue without a bias term");
+        }
+        if ((A && !aligned(A, 16)) || (B && !aligned(B, 16)))
+            return fail(DG_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
+        const int osz = elt_size(pr.out_type);
+        if (!aligned(C, osz) || (D && !aligned(D, osz)) || (b_scale && !aligned(b_scale, 2)))
+            return fail(DG_ERR_ALIGNMENT, "C, D or b_scale is misaligned for its type");
+        // plan
+        const dg_plan_opts o = opts_or_default(opts);
+        Candidate c;
+        s = plan_cached(h, pr, o, c);
+        if (s) return s;
+        if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
+            return fail(DG_ERR_WORKSPACE, "workspace missing or smaller than " + std::to_string(c.ws_bytes) + " bytes");
+        if (c.ws_bytes > 0 && !aligned(workspace, 16)) return fail(DG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+
+        dg_layouts L{};
+        if (lay) L = *lay;
+        const int esz = pr.path == P_I8 ? 1 : 2;
+        (void)esz;
+        EpiArgs ea{};
+        ea.C = C;
+        ea.D = D;
+        ea.bias = E.bias;
+        ea.ldc = L.ldc ? L.ldc : N;
+        ea.ldd = L.ldd ? L.ldd : N;
+        ea.alpha = fa;
+        ea.beta = fb;
+        ea.ialpha = ia;
+        ea.ibeta = ib;
+        ea.rq_scale = E.scale;
+        ea.kind = E.kind;
+        ea.out_type = pr.out_type;
+        ea.bias_type = elt_of(E.bias_type);
+        ea.d_read = beta_nz;
+        const int64_t lda = L.lda ? L.lda : K;
+        const int64_t ldb = L.ldb ? L.ldb : (pr.b_kmajor ? K : N);
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        hipError_t he = hipSuccess;
+        if (c.family == F_TILED) {
+            TiledArgs ta{};
+            ta.A = A;
+            ta.B = B;
+            ta.scale = b_scale;
+            ta.lda = lda;
+            ta.ldb = ldb;
+            ta.ld_scale = K / 32;
+            ta.M = (int)M;
+            ta.N = (int)N;
+            ta.K = (int)K;
+            ta.split_k = c.split_k;
+            ta.k_slice = c.k_slice;
+            ta.tiles_m = (int)((M + c.m_tile - 1) / c.m_tile);
+            ta.tiles_n = (int)((N + c.n_tile - 1) / c.n_tile);
+            ta.group_m = 4;
+            ta.ws = workspace;
+            ta.epi = ea;
+            he = launch_tiled(c.kernel_id, ta, c.grid_x, c.grid_y, st);
+        } else {
+            SkinnyArgs sa{};
+            sa.A = A;
+            sa.B = B;
+            sa.scale = b_scale;
+            sa.lda = lda;
+            sa.ldb = ldb;
+            sa.ld_scale = K / 32;
+            sa.M = (int)M;
+            sa.N = (int)N;
+            sa.K = (int)K;
+            sa.split_k = c.split_k;
+            sa.k_slice = c.k_slice;
+            sa.ws = workspace;
+            sa.epi = ea;
+            if (c.family == F_SKINNY_VALU) he = launch_skinny_valu(c.kernel_id, sa, c.grid_x, c.grid_y, st);
+            else if (c.family == F_SKINNY_MFMA) he = launch_skinny_mfma(c.kernel_id, sa, c.grid_x, c.grid_y, st);
+            else he = launch_skinny_e2m1(c.kernel_id, sa, c.grid_x, c.grid_y, st);
+        }
+        if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
+        if (c.split_k > 1) {
+            ReduceArgs ra{};
+            ra.ws = workspace;
+            ra.split_k = c.split_k;
+            ra.M = (int)M;
+            ra.N = (int)N;
+            ra.is_int = pr.path == P_I8;
+            ra.epi = ea;
+            he = launch_reduce(ra, st);
+            if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
+        }
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_gemm");
+    }
+}
+
+const char *dg_last_error(void) { return g_err.c_str(); }
+
+const char *dg_status_str(dg_status s)
+{
+    if ((int)s < 0 || (int)s >= (int)(sizeof(status_names) / sizeof(status_names[0]))) return "DG_UNKNOWN";
+    return status_names[s];
+}
+
+}  // extern "C"

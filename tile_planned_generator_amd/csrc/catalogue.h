@@ -1,0 +1,65 @@
+// catalogue.h - the compiled kernel variants the planner chooses among.
+//
+// Plain C++ (no HIP): included by the planner, which runs on any host, and by
+// the kernel sources, which instantiate exactly these variants.  The pages'
+// planner searches tile shape x layout x granularity ([overview] DeepGEMM
+// article, section 4.1, stage 2); on gfx950 the tile shapes are multiples of
+// the 32x32 MFMA output block and the granularity is the wave grid.
+#pragma once
+
+namespace dg {
+
+// Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN)
+//   path      P_F16 / P_BF16 / P_I8 / P_E2M1
+//   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
+//   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
+#define DG_TILE_SHAPES(X, path, kmaj) \
+    X(path, kmaj, 256, 256, 2, 2)     \
+    X(path, kmaj, 256, 256, 2, 4)     \
+    X(path, kmaj, 256, 128, 2, 2)     \
+    X(path, kmaj, 128, 128, 2, 2)     \
+    X(path, kmaj, 64, 64, 2, 2)
+
+#define DG_TILED_CATALOGUE(X)       \
+    DG_TILE_SHAPES(X, P_F16, 0)     \
+    DG_TILE_SHAPES(X, P_F16, 1)     \
+    DG_TILE_SHAPES(X, P_BF16, 0)    \
+    DG_TILE_SHAPES(X, P_BF16, 1)    \
+    DG_TILE_SHAPES(X, P_I8, 0)      \
+    DG_TILE_SHAPES(X, P_I8, 1)      \
+    DG_TILE_SHAPES(X, P_E2M1, 1)
+
+// Skinny VALU streaming GEMM over a row-major 16-bit B:
+// X(path, MR, LPR): up to MR rows of A; LPR lanes span one row of B (8 columns each).
+#define DG_SKINNY_VALU_MR(X, path, lpr) X(path, 1, lpr) X(path, 2, lpr) X(path, 4, lpr) X(path, 8, lpr)
+#define DG_SKINNY_VALU_CATALOGUE(X)        \
+    DG_SKINNY_VALU_MR(X, P_F16, 64)        \
+    DG_SKINNY_VALU_MR(X, P_F16, 32)        \
+    DG_SKINNY_VALU_MR(X, P_F16, 16)        \
+    DG_SKINNY_VALU_MR(X, P_BF16, 64)       \
+    DG_SKINNY_VALU_MR(X, P_BF16, 32)       \
+    DG_SKINNY_VALU_MR(X, P_BF16, 16)
+
+// Skinny MFMA streaming GEMM (M <= 16) over a row-major 16-bit B: X(path)
+#define DG_SKINNY_MFMA_CATALOGUE(X) X(P_F16) X(P_BF16)
+
+// Skinny e2m1 GEMM (B codes N x K, K contiguous): X(MR)
+#define DG_SKINNY_E2M1_CATALOGUE(X) X(1) X(2) X(4) X(8)
+
+// Resource facts of the variants, used by the planner's constraints.
+struct TiledShape {
+    int path, b_kmajor, bm, bn, wm, wn;
+};
+
+constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 128 : 64; }
+constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
+
+// LDS bytes of one tiled variant (two stages).  A rows and 16-bit / int8 B rows
+// are 128 bytes; e2m1 B rows are 32 bytes of codes padded to 40, plus 4 bytes of
+// scales per column.
+constexpr int tiled_lds_bytes(int path, int bm, int bn)
+{
+    return 2 * (bm * 128 + (path == 3 ? bn * 40 + bn * 4 : bn * 128));
+}
+
+}  // namespace dg

@@ -1,0 +1,66 @@
+// dg_args.h - argument blocks shared by the host launchers and the kernels.
+//
+// Internal to the library: the C ABI in include/dg.h is the only public surface.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Operand paths of the tiled kernel and the skinny kernels.
+enum Path : int { P_F16 = 0, P_BF16 = 1, P_I8 = 2, P_E2M1 = 3 };
+
+// Storage types of outputs, D and bias.
+enum Elt : int { T_F16 = 0, T_BF16 = 1, T_F32 = 2, T_I32 = 3, T_I8 = 4 };
+
+// Fused epilogue kinds (same numbering as dg_epi_kind).
+enum EpiKind : int {
+    E_NONE = 0, E_BIAS = 1, E_GELU = 2, E_BIAS_GELU = 3, E_RQ_I8 = 4, E_RQ_F16 = 5
+};
+
+// Everything the epilogue needs: alpha*acc + beta*D + bias, activation, the
+// conversion to the output type and the store.
+struct EpiArgs {
+    void *C;
+    const void *D;
+    const void *bias;
+    int64_t ldc, ldd;
+    float alpha, beta;        // floating-point compute
+    int32_t ialpha, ibeta;    // integer compute
+    float rq_scale;           // requantise multiplier
+    int kind;                 // EpiKind
+    int out_type;             // Elt of C (and of D)
+    int bias_type;            // Elt of bias
+    int d_read;               // beta != 0
+};
+
+// Tiled MFMA GEMM.
+struct TiledArgs {
+    const void *A, *B, *scale;
+    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1)
+    int M, N, K;
+    int split_k, k_slice;         // K slices; every slice but the last has k_slice
+    int tiles_m, tiles_n, group_m;
+    void *ws;                     // split partials [split][M][N] (fp32 or int32)
+    EpiArgs epi;
+};
+
+// Skinny split-K streaming GEMM (small M).
+struct SkinnyArgs {
+    const void *A, *B, *scale;
+    int64_t lda, ldb, ld_scale;
+    int M, N, K;
+    int split_k, k_slice;
+    void *ws;                     // split partials [split][M][N] fp32
+    EpiArgs epi;
+};
+
+// Split-K reduction: out = epilogue(sum over s ascending of ws[s]).
+struct ReduceArgs {
+    const void *ws;
+    int split_k, M, N;
+    int is_int;
+    EpiArgs epi;
+};
+
+}  // namespace dg

@@ -1,0 +1,28 @@
+// launch.h - host entry points of the kernel sources (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "dg_args.h"
+
+namespace dg {
+
+// Tiled MFMA GEMM; `id` indexes DG_TILED_CATALOGUE.
+int tiled_kernel_count();
+hipError_t launch_tiled(int id, const TiledArgs &a, int grid_x, int grid_y, hipStream_t s);
+
+// Skinny VALU GEMM; `id` indexes DG_SKINNY_VALU_CATALOGUE.
+int skinny_valu_count();
+hipError_t launch_skinny_valu(int id, const SkinnyArgs &a, int grid_x, int grid_y, hipStream_t s);
+
+// Skinny MFMA GEMM (M <= 16); `id` indexes DG_SKINNY_MFMA_CATALOGUE.
+int skinny_mfma_count();
+hipError_t launch_skinny_mfma(int id, const SkinnyArgs &a, int grid_x, int grid_y, hipStream_t s);
+
+// Skinny e2m1 GEMM; `id` indexes DG_SKINNY_E2M1_CATALOGUE.
+int skinny_e2m1_count();
+hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int grid_x, int grid_y, hipStream_t s);
+
+// Split-K reduction and epilogue.
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,56 @@
+// planner.h - host-side constraint planner (no HIP dependency).
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+// Kernel families the planner can choose.
+enum Family : int { F_TILED = 0, F_SKINNY_VALU = 1, F_SKINNY_MFMA = 2, F_SKINNY_E2M1 = 3 };
+
+// One problem, after validation.
+struct Problem {
+    int64_t M, N, K;
+    int path;        // Path
+    int b_kmajor;    // 1: B stored N x K
+    int out_type;    // Elt
+    int epi;         // EpiKind
+    int beta_nz;     // D is read
+};
+
+struct Candidate {
+    int family;
+    int kernel_id;   // index within the family's catalogue
+    int unit;        // dg_unit
+    int mfma_m, mfma_n, mfma_k;
+    int m_tile, n_tile, waves;
+    int split_k, k_slice;
+    int k_main, n_main, k_tail, n_tail;
+    int lds, vgpr, agpr, waves_per_simd;
+    int grid_x, grid_y;
+    int64_t ws_bytes;
+    double est_us, roof_us;
+    std::string name;
+};
+
+struct PlanResult {
+    dg_status status;
+    std::string message;
+    std::vector<Candidate> pareto;   // best first
+    int enumerated = 0, pruned = 0;
+};
+
+// Enumerate, prune, score, Pareto-filter.  Deterministic.
+PlanResult plan_problem(const Problem &pr, const dg_device_desc &desc, const dg_plan_opts &opts);
+
+// Fill the public description of a candidate.
+void fill_info(const Candidate &c, dg_plan_info *out);
+
+// Roofline time of the problem (microseconds) on the described device.
+double roofline_us(const Problem &pr, const dg_device_desc &desc);
+
+}  // namespace dg
