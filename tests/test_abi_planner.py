@@ -264,3 +264,35 @@ def test_worked_example_shape_is_feasible_on_an_a100_like_description():
     p = h.plan(2048, 2048, 8192, opts=dg.dg_plan_opts(force_m_tile=64, force_n_tile=64))
     assert (p.m_tile, p.n_tile) == (64, 64) and p.k_main % 16 == 0
     h.close()
+
+
+def _resources():
+    rows = []
+    path = os.path.join(ROOT, "tile_planned_generator_amd", "csrc", "resources.inc")
+    for line in open(path):
+        if line.startswith("{"):
+            rows.append([int(x) for x in line.strip().strip("{},").split(",")])
+    return rows
+
+
+def test_planner_uses_the_compiled_resource_usage(off):
+    # the constraints are checked against the registers, LDS and occupancy the
+    # compiler reported for each variant (no spills allowed at build time)
+    rows = _resources()
+    assert rows and all(r[-1] == 0 for r in rows)
+    tiled = {tuple(r[1:7]): r for r in rows if r[0] == 0}
+    names = {"f16": 0, "bf16": 1, "i8": 2, "e2m1": 3}
+    for M, N, K, a, b, c, epi in PROBLEMS:
+        for p in off.candidates(M, N, K, a, b, c, epilogue=epi):
+            if p.path != dg.DG_PATH_TILED:
+                continue
+            nm = p.kernel_name.decode().split("_")
+            wm, wn = map(int, nm[-1][1:].split("x"))
+            key = (names[nm[1]], 1 if nm[2] == "k" else 0, p.m_tile, p.n_tile, wm, wn)
+            r = tiled[key]
+            assert (p.vgpr_est, p.agpr_est, p.lds_bytes) == (r[7], r[8], r[9])
+            assert p.waves_per_simd == r[10]
+    # occupancy 2/8 keeps only variants the compiler gave >= 2 waves per SIMD
+    o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, target_occupancy=0.25)
+    p = off.plan(2048, 2048, 2048, opts=o)
+    assert p.kernel_name.decode().endswith("w2x4") and p.waves_per_simd >= 2

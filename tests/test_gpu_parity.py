@@ -34,10 +34,12 @@ TORCH_OUT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32,
 
 def to_dev(t, pad=0):
     """2-D tensor on the GPU; with pad > 0 the rows are padded (leading dimension
-    = columns + pad) so the kernels see a non-tight leading dimension."""
+    = columns + pad rounded up to 16 elements, so rows stay 16-byte aligned) and
+    the kernels see a non-tight leading dimension."""
     t = t.to(DEV)
     if pad:
-        buf = torch.zeros(t.shape[0], t.shape[1] + pad, dtype=t.dtype, device=DEV)
+        ld = (t.shape[1] + pad + 15) // 16 * 16
+        buf = torch.zeros(t.shape[0], ld, dtype=t.dtype, device=DEV)
         buf[:, : t.shape[1]] = t
         return buf[:, : t.shape[1]]
     return t.contiguous()
@@ -184,9 +186,8 @@ def test_rank_one_closed_form_exact(h):
     x = torch.tensor([(i % 7) - 3 for i in range(M)], dtype=torch.float16)
     y = torch.tensor([(j % 5) - 2 for j in range(N)], dtype=torch.float16)
     A = x[:, None].expand(M, K).contiguous()
-    B = y[None, :].expand(K, 80).contiguous()[:, :N]
-    Bp = torch.zeros(K, 80, dtype=torch.float16)
-    Bp[:, :N] = B
+    Bp = torch.zeros(K, 80, dtype=torch.float16)     # rows padded to 80 columns
+    Bp[:, :N] = y[None, :].expand(K, N)
     Cd = torch.empty(M, N, dtype=torch.float32, device=DEV)
     h.gemm(A.to(DEV), Bp.to(DEV)[:, :N], Cd)
     torch.cuda.synchronize()
@@ -220,12 +221,10 @@ def test_f16_alpha_beta_d_full_size(h):
     run(h, synth.make("f16_256x256x256_alpha_beta_d"))
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(257, 263, 272, 8), (300, 129, 1040, 0), (33, 65, 16, 16)])
+@pytest.mark.parametrize("M,N,K,pad", [(257, 263, 272, 9), (300, 128, 1040, 0), (33, 65, 16, 15)])
 def test_f16_alpha_beta_d_ragged(h, M, N, K, pad):
-    w = synth.make("f16_256x256x256_alpha_beta_d", M=M, N=N, K=K)
-    if N % 8 and not pad:
-        pytest.skip("tight rows need 16-byte alignment")
-    run(h, w, pad=pad if pad else 0)
+    # pad makes the row pitch a multiple of 8 elements (16 bytes)
+    run(h, synth.make("f16_256x256x256_alpha_beta_d", M=M, N=N, K=K), pad=pad)
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 640), (300, 200, 96), (129, 257, 4160)])

@@ -7,7 +7,7 @@ the library links as one unit.  Objects go to ``_build/``, the library to
 """
 import concurrent.futures as cf
 import os
-import shutil
+import re
 import subprocess
 import sys
 
@@ -17,10 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdg.so")
 
-SOURCES = [
-    "gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip", "gemm_tiled_e2m1.hip",
-    "skinny.hip", "gemm_tiled.hip", "api.cpp", "planner.cpp",
-]
+KERNEL_SOURCES = ["gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip",
+                  "gemm_tiled_e2m1.hip", "skinny.hip"]
+HOST_SOURCES = ["gemm_tiled.hip", "api.cpp", "planner.cpp"]
+RESOURCES = os.path.join(CSRC, "resources.inc")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -34,6 +34,8 @@ def _compile(src, verbose):
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
         cmd = [HIPCC, *DEVICE, *COMMON, "-x", "hip", "-c", path, "-o", obj]
+        if src in KERNEL_SOURCES:
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
     else:
         cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
     if verbose:
@@ -43,16 +45,68 @@ def _compile(src, verbose):
                     if "is not a recognized feature for this target" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{out}")
-    if out.strip() and verbose:
-        print(out, flush=True)
-    return obj
+    return obj, out
+
+
+# kernel family ids (planner.h: F_TILED, F_SKINNY_VALU, F_SKINNY_MFMA, F_SKINNY_E2M1)
+_FAMILIES = {"gemm_tiled_kernel": 0, "skinny_valu_kernel": 1, "skinny_mfma_kernel": 2,
+             "skinny_e2m1_kernel": 3}
+
+
+def _parse_resources(remarks):
+    """Per compiled kernel: (family, template args) -> VGPRs, AGPRs, LDS bytes,
+    waves per SIMD, from the compiler's kernel-resource-usage remarks."""
+    rows, cur = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            fam = next((f for k, f in _FAMILIES.items() if k in name), None)
+            if fam is None:
+                cur = None
+                continue
+            args = [int(x) for x in re.findall(r"Li(-?\d+)E", name)]
+            cur = (fam, tuple(args + [0] * (6 - len(args))))
+            rows[cur] = {}
+            continue
+        if cur is None:
+            continue
+        for key, field in (("VGPRs:", "vgpr"), ("AGPRs:", "agpr"), ("LDS Size [bytes/block]:", "lds"),
+                           ("Occupancy [waves/SIMD]:", "occ"), ("VGPRs Spill:", "spill")):
+            m = re.search(re.escape(key) + r" (\d+)", line)
+            if m:
+                rows[cur][field] = int(m.group(1))
+    return rows
+
+
+def _write_resources(rows):
+    lines = ["// resources.inc - registers, LDS and occupancy of every compiled kernel variant,",
+             "// extracted from the compiler's kernel-resource-usage remarks by build.py.",
+             "// {family, template args (6, zero-padded), VGPRs, AGPRs, LDS bytes, waves/SIMD, spills}"]
+    for (fam, args), r in sorted(rows.items()):
+        lines.append("{%d, %s, %d, %d, %d, %d, %d}," % (
+            fam, ", ".join(str(a) for a in args), r.get("vgpr", 0), r.get("agpr", 0),
+            r.get("lds", 0), r.get("occ", 0), r.get("spill", 0)))
+    text = "\n".join(lines) + "\n"
+    old = open(RESOURCES).read() if os.path.exists(RESOURCES) else None
+    if old != text:
+        with open(RESOURCES, "w") as fh:
+            fh.write(text)
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        done = list(ex.map(lambda s: _compile(s, verbose), KERNEL_SOURCES))
+    rows = _parse_resources("\n".join(out for _, out in done))
+    spills = [k for k, r in rows.items() if r.get("spill", 0)]
+    if spills:
+        raise RuntimeError(f"kernel variants spill registers: {spills}")
+    _write_resources(rows)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        done += list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES))
+    objs = [o for o, _ in done]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

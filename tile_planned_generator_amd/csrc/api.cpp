@@ -115,11 +115,13 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
                                           "); padding (pad_k) is not supported");
     if (path == P_E2M1 && group_k != 32) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs group_k == 32");
     const int esz = path == P_I8 ? 1 : 2;
-    if ((lda * esz) % 16) return fail(DG_ERR_ALIGNMENT, "lda is not a multiple of 16 bytes");
-    if (path == P_E2M1) {
-        if (ldb % 32) return fail(DG_ERR_ALIGNMENT, "ldb (codes) is not a multiple of 32");
-    } else if ((ldb * esz) % 16) {
-        return fail(DG_ERR_ALIGNMENT, "ldb is not a multiple of 16 bytes");
+    if (K > 0) {   // with K == 0 neither A nor B is read
+        if ((lda * esz) % 16) return fail(DG_ERR_ALIGNMENT, "lda is not a multiple of 16 bytes");
+        if (path == P_E2M1) {
+            if (ldb % 32) return fail(DG_ERR_ALIGNMENT, "ldb (codes) is not a multiple of 32");
+        } else if ((ldb * esz) % 16) {
+            return fail(DG_ERR_ALIGNMENT, "ldb is not a multiple of 16 bytes");
+        }
     }
     pr.M = M;
     pr.N = N;

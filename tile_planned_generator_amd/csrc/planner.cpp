@@ -67,6 +67,24 @@ const int k_e2m1_mr[] = {
 #undef DG_ES
 };
 
+// Registers, LDS and occupancy of the compiled variants, as the compiler
+// reported them when the library was built.
+struct ResRow {
+    int fam, a0, a1, a2, a3, a4, a5, vgpr, agpr, lds, occ, spill;
+};
+const ResRow k_res[] = {
+#include "resources.inc"
+};
+
+const ResRow *find_res(int fam, int a0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0)
+{
+    for (const ResRow &r : k_res)
+        if (r.fam == fam && r.a0 == a0 && r.a1 == a1 && r.a2 == a2 && r.a3 == a3 && r.a4 == a4 &&
+            r.a5 == a5)
+            return &r;
+    return nullptr;
+}
+
 const char *path_name(int p)
 {
     switch (p) {
@@ -171,7 +189,12 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
         int vgpr, agpr;
         if (acc + other <= 256) { vgpr = acc + other; agpr = 0; }
         else { vgpr = other; agpr = acc; }
-        const int lds = tiled_lds_bytes(s.path, s.bm, s.bn);
+        int lds = tiled_lds_bytes(s.path, s.bm, s.bn);
+        if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn)) {
+            vgpr = r->vgpr;
+            agpr = r->agpr;
+            lds = r->lds;
+        }
         const int occ = waves_per_simd(vgpr + agpr, lds, waves, d);
 
         const int min_slice = 4 * BKE;
@@ -278,8 +301,12 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 16) : 0;
                 const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
                 if (S_eff == 1) k_slice = (int)pr.K;
-                const int lds = SKINNY_A_LDS;
-                const int regs = 40 + s.mr * 8 + 8 * 4 + 16;
+                int lds = SKINNY_A_LDS;
+                int regs = 40 + s.mr * 8 + 8 * 4 + 16;
+                if (const ResRow *r = find_res(F_SKINNY_VALU, s.path, s.mr, s.lpr)) {
+                    regs = r->vgpr + r->agpr;
+                    lds = r->lds;
+                }
                 const int occ = waves_per_simd(regs, lds, 4, d);
                 const char *why = nullptr;
                 if ((int64_t)k_slice * s.mr * 2 > SKINNY_A_LDS) why = "A slice over LDS staging";
@@ -323,7 +350,12 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 32) : 0;
                 const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
                 if (S_eff == 1) k_slice = (int)pr.K;
-                const int occ = waves_per_simd(112, 0, 4, d);
+                int vg = 64, ag = 48;
+                if (const ResRow *r = find_res(F_SKINNY_MFMA, pr.path)) {
+                    vg = r->vgpr;
+                    ag = r->agpr;
+                }
+                const int occ = waves_per_simd(vg + ag, 0, 4, d);
                 const char *why = nullptr;
                 if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
@@ -340,7 +372,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.m_tile = 16; c.n_tile = 512; c.waves = 4;
                 c.split_k = S_eff; c.k_slice = k_slice;
                 schedule(k_slice, 32, c.k_main, c.n_main, c.k_tail, c.n_tail);
-                c.lds = 0; c.vgpr = 64; c.agpr = 48; c.waves_per_simd = occ;
+                c.lds = 0; c.vgpr = vg; c.agpr = ag; c.waves_per_simd = occ;
                 c.grid_x = (int)ceil_div(pr.N, 512);
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
@@ -364,7 +396,9 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 32) : 0;
                 const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
                 if (S_eff == 1) k_slice = (int)pr.K;
-                const int occ = waves_per_simd(48, 0, 4, d);
+                int vg = 48;
+                if (const ResRow *r = find_res(F_SKINNY_E2M1, mr)) vg = r->vgpr + r->agpr;
+                const int occ = waves_per_simd(vg, 0, 4, d);
                 const char *why = nullptr;
                 if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
@@ -381,7 +415,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.split_k = S_eff; c.k_slice = k_slice;
                 schedule(k_slice, 32 * 64, c.k_main, c.n_main, c.k_tail, c.n_tail);
                 if (c.k_tail) { c.n_tail = 1; }
-                c.lds = 0; c.vgpr = 48; c.agpr = 0; c.waves_per_simd = occ;
+                c.lds = 0; c.vgpr = vg; c.agpr = 0; c.waves_per_simd = occ;
                 c.grid_x = (int)ceil_div(pr.N, 4);
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;

@@ -250,9 +250,13 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
             for (int q = 0; q < 4; ++q) {
                 const u32x4 av = ar[q];
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    dsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, av[d]), w[4 * q + d],
+                for (int d = 0; d < 4; ++d) {
+                    // copy the element first: a bit_cast applied directly to a
+                    // vector element with a loop index reads element 0 (clang)
+                    const unsigned ad = av[d];
+                    dsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, ad), w[4 * q + d],
                                                   dsum, false);
+                }
             }
             acc[m] += s * dsum;
         }

@@ -162,7 +162,7 @@ def make(name: str, device="cpu", M=None, N=None, K=None, seed=None) -> Workload
         t["B"] = int8_uniform(_sid(seed, TID_B), K * N, device).view(K, N)
     elif path in ("f16", "bf16"):
         dt = torch.float16 if path == "f16" else torch.bfloat16
-        s = 1.0 / (K ** 0.5)
+        s = 1.0 / (K ** 0.5) if K > 0 else 1.0
         t["A"] = to_storage(normal(_sid(seed, TID_A), M * K, device) * s, dt).view(M, K)
         t["B"] = to_storage(normal(_sid(seed, TID_B), K * N, device) * s, dt).view(K, N)
         if "bias" in epi:
