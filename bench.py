@@ -209,7 +209,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated subset of the other workloads to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 256 MiB once (a plain copy kernel of known size, the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: the planned GEMM is a single-GPU kernel here; "
@@ -221,6 +226,14 @@ def main():
     torch.cuda.init()
     h = dg.Handle(0)
     props = torch.cuda.get_device_properties(0)
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- headline
     p = Prepared(h, HEADLINE, dev, rotate=False)
@@ -235,7 +248,8 @@ def main():
 
     workloads = {HEADLINE: head}
     if not args.only_headline:
-        for name in SECONDARY:
+        chosen = [w for w in args.workloads.split(",") if w] or SECONDARY
+        for name in chosen:
             p = Prepared(h, name, dev, rotate=True)
             small = p.info.est_us < 25
             ms_w, _ = time_steps(p, max(50, args.steps // 2), args.warmup, use_graph=small)

@@ -84,7 +84,7 @@ typedef enum {
 } dg_epi_kind;
 
 typedef enum { DG_UNIT_AUTO = 0, DG_UNIT_MFMA = 1, DG_UNIT_VALU = 2 } dg_unit;
-typedef enum { DG_PATH_AUTO = -1, DG_PATH_TILED = 0, DG_PATH_SKINNY = 1 } dg_path;
+typedef enum { DG_PATH_AUTO = 0, DG_PATH_TILED = 1, DG_PATH_SKINNY = 2 } dg_path;
 
 /* Precision triple plus the accumulator type ([overview] section 2.2, second
  * layer: a precision scheme {weight, activation, output} is declared, not
@@ -102,7 +102,11 @@ typedef struct {
  * B: row-major (f16, bf16, i8) or column-major (f16, bf16, i8, and e2m1, where
  * it is the only layout).  C and D are row-major.  A, B rows (columns for a
  * column-major B) must start on 16-byte boundaries: base pointers 16-byte
- * aligned and lda, ldb multiples of 16 bytes. */
+ * aligned and lda, ldb multiples of 16 bytes.  Every row of A and B must be
+ * readable up to its next 16-byte boundary (any allocation of whole rows of
+ * lda / ldb elements is).  The tiled MFMA path addresses each operand with
+ * 32-bit offsets: M*lda, K*ldb (row-major B) or N*ldb (column-major B) times
+ * the element size must stay below 4 GiB (DG_ERR_UNSUPPORTED otherwise). */
 typedef struct {
     int32_t a, b;             /* dg_layout */
     int64_t lda, ldb, ldc, ldd;
@@ -124,11 +128,12 @@ typedef struct {
 typedef struct {
     int32_t force_m_tile, force_n_tile, force_k_tile; /* tiled path tile (0 = free)   */
     int32_t force_split_k;    /* number of K slices (0 = free)                      */
-    int32_t force_path;       /* dg_path; 0 (TILED) is a valid force, so set -1 for free */
+    int32_t force_path;       /* dg_path (DG_PATH_AUTO = 0: planner decides)         */
     int32_t unit;             /* dg_unit: MFMA (matrix cores) or VALU (vector FMA)  */
     int32_t lds_limit_bytes;  /* LDS budget per workgroup (0 = device maximum)      */
     float target_occupancy;   /* minimum waves per SIMD as a fraction of 8 (0 = 0.125) */
     int32_t pad_k;            /* reserved: must be 0 (K tails must be MFMA-aligned) */
+    int32_t force_waves;      /* waves per workgroup of the tiled path (0 = free)    */
 } dg_plan_opts;
 
 /* Description of the device the planner plans for.  dg_create fills it from

@@ -296,3 +296,7 @@ def test_planner_uses_the_compiled_resource_usage(off):
     o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, target_occupancy=0.25)
     p = off.plan(2048, 2048, 2048, opts=o)
     assert p.kernel_name.decode().endswith("w2x4") and p.waves_per_simd >= 2
+    for nw, suffix in ((4, "w2x2"), (8, "w2x4")):
+        o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, force_waves=nw)
+        p = off.plan(2048, 2048, 2048, opts=o)
+        assert p.kernel_name.decode().endswith(suffix) and p.waves_per_wg == nw

@@ -266,12 +266,10 @@ def test_every_tiled_variant_on_a_ragged_problem(h):
                              ("e2m1", "e2m1_4096x4096x4096", True)):
         ktail = 3 * (128 if path == "i8" else 64) + (64 if path == "i8" else 32)
         w = synth.make(name, M=290, N=272, K=ktail)
-        for bm, bn, occ in ((256, 256, 0.0), (256, 256, 0.25), (256, 128, 0.0), (128, 128, 0.0),
-                            (64, 64, 0.0)):
+        for bm, bn, nw in ((256, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4)):
             for s in (1, 2):
-                # target occupancy 2/8 selects the 8-wave 256 x 256 variant
                 o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
-                                    force_path=dg.DG_PATH_TILED, target_occupancy=occ)
+                                    force_path=dg.DG_PATH_TILED, force_waves=nw)
                 run(h, w, b_colmajor=colm, opts=o)
 
 

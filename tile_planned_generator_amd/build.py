@@ -72,7 +72,8 @@ def _parse_resources(remarks):
         if cur is None:
             continue
         for key, field in (("VGPRs:", "vgpr"), ("AGPRs:", "agpr"), ("LDS Size [bytes/block]:", "lds"),
-                           ("Occupancy [waves/SIMD]:", "occ"), ("VGPRs Spill:", "spill")):
+                           ("Occupancy [waves/SIMD]:", "occ"), ("VGPRs Spill:", "spill"),
+                           ("ScratchSize [bytes/lane]:", "scratch")):
             m = re.search(re.escape(key) + r" (\d+)", line)
             if m:
                 rows[cur][field] = int(m.group(1))
@@ -100,9 +101,9 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         done = list(ex.map(lambda s: _compile(s, verbose), KERNEL_SOURCES))
     rows = _parse_resources("\n".join(out for _, out in done))
-    spills = [k for k, r in rows.items() if r.get("spill", 0)]
+    spills = [k for k, r in rows.items() if r.get("spill", 0) or r.get("scratch", 0)]
     if spills:
-        raise RuntimeError(f"kernel variants spill registers: {spills}")
+        raise RuntimeError(f"kernel variants spill registers or use private memory: {spills}")
     _write_resources(rows)
     with cf.ThreadPoolExecutor(jobs) as ex:
         done += list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES))

@@ -137,7 +137,6 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
 dg_plan_opts opts_or_default(const dg_plan_opts *o)
 {
     dg_plan_opts d{};
-    d.force_path = DG_PATH_AUTO;
     if (o) d = *o;
     if (d.target_occupancy <= 0.f) d.target_occupancy = 0.125f;
     return d;
@@ -146,10 +145,10 @@ dg_plan_opts opts_or_default(const dg_plan_opts *o)
 std::string cache_key(const Problem &p, const dg_plan_opts &o)
 {
     char k[256];
-    std::snprintf(k, sizeof k, "%lld,%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d",
+    std::snprintf(k, sizeof k, "%lld,%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
                   (long long)p.M, (long long)p.N, (long long)p.K, p.path, p.b_kmajor, p.out_type, p.epi,
                   p.beta_nz, o.force_m_tile, o.force_n_tile, o.force_k_tile, o.force_split_k, o.force_path,
-                  o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k);
+                  o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k, o.force_waves);
     return k;
 }
 
@@ -160,6 +159,7 @@ dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, C
     if (o.force_path < DG_PATH_AUTO || o.force_path > DG_PATH_SKINNY)
         return fail(DG_ERR_INVALID_ARG, "unknown path");
     if (o.force_split_k < 0 || o.force_m_tile < 0 || o.force_n_tile < 0 || o.force_k_tile < 0 ||
+        o.force_waves < 0 ||
         o.lds_limit_bytes < 0 || o.target_occupancy > 1.0f)
         return fail(DG_ERR_INVALID_ARG, "invalid planner option");
     const std::string key = cache_key(pr, o);
@@ -360,19 +360,25 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         const int osz = elt_size(pr.out_type);
         if (!aligned(C, osz) || (D && !aligned(D, osz)) || (b_scale && !aligned(b_scale, 2)))
             return fail(DG_ERR_ALIGNMENT, "C, D or b_scale is misaligned for its type");
+        dg_layouts L{};
+        if (lay) L = *lay;
         // plan
         const dg_plan_opts o = opts_or_default(opts);
         Candidate c;
         s = plan_cached(h, pr, o, c);
         if (s) return s;
+        if (c.family == F_TILED) {
+            const int64_t la = L.lda ? L.lda : K, lb = L.ldb ? L.ldb : (pr.b_kmajor ? K : N);
+            const int64_t ea = pr.path == P_I8 ? 1 : 2;
+            const int64_t eb = pr.path == P_E2M1 ? 1 : ea;   // e2m1: ldb counts codes, 2 per byte
+            const int64_t b_ext = pr.b_kmajor ? N * lb * eb / (pr.path == P_E2M1 ? 2 : 1) : K * lb * eb;
+            if (M * la * ea >= (int64_t(1) << 32) || b_ext >= (int64_t(1) << 32))
+                return fail(DG_ERR_UNSUPPORTED, "an operand spans 4 GiB or more (32-bit offsets of the tiled path)");
+        }
         if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
             return fail(DG_ERR_WORKSPACE, "workspace missing or smaller than " + std::to_string(c.ws_bytes) + " bytes");
         if (c.ws_bytes > 0 && !aligned(workspace, 16)) return fail(DG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
 
-        dg_layouts L{};
-        if (lay) L = *lay;
-        const int esz = pr.path == P_I8 ? 1 : 2;
-        (void)esz;
         EpiArgs ea{};
         ea.C = C;
         ea.D = D;

@@ -54,12 +54,13 @@ struct TiledShape {
 constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 128 : 64; }
 constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
 
-// LDS bytes of one tiled variant (two stages).  A rows and 16-bit / int8 B rows
-// are 128 bytes; e2m1 B rows are 32 bytes of codes padded to 40, plus 4 bytes of
-// scales per column.
+// LDS bytes of one tiled variant (two stages of one K step each).  A and
+// 16-bit / int8 B take 128 bytes per row (or per K row of a row-major B: BN
+// columns of a 64-k or 128-k step); e2m1 B takes 32 bytes of codes plus 4 bytes
+// of scales per column.
 constexpr int tiled_lds_bytes(int path, int bm, int bn)
 {
-    return 2 * (bm * 128 + (path == 3 ? bn * 40 + bn * 4 : bn * 128));
+    return 2 * (bm * 128 + (path == 3 ? bn * 36 : bn * 128));
 }
 
 }  // namespace dg

@@ -142,6 +142,101 @@ DG_DEV void epi_store_i(const EpiArgs &e, int64_t i, int64_t j, int32_t acc)
     reinterpret_cast<int32_t *>(e.C)[i * e.ldc + j] = (int32_t)v;
 }
 
+// ------------------------------------------------- vectorised epilogue (4 columns)
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef signed char i8x4v __attribute__((ext_vector_type(4)));
+
+DG_DEV bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+DG_DEV int elt_size(int t) { return (t == T_F16 || t == T_BF16) ? 2 : (t == T_I8 ? 1 : 4); }
+
+// Whether 4 consecutive columns can go through 4-wide vector loads and stores:
+// every pointer, and every row pitch, aligned to 4 elements.
+DG_DEV bool epi_vec_ok(const EpiArgs &e, bool split, const void *ws, int N)
+{
+    if (split) return aligned_to(ws, 16) && (N & 3) == 0;
+    const int os = elt_size(e.out_type);
+    bool ok = aligned_to(e.C, 4 * os) && (e.ldc & 3) == 0;
+    if (e.d_read) ok = ok && aligned_to(e.D, 4 * os) && (e.ldd & 3) == 0;
+    if (e.bias) ok = ok && aligned_to(e.bias, 4 * elt_size(e.bias_type));
+    return ok;
+}
+
+DG_DEV floatx4 load4_f32(const void *p, int type, int64_t idx)
+{
+    if (type == T_F16) {
+        const half4v h = *reinterpret_cast<const half4v *>(reinterpret_cast<const _Float16 *>(p) + idx);
+        return floatx4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+    }
+    if (type == T_BF16) {
+        const bf16x4v h = *reinterpret_cast<const bf16x4v *>(reinterpret_cast<const __bf16 *>(p) + idx);
+        return floatx4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+    }
+    return *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(p) + idx);
+}
+
+DG_DEV void store4_f32(void *p, int type, int64_t idx, floatx4 v)
+{
+    if (type == T_F16)
+        *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(p) + idx) =
+            half4v{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    else if (type == T_BF16)
+        *reinterpret_cast<bf16x4v *>(reinterpret_cast<__bf16 *>(p) + idx) =
+            bf16x4v{(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    else
+        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(p) + idx) = v;
+}
+
+// epi_store_f on four consecutive columns j .. j+3 (the same arithmetic per element)
+DG_DEV void epi_store4_f(const EpiArgs &e, int64_t i, int64_t j, floatx4 acc)
+{
+    floatx4 v = e.alpha * acc;
+    if (e.d_read) v += e.beta * load4_f32(e.D, e.out_type, i * e.ldd + j);
+    if (e.kind == E_BIAS || e.kind == E_BIAS_GELU) v += load4_f32(e.bias, e.bias_type, j);
+    if (e.kind == E_GELU || e.kind == E_BIAS_GELU)
+        v = floatx4{gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)};
+    store4_f32(e.C, e.out_type, i * e.ldc + j, v);
+}
+
+// epi_store_i on four consecutive columns j .. j+3 (the same arithmetic per element)
+DG_DEV void epi_store4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc)
+{
+    if (e.kind == E_RQ_I8 || e.kind == E_RQ_F16) {
+        floatx4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = __fmul_rn((float)acc[c], e.rq_scale);
+        if (e.bias) {
+            const floatx4 b = *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(e.bias) + j);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = __fadd_rn(v[c], b[c]);
+        }
+        if (e.kind == E_RQ_I8) {
+            i8x4v q;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float r = __builtin_rintf(v[c]);
+                r = r > 127.0f ? 127.0f : (r < -128.0f ? -128.0f : r);
+                q[c] = (signed char)(int)r;
+            }
+            *reinterpret_cast<i8x4v *>(reinterpret_cast<int8_t *>(e.C) + i * e.ldc + j) = q;
+        } else {
+            *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(e.C) + i * e.ldc + j) =
+                half4v{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        }
+        return;
+    }
+    intx4 v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = (int)((uint32_t)e.ialpha * (uint32_t)acc[c]);
+    if (e.d_read) {
+        const intx4 d = *reinterpret_cast<const intx4 *>(reinterpret_cast<const int32_t *>(e.D) + i * e.ldd + j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (int)((uint32_t)v[c] + (uint32_t)e.ibeta * (uint32_t)d[c]);
+    }
+    *reinterpret_cast<intx4 *>(reinterpret_cast<int32_t *>(e.C) + i * e.ldc + j) = v;
+}
+
 // Linear workgroup id -> tile index, keeping each accelerator die (XCD) on a
 // contiguous run of tiles.  Workgroups are dispatched round-robin over the 8
 // XCDs, so workgroup w runs on XCD w % 8; the run of XCD x starts at

@@ -212,6 +212,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             else if (o.force_m_tile && o.force_m_tile != s.bm) why = "forced M tile";
             else if (o.force_n_tile && o.force_n_tile != s.bn) why = "forced N tile";
             else if (o.force_k_tile && o.force_k_tile != BKE) why = "forced K tile";
+            else if (o.force_waves && o.force_waves != waves) why = "forced wave count";
             else if (S_eff != S && !o.force_split_k) why = "split collapses";
             if (why) {
                 ++pruned;
@@ -270,7 +271,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
 static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
                         std::vector<Candidate> &out, int &enumerated, int &pruned)
 {
-    if (o.force_m_tile || o.force_n_tile || o.force_k_tile) return;  // tiled-only options
+    if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves) return;  // tiled-only options
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
     const int occ_need = std::max(1, (int)std::ceil(o.target_occupancy * d.max_waves_per_simd - 1e-9));
     const double cpu = clk_per_us(d);
@@ -460,7 +461,8 @@ PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_pla
         res.message = "conflicting compute units: the tiled path runs on MFMA, VALU was requested";
         return res;
     }
-    if (o.force_path == DG_PATH_SKINNY && (o.force_m_tile || o.force_n_tile || o.force_k_tile)) {
+    if (o.force_path == DG_PATH_SKINNY &&
+        (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves)) {
         res.status = DG_ERR_CONFLICT;
         res.message = "forced tile sizes apply to the tiled path, the skinny path was forced";
         return res;

@@ -20,7 +20,7 @@ DG_ROW_MAJOR, DG_COL_MAJOR = 0, 1
 DG_EPI_NONE, DG_EPI_BIAS, DG_EPI_GELU_ERF, DG_EPI_BIAS_GELU_ERF, DG_EPI_REQUANT_I8, \
     DG_EPI_REQUANT_F16 = range(6)
 DG_UNIT_AUTO, DG_UNIT_MFMA, DG_UNIT_VALU = 0, 1, 2
-DG_PATH_AUTO, DG_PATH_TILED, DG_PATH_SKINNY = -1, 0, 1
+DG_PATH_AUTO, DG_PATH_TILED, DG_PATH_SKINNY = 0, 1, 2
 
 EPI = {"none": DG_EPI_NONE, "bias": DG_EPI_BIAS, "gelu_erf": DG_EPI_GELU_ERF,
        "bias_gelu_erf": DG_EPI_BIAS_GELU_ERF, "requant_i8": DG_EPI_REQUANT_I8,
@@ -48,11 +48,11 @@ class dg_plan_opts(C.Structure):
     _fields_ = [("force_m_tile", C.c_int32), ("force_n_tile", C.c_int32),
                 ("force_k_tile", C.c_int32), ("force_split_k", C.c_int32),
                 ("force_path", C.c_int32), ("unit", C.c_int32), ("lds_limit_bytes", C.c_int32),
-                ("target_occupancy", C.c_float), ("pad_k", C.c_int32)]
+                ("target_occupancy", C.c_float), ("pad_k", C.c_int32),
+                ("force_waves", C.c_int32)]
 
     def __init__(self, **kw):
         super().__init__()
-        self.force_path = DG_PATH_AUTO
         for k, v in kw.items():
             setattr(self, k, v)
 
