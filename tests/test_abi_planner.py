@@ -150,16 +150,17 @@ def test_forced_tile_and_split(off):
     o = dg.dg_plan_opts(force_m_tile=128, force_n_tile=128, force_split_k=2)
     p = off.plan(1024, 1024, 1024, opts=o)
     assert (p.m_tile, p.n_tile, p.split_k) == (128, 128, 2)
-    assert p.k_slice == 512 and p.n_main == 8 and p.n_tail == 0
+    assert p.k_slice == 512 and p.n_main == 16 and p.n_tail == 0
 
 
 def test_variable_k_schedule_tail(off):
-    # K = 4096 + 48: 64 full steps of 64 and one tail step of 48 (3 MFMA depths)
+    # K = 4096 + 48: 129 full steps of 32 and one tail step of 16 (one MFMA depth)
     o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_split_k=1)
     p = off.plan(512, 512, 4096 + 48, opts=o)
-    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (64, 64, 48, 1)
+    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (32, 129, 16, 1)
+    # int8, K = 4096 + 96: 65 full steps of 64 and one tail step of 32
     p = off.plan(512, 512, 4096 + 96, "i8", "i8", "i32", opts=o)
-    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (128, 32, 96, 1)
+    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (64, 65, 32, 1)
 
 
 def test_skinny_shapes_choose_streaming_path(off):
@@ -297,6 +298,6 @@ def test_planner_uses_the_compiled_resource_usage(off):
     p = off.plan(2048, 2048, 2048, opts=o)
     assert p.kernel_name.decode().endswith("w2x4") and p.waves_per_simd >= 2
     for nw, suffix in ((4, "w2x2"), (8, "w2x4")):
-        o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, force_waves=nw)
+        o = dg.dg_plan_opts(force_m_tile=256, force_waves=nw)
         p = off.plan(2048, 2048, 2048, opts=o)
         assert p.kernel_name.decode().endswith(suffix) and p.waves_per_wg == nw

@@ -257,16 +257,18 @@ def test_e2m1_tiled_small(h, M, N, K):
 
 def test_every_tiled_variant_on_a_ragged_problem(h):
     # each compiled tile shape, forced in turn, on a problem with ragged M and N,
-    # a K tail (K = 3 full steps + a partial one) and a K split
+    # a K tail (K = 7 full steps + a half step; e2m1 K is whole 32-groups, so
+    # 8 full steps) and a K split (slices of 4 and 3.5 steps: fewer steps than
+    # LDS stages)
     for path, name, colm in (("f16", "f16_2048x2048x8192_bias_gelu", False),
                              ("f16", "f16_2048x2048x8192_bias_gelu", True),
                              ("bf16", "bf16_16x4096x131072", False),
                              ("i8", "i8_4096x4096x4096", False),
                              ("i8", "i8_4096x4096x4096", True),
                              ("e2m1", "e2m1_4096x4096x4096", True)):
-        ktail = 3 * (128 if path == "i8" else 64) + (64 if path == "i8" else 32)
+        ktail = {"i8": 7 * 64 + 32, "e2m1": 8 * 32}.get(path, 7 * 32 + 16)
         w = synth.make(name, M=290, N=272, K=ktail)
-        for bm, bn, nw in ((256, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4)):
+        for bm, bn, nw in ((128, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4)):
             for s in (1, 2):
                 o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
                                     force_path=dg.DG_PATH_TILED, force_waves=nw)

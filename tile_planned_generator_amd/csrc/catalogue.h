@@ -14,7 +14,7 @@ namespace dg {
 //   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
 //   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
 #define DG_TILE_SHAPES(X, path, kmaj) \
-    X(path, kmaj, 256, 256, 2, 2)     \
+    X(path, kmaj, 128, 256, 2, 2)     \
     X(path, kmaj, 256, 256, 2, 4)     \
     X(path, kmaj, 256, 128, 2, 2)     \
     X(path, kmaj, 128, 128, 2, 2)     \
@@ -51,16 +51,38 @@ struct TiledShape {
     int path, b_kmajor, bm, bn, wm, wn;
 };
 
-constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 128 : 64; }
+// Fewest direct-to-LDS loads any wave issues per stage when load i of an
+// operand goes to wave i % nw (the scale loads counted from the last wave down).
+constexpr int tiled_min_loads_per_wave(int a_nl, int b_nl, int s_nl, int nw)
+{
+    int m = 1 << 30;
+    for (int w = 0; w < nw; ++w) {
+        const int ws = nw - 1 - w;
+        const int c = a_nl / nw + (w < a_nl % nw) + b_nl / nw + (w < b_nl % nw) + s_nl / nw +
+                      (ws < s_nl % nw);
+        m = c < m ? c : m;
+    }
+    return m;
+}
+
+constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 64 : 32; }
 constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
 
-// LDS bytes of one tiled variant (two stages of one K step each).  A and
-// 16-bit / int8 B take 128 bytes per row (or per K row of a row-major B: BN
-// columns of a 64-k or 128-k step); e2m1 B takes 32 bytes of codes plus 4 bytes
-// of scales per column.
-constexpr int tiled_lds_bytes(int path, int bm, int bn)
+// LDS bytes of one tiled variant: four stages of one K step each.  A and a
+// K-contiguous B take 64 bytes per row (per column of B), a row-major B 64 bytes
+// per column (BN columns of a 32-k or 64-k step); e2m1 B takes 16 bytes of codes
+// plus a 4-byte scale word per column.
+constexpr int tiled_stage_bytes(int path, int bm, int bn)
 {
-    return 2 * (bm * 128 + (path == 3 ? bn * 36 : bn * 128));
+    return bm * 64 + (path == 3 ? bn * 20 : bn * 64);
+}
+// The epilogue reuses the LDS to stage 32 rows of every wave's accumulators
+// (4-byte values, rows padded by 4): the allocation is the larger of the two.
+constexpr int tiled_lds_bytes(int path, int bm, int bn, int wm, int wn)
+{
+    return 4 * tiled_stage_bytes(path, bm, bn) > wm * wn * 32 * (bn / wn + 4) * 4
+               ? 4 * tiled_stage_bytes(path, bm, bn)
+               : wm * wn * 32 * (bn / wn + 4) * 4;
 }
 
 }  // namespace dg

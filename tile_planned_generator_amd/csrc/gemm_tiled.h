@@ -3,14 +3,20 @@
 // One workgroup computes a BM x BN tile of C over one K slice.
 //   - Operands go from HBM straight into LDS with buffer loads that write LDS
 //     directly (buffer_load_dwordx4 ... lds): no staging registers and no LDS
-//     store instructions.  Two LDS stages: while the MFMAs consume stage s, the
-//     loads of step s+1 fill the other stage; one vmcnt wait and one barrier per
-//     step.  The buffer range check returns zeros past the end of an operand, so
-//     ragged rows and K tails need no clamping.
-//   - A (and a K-contiguous B) is kept as rows of 128 bytes (eight 16-byte
-//     chunks, one K step) whose chunk index is XORed with (row >> 1) & 7, so the
-//     16 rows a 16-lane phase of a fragment read touches hit 16 distinct
-//     16-byte bank groups of gfx950's 64-bank LDS.
+//     store instructions.  The buffer range check returns zeros past the end of
+//     an operand, so ragged rows need no clamping.
+//   - Four LDS stages of one K step each (32 k for 16-bit and e2m1 operands, 64 k
+//     for int8: two MFMA k-substeps).  Step st runs its first substep, then one
+//     barrier, then its second substep; the barrier is placed where every wave
+//     holds both fragments of stage st in registers, so right after it the loads
+//     of stage st+4 are issued into stage st's buffer.  Loads therefore have
+//     three steps to land.  The barrier waits only for this wave's loads of the
+//     next stage (vmcnt with the later stages still in flight) and for its LDS
+//     reads; the workgroup fence of __syncthreads would wait for every load.
+//   - A (and a K-contiguous B) is kept as rows of 64 bytes (four 16-byte chunks,
+//     one K step) whose chunk index is XORed with (row >> 2) & 3, so the 16 rows a
+//     16-lane phase of a fragment read touches hit 16 distinct 16-byte bank
+//     groups of gfx950's 64-bank LDS.
 //   - A row-major B (N contiguous) is kept as it is in memory, K rows of BN
 //     columns, and read with the transposing LDS reads of gfx950
 //     (ds_read_b64_tr_b16 / ds_read_b64_tr_b8): within each group of 16 lanes,
@@ -20,17 +26,19 @@
 //     neighbouring columns hand every lane the consecutive K values of one
 //     column - the MFMA B operand.  The 16-byte chunks of row k are XORed with
 //     4*(k & 3) (b16) or 2*(k & 7) (b8) so those rows fall into distinct banks.
-//   - e2m1 codes are staged packed (two per byte), chunk-major, with their
-//     fp16 group scales, and decoded to fp16 when the fragment is read
-//     (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then a packed fp16 multiply
-//     by the group scale).
-//   - MFMA fragments are read from LDS one k-substep ahead of the MFMAs that use
-//     them; accumulators stay in registers for the whole K range (32x32 blocks:
+//     These reads are issued from inline assembly: the compiler treats its own
+//     transposing-read builtins as possibly aliasing every in-flight
+//     direct-to-LDS load and would wait for all of them before each read.  Their
+//     completion is awaited explicitly, tied to the fragment registers.
+//   - e2m1 codes are staged packed (two per byte), 16 bytes per column and step,
+//     with the dword holding the column's fp16 group scale, and decoded to fp16
+//     when the fragment is read (v_cvt_scalef32_pk_f16_fp4 with a unit scale,
+//     then a packed fp16 multiply by the group scale).
+//   - Accumulators stay in registers for the whole K range (32x32 blocks:
 //     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8).
-//   - The K schedule is n_main steps of the full step (64 k for 16-bit, 128 k
-//     for int8) then at most one smaller tail step that still fills whole
-//     MFMAs (the pages' variable K step, [generator] DeepGEMM article, kwkr.cn,
-//     section 2.2, first layer).
+//   - The K schedule is n_main full steps then at most one half step (one
+//     substep) for the tail (the pages' variable K step, [generator] DeepGEMM
+//     article, kwkr.cn, section 2.2, first layer).
 //   - The epilogue (alpha, beta*D, bias, GELU, requantise, conversion) runs once
 //     per output element after the K loop, four columns per lane with vector
 //     loads and stores; with a K split the raw fp32 / int32 partials go to the
@@ -43,7 +51,6 @@
 
 namespace dg {
 
-typedef short short4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 #define DG_LDS __attribute__((address_space(3)))
 
@@ -62,44 +69,91 @@ DG_DEV void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (DG_LDS void *)lds, 16, (int)off, 0, 0, 0);
 }
 
-DG_DEV unsigned short buf_ld2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// 4 bytes per lane from buffer offset `off` (a multiple of 4), written to LDS at
+// lds + 4 * lane.
+DG_DEV void buf_ld4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds)
 {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (DG_LDS void *)lds, 4, (int)off, 0, 0, 0);
+}
+
+// Transposing LDS reads at LDS byte address addr + OFF (see the header).
+template <int OFF>
+DG_DEV u32x2 lds_tr16(uint32_t addr)
+{
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+template <int OFF>
+DG_DEV u32x2 lds_tr8(uint32_t addr)
+{
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most vm vector-memory and lgkm
+// LDS/scalar operations outstanding, export counter not waited on.
+constexpr int waitcnt_imm(int vm, int lgkm)
+{
+    return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+// Wait until at most N of this wave's buffer loads are outstanding and all its
+// LDS operations are done, then join the workgroup barrier.  The wait is the
+// builtin, so the compiler's own wait insertion knows what it covers; the
+// barrier is assembly with a memory clobber so that no LDS access moves across
+// it (the barrier builtin alone does not order memory, and __syncthreads adds a
+// fence that waits for every outstanding load).
+template <int N>
+DG_DEV void wait_vm_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
+    asm volatile("s_barrier" : : : "memory");
 }
 
 template <int PATH, int BKMAJ, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 {
     constexpr int NW = WM * WN;
-    constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr bool IS_I8 = PATH == P_I8;
     constexpr bool IS_E2M1 = PATH == P_E2M1;
-    constexpr int BKE = IS_I8 ? 128 : 64;      // k elements per full step
-    constexpr int KSUB = IS_I8 ? 32 : 16;      // k elements per MFMA
-    constexpr int NSUB = BKE / KSUB;           // MFMA k-substeps per full step
-    constexpr int ESZ = IS_I8 ? 1 : 2;         // bytes per element of A and of a 16-bit / int8 B
-    constexpr int A_BYTES = BM * 128;
-    constexpr int B_TILE = IS_E2M1 ? BN * 32 : BN * 128;   // e2m1: BKE/2 bytes of codes per column
-    constexpr int S_BYTES = IS_E2M1 ? BN * 4 : 0;
+    constexpr bool B_TR = !BKMAJ && !IS_E2M1;          // row-major B, transposing reads
+    constexpr int BKE = tiled_bk_elems(PATH);          // k elements per step
+    constexpr int KSUB = tiled_ksub(PATH);             // k elements per MFMA
+    static_assert(BKE == 2 * KSUB, "two substeps per step");
+    constexpr int NBUF = 4;
+    constexpr int ESZ = IS_I8 ? 1 : 2;                 // bytes per element of A and of a 16-bit / int8 B
+    static_assert(BKE * ESZ == 64, "64-byte rows");
+    constexpr int A_BYTES = BM * 64;
+    constexpr int B_TILE = IS_E2M1 ? BN * 16 : BN * 64;   // e2m1: BKE/2 bytes of codes per column
+    constexpr int S_BYTES = IS_E2M1 ? BN * 4 : 0;          // e2m1: one scale dword per column
     constexpr int STAGE = A_BYTES + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    static_assert(2 * STAGE == tiled_lds_bytes(PATH, BM, BN), "LDS size");
-    // direct-to-LDS loads: every wave instruction fills 1 KB (64 lanes x 16 B)
-    constexpr int A_NL = A_BYTES / 1024, B_NL = B_TILE / 1024;   // 1 KB loads per step
-    constexpr int A_LD = (A_NL + NW - 1) / NW;                   // per wave and step
-    constexpr int B_LD = (B_NL + NW - 1) / NW;
-    static_assert(A_NL * 1024 == A_BYTES && B_NL * 1024 == B_TILE, "tile not whole 1 KB loads");
-    constexpr int SC_IT = IS_E2M1 ? (BN * 2 + NT - 1) / NT : 0;
+    constexpr int LDS_BYTES = tiled_lds_bytes(PATH, BM, BN, WM, WN);
+    static_assert(STAGE == tiled_stage_bytes(PATH, BM, BN), "stage size");
+    static_assert(STAGE % 1024 == 0 || IS_E2M1, "stage alignment");
+    // direct-to-LDS loads: a 16-byte load fills 1 KB (64 lanes), a dword load 256 B.
+    // Load i of an operand is issued by wave i % NW (the scale loads from the
+    // last wave down, to even out the per-wave counts).
+    constexpr int A_NL = A_BYTES / 1024, B_NL = B_TILE / 1024, S_NL = S_BYTES / 256;
+    static_assert(A_NL * 1024 == A_BYTES && B_NL * 1024 == B_TILE && S_NL * 256 == S_BYTES,
+                  "tile not whole loads");
+    constexpr int A_LD = (A_NL + NW - 1) / NW, B_LD = (B_NL + NW - 1) / NW, S_LD = (S_NL + NW - 1) / NW;
+    constexpr int LPS = tiled_min_loads_per_wave(A_NL, B_NL, S_NL, NW);   // fewest loads a wave issues per stage
+    static_assert(3 * LPS < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(DG_LDS char *)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS bases
     const int wm = wave / WN, wn = wave % WN;
     const int lr = lane & 31, kg = lane >> 5;
 
@@ -119,7 +173,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     const int kbeg = split * p.k_slice;
     const int kend = min(p.K, kbeg + p.k_slice);
     const int nfull = (kend - kbeg) / BKE;
-    const int tail = (kend - kbeg) - nfull * BKE;
+    const int tail = (kend - kbeg) - nfull * BKE;   // 0 or KSUB (K is a multiple of KSUB)
     const int nsteps = nfull + (tail ? 1 : 0);
 
     const int M = p.M, N = p.N;
@@ -142,30 +196,40 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         Bbase = reinterpret_cast<const char *>(p.B) + (int64_t)n0 * ESZ;
         b_bytes = (uint32_t)((p.K - 1) * (int64_t)ldb_b + (nr - n0) * ESZ);
     }
-    const char *Sbase = IS_E2M1 ? reinterpret_cast<const char *>(p.scale) + (int64_t)n0 * p.ld_scale * 2
-                                : nullptr;
-    const uint32_t s_bytes = IS_E2M1 ? (uint32_t)((N - n0) * (int64_t)p.ld_scale * 2) : 0;
+    // e2m1 scales: fp16 scale (n, g) sits at element n * ld_scale + g.  They are
+    // fetched as the aligned dword that holds them, from a descriptor based at
+    // the scale pointer rounded down to 4 bytes; `smis` is the byte distance
+    // of the pointer from that base (0 or 2).  The range is rounded up to whole
+    // dwords: the last dword never leaves the 4-byte word holding the array's end.
+    const char *Sbase = nullptr;
+    uint32_t s_bytes = 0, smis = 0;
+    if constexpr (IS_E2M1) {
+        const uintptr_t sp = reinterpret_cast<uintptr_t>(p.scale);
+        smis = (uint32_t)(sp & 3);
+        Sbase = reinterpret_cast<const char *>(sp - smis);
+        const int64_t last = (int64_t)(N - 1) * p.ld_scale + p.K / 32;   // one past the last element
+        s_bytes = (uint32_t)((smis + 2 * last + 3) & ~(int64_t)3);
+    }
 
-    // ---- per-lane source offsets of this wave's direct-to-LDS loads.  Load i of
-    // wave w fills LDS bytes [(i*NW + w) * 1024, +1024) of the operand region;
-    // lane l writes 16-byte chunk pc = (i*NW + w)*64 + l of it.  Rows past the
-    // operand start at or beyond its extent, so their loads return zeros.
+    // ---- per-lane source offsets of this wave's direct-to-LDS loads.  Load q of
+    // an operand fills LDS bytes [q * 1024, +1024) of its region; lane l writes
+    // 16-byte chunk pc = q * 64 + l of it.  Rows past the operand start at or
+    // beyond its extent: their loads return zeros.
     uint32_t oa[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int pc = (i * NW + wave) * 64 + lane;
-        const int r = pc >> 3, c = (pc & 7) ^ ((r >> 1) & 7);
+        const int r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
         oa[i] = r * lda_b + c * 16;
     }
     uint32_t ob[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
         const int pc = (i * NW + wave) * 64 + lane;
-        if constexpr (IS_E2M1) {            // chunk-major: [chunk 0/1][BN columns][16 B]
-            const int c = pc / BN, r = pc % BN;
-            ob[i] = r * ldb_b + c * 16;
+        if constexpr (IS_E2M1) {            // [BN columns][16 B]
+            ob[i] = pc * ldb_b;
         } else if constexpr (BKMAJ) {       // as A, rows are columns of B
-            const int r = pc >> 3, c = (pc & 7) ^ ((r >> 1) & 7);
+            const int r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
             ob[i] = r * ldb_b + c * 16;
         } else {                            // K rows of BN columns
             const int k = pc / CPR, pcol = pc % CPR;
@@ -173,51 +237,44 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             ob[i] = k * ldb_b + (pcol ^ sw) * 16;
         }
     }
-    uint32_t os[SC_IT > 0 ? SC_IT : 1];
-    if constexpr (IS_E2M1) {
+    const int swave = NW - 1 - wave;        // scale loads go from the last wave down
+    uint32_t os[S_LD > 0 ? S_LD : 1];
 #pragma unroll
-        for (int i = 0; i < SC_IT; ++i) {
-            const int q = min(tid + i * NT, BN * 2 - 1), r = q >> 1, g = q & 1;
-            os[i] = (uint32_t)(r * p.ld_scale + g) * 2;
-        }
+    for (int i = 0; i < S_LD; ++i) {
+        const int col = (i * NW + swave) * 64 + lane;   // byte of scale (n0 + col, 0) from Sbase
+        os[i] = smis + 2 * (uint32_t)((n0 + col) * p.ld_scale);
     }
-    unsigned short rs[SC_IT > 0 ? SC_IT : 1];
 
-    // Issue the loads of the step starting at k0 into LDS stage `buf` (the e2m1
-    // scales go through registers and are written by store_scales).
-    auto load_stage = [&](int k0, int buf) {
-        char *sA = smem + buf * STAGE;
-        char *sB = sA + A_BYTES;
+    // Issue the loads of step j (k0 = kbeg + j * BKE) into LDS stage j % NBUF.
+    // Steps past the last one issue the same loads over empty ranges: they only
+    // write zeros into a stage nobody reads again, and keep every wave's count
+    // of outstanding loads the same at each barrier.
+    auto load_stage = [&](int j) {
+        const bool real = j < nsteps;
+        const int k0 = real ? kbeg + j * BKE : 0;
+        char *sb = smem + (j & (NBUF - 1)) * STAGE;
         const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(Abase + (int64_t)k0 * ESZ, a_bytes - (uint32_t)(k0 * ESZ));
+            make_rsrc(Abase + (int64_t)k0 * ESZ, real ? a_bytes - (uint32_t)(k0 * ESZ) : 0u);
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             if (A_NL % NW == 0 || i * NW + wave < A_NL)   // wave-uniform
-                buf_ld16_lds(rA, oa[i], sA + (i * NW + wave) * 1024);
+                buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
         uint32_t kb;
         if constexpr (IS_E2M1) kb = (uint32_t)(k0 >> 1);
         else if constexpr (BKMAJ) kb = (uint32_t)(k0 * ESZ);
         else kb = (uint32_t)k0 * ldb_b;
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + kb, b_bytes - kb);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + kb, real ? b_bytes - kb : 0u);
 #pragma unroll
         for (int i = 0; i < B_LD; ++i)
             if (B_NL % NW == 0 || i * NW + wave < B_NL)   // wave-uniform
-                buf_ld16_lds(rB, ob[i], sB + (i * NW + wave) * 1024);
+                buf_ld16_lds(rB, ob[i], sb + A_BYTES + (i * NW + wave) * 1024);
         if constexpr (IS_E2M1) {
-            const uint32_t sb = (uint32_t)(k0 >> 5) * 2;
-            const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sbase + sb, s_bytes - sb);
+            const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sbase, real ? s_bytes : 0u);
+            const uint32_t gb = 2 * (uint32_t)(k0 >> 5);
 #pragma unroll
-            for (int i = 0; i < SC_IT; ++i) rs[i] = buf_ld2(rS, os[i]);
-        }
-    };
-    auto store_scales = [&](int buf) {
-        if constexpr (IS_E2M1) {
-            unsigned short *sS = reinterpret_cast<unsigned short *>(smem + buf * STAGE + A_BYTES + B_TILE);
-#pragma unroll
-            for (int i = 0; i < SC_IT; ++i) {
-                const int q = tid + i * NT;
-                if (q < BN * 2) sS[q] = rs[i];
-            }
+            for (int i = 0; i < S_LD; ++i)
+                if (S_NL % NW == 0 || i * NW + swave < S_NL)   // wave-uniform
+                    buf_ld4_lds(rS, (os[i] + gb) & ~3u, sb + A_BYTES + B_TILE + (i * NW + swave) * 256);
         }
     };
 
@@ -235,55 +292,85 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         u32x4 a[FM];
         u32x4 b[FN];
     };
-    // transposing-read addressing of a row-major B tile: lane L of 16-lane group
-    // g supplies K row (b16) kb + (L >> 2) at column 16*(g&1) + 4*(L&3), or (b8)
-    // kb + (L >> 1) at column 16*(g&1) + 8*(L&1)
+    // Per-lane LDS byte offsets (within a stage) of the fragment reads.
+    //   A / K-major B: row `row`, logical chunk 2s + kg.
+    //   row-major B (transposing reads): lane L of 16-lane group g supplies K row
+    //   (b16) kb + (L >> 2) at column 16*(g&1) + 4*(L&3), or (b8) kb + (L >> 1) at
+    //   column 16*(g&1) + 8*(L&1); kb = KSUB*s + 8*(g>>1) (b16) or 16*(g>>1) (b8).
+    //   The two reads of a block cover K rows kb.. and kb+4.. (b16) / kb+8.. (b8);
+    //   row k and k + 4 (k + 8) share their swizzle, as do substeps 0 and 1, so
+    //   those reads differ by immediate offsets.
     const int grp16 = lane >> 4, L16 = lane & 15;
-    auto read_frag = [&](const char *sA, const char *sB, int s, Frag &f) {
+    uint32_t boff[FN];
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+        const int col0 = wn * WTN + ni * 32;
+        if constexpr (B_TR) {
+            if constexpr (!IS_I8) {
+                const int col = col0 + 16 * (grp16 & 1) + 4 * (L16 & 3);
+                const int k = 8 * (grp16 >> 1) + (L16 >> 2);
+                boff[ni] = A_BYTES + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
+            } else {
+                const int col = col0 + 16 * (grp16 & 1) + 8 * (L16 & 1);
+                const int k = 16 * (grp16 >> 1) + (L16 >> 1);
+                boff[ni] = A_BYTES + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
+            }
+        } else {
+            boff[ni] = 0;
+        }
+    }
+    // e2m1: parity of the scale's half within its dword, at group 0
+    uint32_t spar[FN];
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+        spar[ni] = IS_E2M1 ? ((smis >> 1) + (uint32_t)((n0 + wn * WTN + ni * 32 + lr) * p.ld_scale)) & 1u : 0u;
+
+    auto read_frag = [&](int buf, auto s_tag, Frag &f, int g) {
+        constexpr int s = decltype(s_tag)::value;
+        const char *sA = smem + buf * STAGE;
+        const char *sB = sA + A_BYTES;
         const int c = 2 * s + kg;
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi) {
             const int row = wm * WTM + mi * 32 + lr;
-            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
         }
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni) {
             const int col0 = wn * WTN + ni * 32;
             if constexpr (IS_E2M1) {
                 const int row = col0 + lr;
-                const int w = 2 * s + kg;   // 4-byte word of the column's 32 code bytes
-                const unsigned codes =
-                    *reinterpret_cast<const unsigned *>(sB + (w >> 2) * (BN * 16) + row * 16 + (w & 3) * 4);
-                const _Float16 sc =
-                    reinterpret_cast<const _Float16 *>(sB + B_TILE)[row * 2 + (s >> 1)];
-                f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, sc));
+                const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + (2 * s + kg) * 4);
+                const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
+                const unsigned short sh = (unsigned short)(((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd);
+                f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
             } else if constexpr (BKMAJ) {
                 const int row = col0 + lr;
-                f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-            } else if constexpr (!IS_I8) {
-                // two reads of 4 K rows each: K = 16s + 8*(g>>1) + {0..3, 4..7}
-                const int col = col0 + 16 * (grp16 & 1) + 4 * (L16 & 3);
-                const int kb = KSUB * s + 8 * (grp16 >> 1) + (L16 >> 2);
-                const int cc = col >> 3, cb = (col & 7) * 2;
-                const int k1 = kb, k2 = kb + 4;
-                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DG_LDS short4v *)(sB + k1 * RB + ((cc ^ ((4 * (k1 & 3)) % CPR)) << 4) + cb));
-                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DG_LDS short4v *)(sB + k2 * RB + ((cc ^ ((4 * (k2 & 3)) % CPR)) << 4) + cb));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                f.b[ni] = u32x4{l2.x, l2.y, h2.x, h2.y};
+                f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
             } else {
-                // two reads of 8 K rows each: K = 32s + 16*(g>>1) + {0..7, 8..15}
-                const int col = col0 + 16 * (grp16 & 1) + 8 * (L16 & 1);
-                const int kb = KSUB * s + 16 * (grp16 >> 1) + (L16 >> 1);
-                const int cc = col >> 4, cb = col & 15;
-                const int k1 = kb, k2 = kb + 8;
-                const int2v lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (DG_LDS int2v *)(sB + k1 * RB + ((cc ^ ((2 * (k1 & 7)) % CPR)) << 4) + cb));
-                const int2v hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (DG_LDS int2v *)(sB + k2 * RB + ((cc ^ ((2 * (k2 & 7)) % CPR)) << 4) + cb));
-                f.b[ni] = u32x4{(unsigned)lo.x, (unsigned)lo.y, (unsigned)hi.x, (unsigned)hi.y};
+                const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
+                u32x2 lo, hi;
+                if constexpr (!IS_I8) {
+                    lo = lds_tr16<KSUB * s * RB>(a);
+                    hi = lds_tr16<KSUB * s * RB + 4 * RB>(a);
+                } else {
+                    lo = lds_tr8<KSUB * s * RB>(a);
+                    hi = lds_tr8<KSUB * s * RB + 8 * RB>(a);
+                }
+                f.b[ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
+        }
+    };
+    // The transposing reads are invisible to the compiler's wait insertion:
+    // wait for all LDS reads, then tie the B registers to that point so the
+    // MFMAs that use them cannot move above it.  The memory clobber keeps the
+    // next reads below it.  Call it before issuing the reads of the next
+    // fragments, or it would wait for those as well.
+    auto settle = [&](Frag &f) {
+        if constexpr (B_TR) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[ni]) : : "memory");
         }
     };
     auto mfmas = [&](const Frag &f) {
@@ -305,42 +392,82 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                         acc[mi][ni], 0, 0, 0);
             }
     };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    const int g0 = kbeg >> 5;   // e2m1 scale group of step 0
 
-    // ---- main loop: stage st & 1 is consumed while step st+1 streams into the other
-    Frag fr[2];
-    if (nsteps > 0) {
-        load_stage(kbeg, 0);
-        store_scales(0);
-        __builtin_amdgcn_s_waitcnt(0);   // every counter at zero: the LDS-direct loads have landed
-        __syncthreads();
-        read_frag(smem, smem + A_BYTES, 0, fr[0]);
-    }
-    for (int st = 0; st < nsteps; ++st) {
-        const int cur = st & 1;
-        const bool more = st + 1 < nsteps;
-        if (more) load_stage(kbeg + (st + 1) * BKE, cur ^ 1);
-        const char *sA = smem + cur * STAGE;
-        const char *sB = sA + A_BYTES;
-        const int nsub = st < nfull ? NSUB : tail / KSUB;
+    // ---- main loop (four waves).  One step: [substep 0 of stage st, reads of
+    // substep 1 in its shadow] barrier [loads of stage st+4, reads of substep 0
+    // of stage st+1, substep 1 of stage st].  The barrier guarantees that stage st+1 has landed
+    // for every wave (the loads of stages st+2 and st+3 may still be in flight)
+    // and that no wave still reads stage st, whose buffer takes stage st+4.  The
+    // body is branch-free but for the MFMAs of a final half step.
+    Frag f0, f1;
+    if constexpr (NW == 8) {
+        // Eight waves: two groups of four (waves 0-3 and 4-7, one of each per
+        // SIMD) alternate a memory phase (read both fragments of stage st, issue
+        // the loads of stage st+3, wait for this wave's loads of stage st+1) and
+        // a compute phase (the MFMAs of stage st only), with a barrier after each
+        // phase.  The second group runs one barrier behind, so on every SIMD one
+        // wave computes while the other does its memory phase.  Stage st is read
+        // by the first group between barriers 2st+1 and 2st+2 and by the second
+        // between 2st+2 and 2st+3; its buffer is refilled (stage st+4) in the
+        // memory phases that start at or after barrier 2st+3.
+        const bool lag = wave >= 4;
+        auto bar = [] {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_barrier" : : : "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto tie = [&](Frag &f) {
+            if constexpr (B_TR) {
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-            if (s < nsub) {
-                if (s + 1 < nsub) read_frag(sA, sB, s + 1, fr[(s + 1) & 1]);
-                mfmas(fr[s & 1]);
+                for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[ni]) : : "memory");
             }
+        };
+#pragma unroll
+        for (int j = 0; j < NBUF - 1; ++j) load_stage(j);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * LPS, 15));
+        bar();
+        if (lag) bar();
+        for (int st = 0; st < nsteps; ++st) {
+            const int buf = st & (NBUF - 1);
+            // memory phase
+            read_frag(buf, S0{}, f0, g0 + st);
+            read_frag(buf, S1{}, f1, g0 + st);
+            load_stage(st + NBUF - 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * LPS, 0));
+            tie(f0);
+            tie(f1);
+            bar();
+            // compute phase
+            mfmas(f0);
+            if (st < nfull) mfmas(f1);   // not on a final half step
+            bar();
         }
-        if (more) {
-            store_scales(cur ^ 1);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            read_frag(smem + (cur ^ 1) * STAGE, smem + (cur ^ 1) * STAGE + A_BYTES, 0, fr[0]);
+        if (!lag) bar();
+    } else {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) load_stage(j);
+        wait_vm_barrier<(NBUF - 1) * LPS>();
+        read_frag(0, S0{}, f0, g0);
+        for (int st = 0; st < nsteps; ++st) {
+            const int buf = st & (NBUF - 1);
+            settle(f0);
+            read_frag(buf, S1{}, f1, g0 + st);
+            mfmas(f0);
+            wait_vm_barrier<(NBUF - 2) * LPS>();
+            settle(f1);
+            load_stage(st + NBUF);
+            read_frag((st + 1) & (NBUF - 1), S0{}, f0, g0 + st + 1);
+            if (st < nfull) mfmas(f1);   // not on a final half step
         }
     }
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
     // and stores them four columns per lane, row-contiguously.
     constexpr int RP = WTN + 4;   // padded row pitch (elements) of the staging area
-    static_assert(NW * 32 * RP * 4 <= 2 * STAGE, "epilogue staging");
+    static_assert(NW * 32 * RP * 4 <= LDS_BYTES, "epilogue staging");
     __syncthreads();   // every wave is done with the last K stage
     using ScalarT = typename std::conditional<IS_I8, int32_t, float>::type;
     using Vec4 = typename std::conditional<IS_I8, intx4, floatx4>::type;

@@ -189,7 +189,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
         int vgpr, agpr;
         if (acc + other <= 256) { vgpr = acc + other; agpr = 0; }
         else { vgpr = other; agpr = acc; }
-        int lds = tiled_lds_bytes(s.path, s.bm, s.bn);
+        int lds = tiled_lds_bytes(s.path, s.bm, s.bn, s.wm, s.wn);
         if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn)) {
             vgpr = r->vgpr;
             agpr = r->agpr;
