@@ -444,6 +444,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             ra.M = (int)M;
             ra.N = (int)N;
             ra.is_int = pr.path == P_I8;
+            ra.lanes = c.split_k <= 8 ? 1 : (c.split_k <= 32 ? 4 : 16);
             ra.epi = ea;
             he = launch_reduce(ra, st);
             if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));

@@ -55,11 +55,14 @@ struct SkinnyArgs {
     EpiArgs epi;
 };
 
-// Split-K reduction: out = epilogue(sum over s ascending of ws[s]).
+// Split-K reduction: out = epilogue(sum of ws[s] over the slices s).  `lanes`
+// lanes share one output (a power of two, at most 16): lane t sums a contiguous
+// run of slices in ascending order and the runs are combined in a fixed pattern.
 struct ReduceArgs {
     const void *ws;
     int split_k, M, N;
     int is_int;
+    int lanes;
     EpiArgs epi;
 };
 

@@ -41,6 +41,7 @@ namespace dg {
 namespace {
 
 constexpr int SKINNY_A_LDS = 32768;   // must match skinny.hip
+constexpr int E2M1_A_LDS = 32768;     // must match skinny.hip
 
 const TiledShape k_tiled_shapes[] = {
 #define DG_TS(path, kmaj, bm, bn, wm, wn) {path, kmaj, bm, bn, wm, wn},
@@ -268,6 +269,9 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
     }
 }
 
+// Skinny families: a requested split S whose rounded slices give fewer slices
+// (S_eff) is kept as a plan with S_eff slices (the streaming kernels take any
+// slice count).
 static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
                         std::vector<Candidate> &out, int &enumerated, int &pruned)
 {
@@ -277,8 +281,10 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
     const double cpu = clk_per_us(d);
     const double out_bytes = (double)pr.M * pr.N * elt_bytes(pr.out_type) * (pr.beta_nz ? 2 : 1);
 
-    auto finish = [&](Candidate &c, double b_bytes, double valu_lane_ops) {
-        const double waves_active = c.grid_y * (double)c.grid_x * 4.0;
+    // `cols_per_wave`: columns one wave streams; waves past N idle, and a partly
+    // filled wave counts for the share of its lanes that have columns.
+    auto finish = [&](Candidate &c, double b_bytes, double valu_lane_ops, int cols_per_wave) {
+        const double waves_active = c.grid_y * (double)pr.N / cols_per_wave;
         const double eff = std::min(1.0, waves_active / (d.cu_count * 8.0));
         const double t_mem = hbm_us(b_bytes, d) / (0.92 * std::max(eff, 1e-3));
         const double t_valu = valu_lane_ops / (d.cu_count * 64.0 * cpu);
@@ -314,7 +320,6 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 else if (lds > lds_cap) why = "LDS over budget";
                 else if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
-                else if (S_eff != S && !o.force_split_k) why = "split collapses";
                 if (why) {
                     ++pruned;
                     continue;
@@ -332,7 +337,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
                 finish(c, (double)pr.K * pr.N * 2 + pr.M * pr.K * 2.0,
-                       (double)s.mr * pr.K * pr.N * 1.3 + (double)pr.K * pr.N);
+                       (double)s.mr * pr.K * pr.N * 1.3 + (double)pr.K * pr.N, wcols);
                 char nm[64];
                 std::snprintf(nm, sizeof nm, "skinny_valu_%s_mr%d_lpr%d", path_name(pr.path), s.mr, s.lpr);
                 c.name = nm;
@@ -360,7 +365,6 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 const char *why = nullptr;
                 if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
-                else if (S_eff != S && !o.force_split_k) why = "split collapses";
                 if (why) {
                     ++pruned;
                     continue;
@@ -378,7 +382,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
                 finish(c, (double)pr.K * pr.N * 2 + 16.0 * pr.K * 2 * c.grid_x,
-                       (double)pr.K * pr.N * 0.6);
+                       (double)pr.K * pr.N * 0.6, 128);
                 char nm[64];
                 std::snprintf(nm, sizeof nm, "skinny_mfma_%s", path_name(pr.path));
                 c.name = nm;
@@ -399,11 +403,14 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 if (S_eff == 1) k_slice = (int)pr.K;
                 int vg = 48;
                 if (const ResRow *r = find_res(F_SKINNY_E2M1, mr)) vg = r->vgpr + r->agpr;
-                const int occ = waves_per_simd(vg, 0, 4, d);
+                int lds_e = E2M1_A_LDS;
+                if (const ResRow *r = find_res(F_SKINNY_E2M1, mr)) lds_e = r->lds;
+                const int occ = waves_per_simd(vg, lds_e, 4, d);
                 const char *why = nullptr;
-                if (occ < occ_need) why = "occupancy below target";
+                if ((int64_t)k_slice * mr * 2 > E2M1_A_LDS) why = "A slice over LDS staging";
+                else if (lds_e > lds_cap) why = "LDS over budget";
+                else if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
-                else if (S_eff != S && !o.force_split_k) why = "split collapses";
                 if (why) {
                     ++pruned;
                     continue;
@@ -412,16 +419,16 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.family = F_SKINNY_E2M1;
                 c.kernel_id = id;
                 c.unit = DG_UNIT_VALU;
-                c.m_tile = mr; c.n_tile = 4; c.waves = 4;
+                c.m_tile = mr; c.n_tile = 16; c.waves = 4;
                 c.split_k = S_eff; c.k_slice = k_slice;
                 schedule(k_slice, 32 * 64, c.k_main, c.n_main, c.k_tail, c.n_tail);
                 if (c.k_tail) { c.n_tail = 1; }
-                c.lds = 0; c.vgpr = vg; c.agpr = 0; c.waves_per_simd = occ;
-                c.grid_x = (int)ceil_div(pr.N, 4);
+                c.lds = lds_e; c.vgpr = vg; c.agpr = 0; c.waves_per_simd = occ;
+                c.grid_x = (int)ceil_div(pr.N, 16);
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
                 finish(c, (double)pr.K * pr.N * 0.5 + (double)pr.N * (pr.K / 32) * 2 + pr.M * pr.K * 2.0,
-                       (double)pr.N * (pr.K / 32) * (24.0 + 16.0 * mr));
+                       (double)pr.N * (pr.K / 32) * (24.0 + 16.0 * mr), 4);
                 char nm[64];
                 std::snprintf(nm, sizeof nm, "skinny_e2m1_mr%d", mr);
                 c.name = nm;

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
 {
     constexpr int RPI = 64 / LPR;       // row groups per wave
     constexpr int WCOLS = LPR * 8;      // columns per wave
-    constexpr int U = 8;                // rows in flight per lane
+    constexpr int U = 8;                // rows per lane and batch
     __shared__ __attribute__((aligned(16))) unsigned short sA[SKINNY_A_LDS / 2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,6 +58,20 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
     const int L = kend - kbeg;
     const int M = p.M;
 
+    const char *Bb = reinterpret_cast<const char *>(p.B) + (int64_t)(col < p.N ? col : 0) * 2 +
+                     (int64_t)kbeg * p.ldb * 2;
+    const int64_t ldb_b = p.ldb * 2;
+    // batches of U rows per lane (U * RPI rows per wave), then single rows
+    const int nmain = L / (U * RPI);
+    auto load_batch = [&](int it, u32x4 (&b)[U]) {
+        const int r = g + it * U * RPI;
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = ld16_nt(Bb + (int64_t)(r + u * RPI) * ldb_b);
+    };
+    // the first batch of B is in flight while A is staged
+    u32x4 b0[U], b1[U];
+    if (nmain > 0) load_batch(0, b0);
+
     // stage A[0:M][kbeg:kend]
     const unsigned short *A = reinterpret_cast<const unsigned short *>(p.A);
     for (int idx = tid; idx < MR * L; idx += 256) {
@@ -66,22 +80,14 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
     }
     __syncthreads();
 
-    const char *Bb = reinterpret_cast<const char *>(p.B) + (int64_t)(col < p.N ? col : 0) * 2;
-    const int64_t ldb_b = p.ldb * 2;
-
     float acc[MR][8];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
 
-    // K schedule of the slice: main steps of U*RPI rows, then single-row-group steps.
-    const int nmain = L / (U * RPI);
-    int r = g;
-    for (int it = 0; it < nmain; ++it, r += U * RPI) {
-        u32x4 b[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = ld16_nt(Bb + (int64_t)(kbeg + r + u * RPI) * ldb_b);
+    auto fma_batch = [&](int it, const u32x4 (&b)[U]) {
+        const int r = g + it * U * RPI;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float w[8];
@@ -93,9 +99,18 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
                 for (int e = 0; e < 8; ++e) acc[m][e] += a * w[e];
             }
         }
+    };
+    // two register buffers: batch it+1 streams in while batch it is consumed
+    int it = 0;
+    for (; it + 1 < nmain; it += 2) {
+        load_batch(it + 1, b1);
+        fma_batch(it, b0);
+        if (it + 2 < nmain) load_batch(it + 2, b0);
+        fma_batch(it + 1, b1);
     }
-    for (; r < L; r += RPI) {
-        u32x4 b = ld16_nt(Bb + (int64_t)(kbeg + r) * ldb_b);
+    if (it < nmain) fma_batch(it, b0);
+    for (int r = g + nmain * U * RPI; r < L; r += RPI) {
+        u32x4 b = ld16_nt(Bb + (int64_t)r * ldb_b);
         float w[8];
         unpack8(PATH, b, w);
 #pragma unroll
@@ -157,35 +172,55 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int k0, bool partial) {
+    // one step: 8 rows of 8 columns of B per lane and 8 k of A
+    struct Tile {
+        u32x4 b[8];
+        u32x4 a;
+    };
+    auto load = [&](int k0, bool partial, Tile &t) {
         const int kr = k0 + 8 * kg;
-        u32x4 b[8], bt[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int k = partial ? min(kr + r, kend - 1) : kr + r;
-            b[r] = ld16_nt(Bb + (int64_t)k * ldb_b);
-            if (partial && kr + r >= kend) b[r] = u32x4{0, 0, 0, 0};
+            t.b[r] = ld16_nt(Bb + (int64_t)k * ldb_b);
+            if (partial && kr + r >= kend) t.b[r] = u32x4{0, 0, 0, 0};
         }
-        u32x4 a = ld16(Ab + (int64_t)(partial ? min(kr, kend - 8) : kr) * 2);
-        if (partial && kr >= kend) a = u32x4{0, 0, 0, 0};
-        transpose8x8_b16(b, bt);
+        t.a = ld16(Ab + (int64_t)(partial ? min(kr, kend - 8) : kr) * 2);
+        if (partial && kr >= kend) t.a = u32x4{0, 0, 0, 0};
+    };
+    auto compute = [&](const Tile &t) {
+        u32x4 bt[8];
+        transpose8x8_b16(t.b, bt);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int q = 0; q < 8; ++q) {
             if constexpr (PATH == P_BF16)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                 __builtin_bit_cast(bf16x8, bt[t]),
-                                                                 acc[t], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.a),
+                                                                 __builtin_bit_cast(bf16x8, bt[q]),
+                                                                 acc[q], 0, 0, 0);
             else
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
-                                                                __builtin_bit_cast(half8, bt[t]),
-                                                                acc[t], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, t.a),
+                                                                __builtin_bit_cast(half8, bt[q]),
+                                                                acc[q], 0, 0, 0);
         }
     };
 
+    // two register buffers: step it+1 streams in while step it is consumed
     const int nfull = (kend - kbeg) / 32;
-    int k0 = kbeg;
-    for (int it = 0; it < nfull; ++it, k0 += 32) step(k0, false);
-    if (k0 < kend) step(k0, true);   // tail step: rows past the slice are zero
+    Tile t0, t1;
+    if (nfull > 0) load(kbeg, false, t0);
+    int it = 0;
+    for (; it + 1 < nfull; it += 2) {
+        load(kbeg + (it + 1) * 32, false, t1);
+        compute(t0);
+        if (it + 2 < nfull) load(kbeg + (it + 2) * 32, false, t0);
+        compute(t1);
+    }
+    if (it < nfull) compute(t0);
+    const int k0 = kbeg + nfull * 32;
+    if (k0 < kend) {   // tail step: rows past the slice are zero
+        load(k0, true, t1);
+        compute(t1);
+    }
 
     // lane holds rows 4*kg + v of columns c0 + 8j + t
 #pragma unroll
@@ -206,66 +241,104 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
 
 // ----------------------------------------------------------------- e2m1 path
 // B codes stored N x K (K contiguous, even k in the low nibble), scales N x G.
-// One wave per column; lane l takes 32-code groups l, l+64, ... of the slice:
-// one 16-byte load of codes, one fp16 scale, the group's dot product with A in
-// fp32 (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then v_dot2_f32_f16), and
-// the scale applied to the group sum.
+// Four columns per wave, 16 lanes each (16 columns per workgroup); lane q of a
+// column takes the 32-code groups q, q+16, ... of the slice: one 16-byte load of
+// codes, one fp16 scale, the group's dot product with A in fp32
+// (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then v_dot2_f32_f16), and the
+// scale applied to the group sum.  A's slice is staged in LDS once per
+// workgroup, after the first codes are requested; groups are taken GU at a
+// time, all their loads issued before any arithmetic; the 16 lanes of a column
+// are summed in a fixed order at the end.
+constexpr int E2M1_COLS_PER_WG = 16;
+constexpr int E2M1_A_LDS = 32768;   // bytes of A staged per workgroup
+
 template <int MR>
 __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
 {
+    constexpr int GU = MR <= 2 ? 8 : 4;   // groups in flight per lane
+    __shared__ __attribute__((aligned(16))) _Float16 sA[E2M1_A_LDS / 2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = blockIdx.x * 4 + wave;
-    if (n >= p.N) return;
+    const int q = lane & 15;
+    const int n = blockIdx.x * E2M1_COLS_PER_WG + wave * 4 + (lane >> 4);
+    const bool valid = n < p.N;
+    const int nc = valid ? n : 0;   // columns past N read column 0 and store nothing
     const int split = blockIdx.y;
     const int kbeg = split * p.k_slice;
     const int kend = min(p.K, kbeg + p.k_slice);
     const int gbeg = kbeg >> 5, gend = kend >> 5;
+    const int L = kend - kbeg;      // a multiple of 32
     const int M = p.M;
 
-    const char *Bc = reinterpret_cast<const char *>(p.B) + (int64_t)n * (p.ldb / 2);
-    const _Float16 *S = reinterpret_cast<const _Float16 *>(p.scale) + (int64_t)n * p.ld_scale;
+    const char *Bc = reinterpret_cast<const char *>(p.B) + (int64_t)nc * (p.ldb / 2);
+    const _Float16 *S = reinterpret_cast<const _Float16 *>(p.scale) + (int64_t)nc * p.ld_scale;
     const _Float16 *A = reinterpret_cast<const _Float16 *>(p.A);
+
+    u32x4 c[GU];
+    float sc[GU];
+    int gcs[GU];
+    auto load_groups = [&](int g0) {
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+            const int gi = g0 + 16 * u;
+            const bool in = gi < gend;
+            gcs[u] = in ? gi : gbeg;   // a valid group; its terms are dropped below
+            c[u] = ld16_nt(Bc + (int64_t)gcs[u] * 16);
+            sc[u] = in ? (float)S[gcs[u]] : 0.f;
+        }
+    };
+    if (gbeg + q < gend) load_groups(gbeg + q);
+
+    // stage A[0:M][kbeg:kend] (16-byte chunks; rows past M are zero)
+    for (int idx = tid; idx < MR * L / 8; idx += 256) {
+        const int m = idx / (L / 8), k8 = idx - m * (L / 8);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (m < M) v = ld16(A + (int64_t)m * p.lda + kbeg + 8 * k8);
+        *reinterpret_cast<u32x4 *>(sA + m * L + 8 * k8) = v;
+    }
+    __syncthreads();
 
     float acc[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[m] = 0.f;
 
-    for (int gi = gbeg + lane; gi < gend; gi += 64) {
-        const u32x4 c = ld16_nt(Bc + (int64_t)gi * 16);
-        const float s = (float)S[gi];
-        half2v w[16];
+    for (int g0 = gbeg + q; g0 < gend; g0 += 16 * GU) {
+        if (g0 != gbeg + q) load_groups(g0);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            w[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 0);
-            w[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 1);
-            w[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 2);
-            w[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 3);
-        }
+        for (int u = 0; u < GU; ++u) {
+            half2v w[16];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m >= M) break;
-            const u32x4 *ar = reinterpret_cast<const u32x4 *>(A + (int64_t)m * p.lda + gi * 32);
-            float dsum = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 av = ar[q];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    // copy the element first: a bit_cast applied directly to a
-                    // vector element with a loop index reads element 0 (clang)
-                    const unsigned ad = av[d];
-                    dsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, ad), w[4 * q + d],
-                                                  dsum, false);
-                }
+            for (int d = 0; d < 4; ++d) {
+                w[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[u][d], 1.0f, 0);
+                w[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[u][d], 1.0f, 1);
+                w[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[u][d], 1.0f, 2);
+                w[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[u][d], 1.0f, 3);
             }
-            acc[m] += s * dsum;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                if (m >= M) break;
+                const u32x4 *ar = reinterpret_cast<const u32x4 *>(sA + m * L + (gcs[u] - gbeg) * 32);
+                float dsum = 0.f;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const u32x4 av = ar[h];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        // copy the element first: a bit_cast applied directly to a
+                        // vector element with a loop index reads element 0 (clang)
+                        const unsigned ad = av[d];
+                        dsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, ad), w[4 * h + d],
+                                                      dsum, false);
+                    }
+                }
+                if (g0 + 16 * u < gend) acc[m] += sc[u] * dsum;
+            }
         }
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off, 64);
-    if (lane != 0) return;
+        for (int off = 8; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off, 64);
+    if (q != 0 || !valid) return;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         if (m >= M) break;
@@ -288,6 +361,11 @@ struct SkinnyEntry {
 static const SkinnyEntry k_valu[] = {DG_SKINNY_VALU_CATALOGUE(DG_SV_ENTRY)};
 static const SkinnyEntry k_mfma[] = {DG_SKINNY_MFMA_CATALOGUE(DG_SM_ENTRY)};
 static const SkinnyEntry k_e2m1[] = {DG_SKINNY_E2M1_CATALOGUE(DG_SE_ENTRY)};
+// rows of A each staging kernel holds in LDS (its MR)
+#define DG_SV_MR(path, mr, lpr) mr,
+#define DG_SE_MR(mr) mr,
+static const int k_valu_mr[] = {DG_SKINNY_VALU_CATALOGUE(DG_SV_MR)};
+static const int k_e2m1_mr[] = {DG_SKINNY_E2M1_CATALOGUE(DG_SE_MR)};
 
 int skinny_valu_count() { return (int)(sizeof(k_valu) / sizeof(k_valu[0])); }
 int skinny_mfma_count() { return (int)(sizeof(k_mfma) / sizeof(k_mfma[0])); }
@@ -303,6 +381,9 @@ static hipError_t launch_entry(const SkinnyEntry *tab, int count, int id, const 
 
 hipError_t launch_skinny_valu(int id, const SkinnyArgs &a, int gx, int gy, hipStream_t s)
 {
+    // the A slice must fit the kernel's LDS staging area
+    if (id >= 0 && id < skinny_valu_count() && (int64_t)a.k_slice * k_valu_mr[id] * 2 > SKINNY_A_LDS)
+        return hipErrorInvalidValue;
     return launch_entry(k_valu, skinny_valu_count(), id, a, gx, gy, s);
 }
 hipError_t launch_skinny_mfma(int id, const SkinnyArgs &a, int gx, int gy, hipStream_t s)
@@ -311,36 +392,74 @@ hipError_t launch_skinny_mfma(int id, const SkinnyArgs &a, int gx, int gy, hipSt
 }
 hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int gx, int gy, hipStream_t s)
 {
+    // the A slice must fit the kernel's LDS staging area, in whole 32-k groups
+    if (id >= 0 && id < skinny_e2m1_count() &&
+        ((int64_t)a.k_slice * k_e2m1_mr[id] * 2 > E2M1_A_LDS || a.k_slice % 32))
+        return hipErrorInvalidValue;
     return launch_entry(k_e2m1, skinny_e2m1_count(), id, a, gx, gy, s);
 }
 
 // ------------------------------------------------------------ split-K reduce
-// out[i][j] = epilogue( sum_{s = 0 .. S-1} ws[s][i][j] ), s ascending, so the
-// result does not depend on the order in which the slices finished.
+// out[i][j] = epilogue( sum over the slices s of ws[s][i][j] ).  `lanes`
+// consecutive lanes share an output: lane t adds slices [t*C, (t+1)*C) in
+// ascending order (C = ceil(S / lanes)), eight loads in flight, and the lanes'
+// sums are combined by a butterfly whose pairs add in the same order on both
+// sides, so the result does not depend on timing.
 __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a)
 {
+    const int T = a.lanes;
     const int64_t MN = (int64_t)a.M * a.N;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= MN) return;
-    const int i = (int)(idx / a.N), j = (int)(idx - (int64_t)i * a.N);
+    const int t = threadIdx.x & (T - 1);
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) / T;
+    const bool ok = idx < MN;
+    const int S = a.split_k;
+    const int C = (S + T - 1) / T;
+    const int s0 = min(S, t * C), s1 = min(S, s0 + C);
+    const int64_t base = ok ? idx : 0;
     if (a.is_int) {
-        const int32_t *w = reinterpret_cast<const int32_t *>(a.ws);
-        uint32_t s = 0;
-        for (int k = 0; k < a.split_k; ++k) s += (uint32_t)w[k * MN + idx];
-        epi_store_i(a.epi, i, j, (int32_t)s);
+        const int32_t *w = reinterpret_cast<const int32_t *>(a.ws) + base;
+        uint32_t acc = 0;
+        int s = s0;
+        for (; s + 8 <= s1; s += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ok ? w[(int64_t)(s + u) * MN] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += (uint32_t)v[u];
+        }
+        for (; s < s1; ++s) acc += ok ? (uint32_t)w[(int64_t)s * MN] : 0u;
+        for (int off = T / 2; off >= 1; off >>= 1) acc += (uint32_t)__shfl_xor((int)acc, off, 64);
+        if (t == 0 && ok) {
+            const int i = (int)(idx / a.N), j = (int)(idx - (int64_t)i * a.N);
+            epi_store_i(a.epi, i, j, (int32_t)acc);
+        }
     } else {
-        const float *w = reinterpret_cast<const float *>(a.ws);
-        float s = 0.f;
-        for (int k = 0; k < a.split_k; ++k) s += w[k * MN + idx];
-        epi_store_f(a.epi, i, j, s);
+        const float *w = reinterpret_cast<const float *>(a.ws) + base;
+        float acc = 0.f;
+        int s = s0;
+        for (; s + 8 <= s1; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ok ? w[(int64_t)(s + u) * MN] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        for (; s < s1; ++s) acc += ok ? w[(int64_t)s * MN] : 0.f;
+        for (int off = T / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (t == 0 && ok) {
+            const int i = (int)(idx / a.N), j = (int)(idx - (int64_t)i * a.N);
+            epi_store_f(a.epi, i, j, acc);
+        }
     }
 }
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
+    if (a.lanes < 1 || a.lanes > 64 || (a.lanes & (a.lanes - 1))) return hipErrorInvalidValue;
     const int64_t MN = (int64_t)a.M * a.N;
-    const int grid = (int)((MN + 255) / 256);
-    hipLaunchKernelGGL(reduce_kernel, dim3(grid, 1, 1), dim3(256, 1, 1), 0, s, a);
+    const int64_t grid = (MN * a.lanes + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid, 1, 1), dim3(256, 1, 1), 0, s, a);
     return hipGetLastError();
 }
 
