@@ -164,7 +164,9 @@ typedef struct {
     int32_t m_tile, n_tile;   /* workgroup tile (skinny path: M rows x N columns) */
     int32_t k_main, n_main;   /* K schedule of the first K slice: n_main steps of k_main */
     int32_t k_tail, n_tail;   /* then n_tail steps of k_tail (the smaller tail step) */
-    int32_t split_k;          /* K slices; partials reduced in ascending slice order */
+    int32_t split_k;          /* K slices; partials reduced in a fixed order (runs of
+                                 consecutive slices summed in ascending order, the runs
+                                 combined in a fixed pattern): run-to-run identical */
     int32_t k_slice;          /* K length of every slice but the last */
     int32_t waves_per_wg;
     int32_t lds_bytes;        /* LDS per workgroup */
