@@ -68,7 +68,7 @@ constexpr int tiled_min_loads_per_wave(int a_nl, int b_nl, int s_nl, int nw)
 constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 64 : 32; }
 constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
 
-// LDS bytes of one tiled variant: four stages of one K step each.  A and a
+// LDS bytes of one stage (one K step) of a tiled variant.  A and a
 // K-contiguous B take 64 bytes per row (per column of B), a row-major B 64 bytes
 // per column (BN columns of a 32-k or 64-k step); e2m1 B takes 16 bytes of codes
 // plus a 4-byte scale word per column.
@@ -76,12 +76,20 @@ constexpr int tiled_stage_bytes(int path, int bm, int bn)
 {
     return bm * 64 + (path == 3 ? bn * 20 : bn * 64);
 }
+// LDS stages: five for the eight-wave variants when they fit gfx950's 160 KB
+// (the loads of a stage are then issued a phase later, in the MFMA phase, with
+// the same lookahead), four otherwise.
+constexpr int tiled_nbuf(int path, int bm, int bn, int wm, int wn)
+{
+    return wm * wn == 8 && 5 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 5 : 4;
+}
 // The epilogue reuses the LDS to stage 32 rows of every wave's accumulators
 // (4-byte values, rows padded by 4): the allocation is the larger of the two.
 constexpr int tiled_lds_bytes(int path, int bm, int bn, int wm, int wn)
 {
-    return 4 * tiled_stage_bytes(path, bm, bn) > wm * wn * 32 * (bn / wn + 4) * 4
-               ? 4 * tiled_stage_bytes(path, bm, bn)
+    return tiled_nbuf(path, bm, bn, wm, wn) * tiled_stage_bytes(path, bm, bn) >
+                   wm * wn * 32 * (bn / wn + 4) * 4
+               ? tiled_nbuf(path, bm, bn, wm, wn) * tiled_stage_bytes(path, bm, bn)
                : wm * wn * 32 * (bn / wn + 4) * 4;
 }
 

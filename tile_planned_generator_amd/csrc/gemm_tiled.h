@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int BKE = tiled_bk_elems(PATH);          // k elements per step
     constexpr int KSUB = tiled_ksub(PATH);             // k elements per MFMA
     static_assert(BKE == 2 * KSUB, "two substeps per step");
-    constexpr int NBUF = 4;
+    constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN);
     constexpr int ESZ = IS_I8 ? 1 : 2;                 // bytes per element of A and of a 16-bit / int8 B
     static_assert(BKE * ESZ == 64, "64-byte rows");
     constexpr int A_BYTES = BM * 64;
@@ -249,16 +249,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // Steps past the last one issue the same loads over empty ranges: they only
     // write zeros into a stage nobody reads again, and keep every wave's count
     // of outstanding loads the same at each barrier.
-    auto load_stage = [&](int j) {
+    auto load_stage = [&](int j, int part = -1) {
         const bool real = j < nsteps;
         const int k0 = real ? kbeg + j * BKE : 0;
-        char *sb = smem + (j & (NBUF - 1)) * STAGE;
+        char *sb = smem + (j % NBUF) * STAGE;
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(Abase + (int64_t)k0 * ESZ, real ? a_bytes - (uint32_t)(k0 * ESZ) : 0u);
+        if (part != 1) {
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            if (A_NL % NW == 0 || i * NW + wave < A_NL)   // wave-uniform
-                buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
+            for (int i = 0; i < A_LD; ++i)
+                if (A_NL % NW == 0 || i * NW + wave < A_NL)   // wave-uniform
+                    buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
+        }
+        if (part == 0) return;
         uint32_t kb;
         if constexpr (IS_E2M1) kb = (uint32_t)(k0 >> 1);
         else if constexpr (BKMAJ) kb = (uint32_t)(k0 * ESZ);
@@ -392,6 +395,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                         acc[mi][ni], 0, 0, 0);
             }
     };
+    // A final half step runs its second substep on zero fragments (0 x 0 adds
+    // nothing), so the loop body has no branch around MFMAs: a branch there
+    // makes the compiler copy every accumulator on each step.
+    auto zero = [&](Frag &f) {
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) f.a[mi] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) f.b[ni] = u32x4{0u, 0u, 0u, 0u};
+    };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     const int g0 = kbeg >> 5;   // e2m1 scale group of step 0
@@ -401,18 +413,21 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // of stage st+1, substep 1 of stage st].  The barrier guarantees that stage st+1 has landed
     // for every wave (the loads of stages st+2 and st+3 may still be in flight)
     // and that no wave still reads stage st, whose buffer takes stage st+4.  The
-    // body is branch-free but for the MFMAs of a final half step.
+    // body is branch-free.
     Frag f0, f1;
     if constexpr (NW == 8) {
         // Eight waves: two groups of four (waves 0-3 and 4-7, one of each per
-        // SIMD) alternate a memory phase (read both fragments of stage st, issue
-        // the loads of stage st+3, wait for this wave's loads of stage st+1) and
-        // a compute phase (the MFMAs of stage st only), with a barrier after each
-        // phase.  The second group runs one barrier behind, so on every SIMD one
-        // wave computes while the other does its memory phase.  Stage st is read
-        // by the first group between barriers 2st+1 and 2st+2 and by the second
-        // between 2st+2 and 2st+3; its buffer is refilled (stage st+4) in the
-        // memory phases that start at or after barrier 2st+3.
+        // SIMD) alternate a memory phase (read both fragments of stage st, wait
+        // for this wave's loads of stage st+1) and a compute phase (the MFMAs of
+        // stage st), with a barrier after each phase.  The second group runs one
+        // barrier behind, so on every SIMD one wave computes while the other does
+        // its memory phase.  Stage st is read by the first group between barriers
+        // 2st+1 and 2st+2 and by the second between 2st+2 and 2st+3, so its buffer
+        // may be refilled by any phase that starts at or after barrier 2st+3.
+        // With five stages the loads of stage st+4 are issued in the compute
+        // phase of step st, between the MFMAs (into the buffer of stage st-1);
+        // with four, the loads of stage st+3 in the memory phase.  Either way
+        // two later stages stay in flight at each wait.
         const bool lag = wave >= 4;
         auto bar = [] {
             __builtin_amdgcn_sched_barrier(0);
@@ -425,25 +440,31 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[ni]) : : "memory");
             }
         };
+        constexpr int AHEAD = NBUF - 1;   // stages issued before the loop
 #pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j) load_stage(j);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * LPS, 15));
+        for (int j = 0; j < AHEAD; ++j) load_stage(j);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
         bar();
         if (lag) bar();
+        int buf = 0;
         for (int st = 0; st < nsteps; ++st) {
-            const int buf = st & (NBUF - 1);
-            // memory phase
+            // memory phase: the fragment reads of stage st, with the loads of
+            // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
+            // to different units)
             read_frag(buf, S0{}, f0, g0 + st);
+            load_stage(st + AHEAD, 0);
             read_frag(buf, S1{}, f1, g0 + st);
-            load_stage(st + NBUF - 1);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * LPS, 0));
+            load_stage(st + AHEAD, 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
             tie(f0);
             tie(f1);
+            if (st >= nfull) zero(f1);   // final half step: substep 1 adds 0 x 0
             bar();
             // compute phase
             mfmas(f0);
-            if (st < nfull) mfmas(f1);   // not on a final half step
+            mfmas(f1);
             bar();
+            buf = buf + 1 == NBUF ? 0 : buf + 1;
         }
         if (!lag) bar();
     } else {
@@ -452,15 +473,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         wait_vm_barrier<(NBUF - 1) * LPS>();
         read_frag(0, S0{}, f0, g0);
         for (int st = 0; st < nsteps; ++st) {
-            const int buf = st & (NBUF - 1);
+            const int buf = st % NBUF;
             settle(f0);
             read_frag(buf, S1{}, f1, g0 + st);
             mfmas(f0);
             wait_vm_barrier<(NBUF - 2) * LPS>();
             settle(f1);
+            if (st >= nfull) zero(f1);   // final half step: substep 1 adds 0 x 0
             load_stage(st + NBUF);
-            read_frag((st + 1) & (NBUF - 1), S0{}, f0, g0 + st + 1);
-            if (st < nfull) mfmas(f1);   // not on a final half step
+            read_frag((st + 1) % NBUF, S0{}, f0, g0 + st + 1);
+            mfmas(f1);
         }
     }
 
