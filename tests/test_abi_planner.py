@@ -128,7 +128,7 @@ def test_pareto_matches_bruteforce_over_forced_plans(off):
     M, N, K = 2048, 2048, 8192
     pareto = {(p.m_tile, p.n_tile, p.split_k, p.kernel_name) for p in off.candidates(M, N, K)}
     forced = []
-    for mt, nt in [(256, 256), (256, 128), (128, 128), (64, 64)]:
+    for mt, nt in [(256, 256), (128, 256), (256, 128), (128, 128), (64, 64)]:   # every compiled tile
         for s in (1, 2, 4, 8, 16, 32):
             o = dg.dg_plan_opts(force_m_tile=mt, force_n_tile=nt, force_split_k=s,
                                 force_path=dg.DG_PATH_TILED)

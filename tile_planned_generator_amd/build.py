@@ -20,6 +20,8 @@ LIB = os.path.join(HERE, "libdg.so")
 KERNEL_SOURCES = ["gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip",
                   "gemm_tiled_e2m1.hip", "skinny.hip"]
 HOST_SOURCES = ["gemm_tiled.hip", "api.cpp", "planner.cpp"]
+# kernel sources that issue transposing LDS reads (row-major B operands)
+TILED_TR_SOURCES = ["gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip"]
 RESOURCES = os.path.join(CSRC, "resources.inc")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -80,6 +82,48 @@ def _parse_resources(remarks):
     return rows
 
 
+def _regs(operands):
+    out = set()
+    for m in re.finditer(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b", operands):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _check_transposing_reads(src):
+    """The tiled kernel issues its transposing LDS reads from inline assembly,
+    which the compiler's wait insertion does not see: until an lgkmcnt(0) wait,
+    the destination registers of such a read are still being written.  Scan the
+    device assembly of `src` and return every instruction that touches one of
+    those registers before that wait (an instruction that would read a value not
+    yet landed, or write a register the read will overwrite)."""
+    path = os.path.join(CSRC, src)
+    cmd = [HIPCC, *DEVICE, *COMMON, "-x", "hip", "--cuda-device-only", "-S", path, "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"assembling {src} failed:\n{r.stderr}")
+    bad, pend, kernel = [], set(), None
+    for line in r.stdout.splitlines():
+        if re.match(r"^_ZN\w+:", line):
+            kernel, pend = line.split(":")[0], set()
+            continue
+        t = line.strip()
+        if not t or t.startswith((";", ".")) or kernel is None:
+            continue
+        op = t.split()[0]
+        if op == "s_waitcnt" and "lgkmcnt(0)" in t:
+            pend = set()
+            continue
+        operands = t.split(";")[0][len(op):]
+        if op.startswith("ds_read_b64_tr"):
+            pend |= _regs(operands.split(",")[0])
+        elif pend & _regs(operands):
+            bad.append(f"{kernel}: {t}")
+    return bad
+
+
 def _write_resources(rows):
     lines = ["// resources.inc - registers, LDS and occupancy of every compiled kernel variant,",
              "// extracted from the compiler's kernel-resource-usage remarks by build.py.",
@@ -105,6 +149,11 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     if spills:
         raise RuntimeError(f"kernel variants spill registers or use private memory: {spills}")
     _write_resources(rows)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        hazards = [h for hs in ex.map(_check_transposing_reads, TILED_TR_SOURCES) for h in hs]
+    if hazards:
+        raise RuntimeError("instructions touch registers of in-flight transposing LDS reads:\n" +
+                           "\n".join(hazards[:20]))
     with cf.ThreadPoolExecutor(jobs) as ex:
         done += list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES))
     objs = [o for o, _ in done]

@@ -328,41 +328,46 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     for (int ni = 0; ni < FN; ++ni)
         spar[ni] = IS_E2M1 ? ((smis >> 1) + (uint32_t)((n0 + wn * WTN + ni * 32 + lr) * p.ld_scale)) & 1u : 0u;
 
-    auto read_frag = [&](int buf, auto s_tag, Frag &f, int g) {
+    // One fragment read: A block mi, or B block ni, of substep s of stage buf.
+    auto read_a = [&](int buf, auto s_tag, int mi, Frag &f) {
         constexpr int s = decltype(s_tag)::value;
         const char *sA = smem + buf * STAGE;
-        const char *sB = sA + A_BYTES;
         const int c = 2 * s + kg;
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi) {
-            const int row = wm * WTM + mi * 32 + lr;
-            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
-        }
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) {
-            const int col0 = wn * WTN + ni * 32;
-            if constexpr (IS_E2M1) {
-                const int row = col0 + lr;
-                const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + (2 * s + kg) * 4);
-                const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
-                const unsigned short sh = (unsigned short)(((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd);
-                f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
-            } else if constexpr (BKMAJ) {
-                const int row = col0 + lr;
-                f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+        const int row = wm * WTM + mi * 32 + lr;
+        f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+    };
+    auto read_b = [&](int buf, auto s_tag, int ni, Frag &f, int g) {
+        constexpr int s = decltype(s_tag)::value;
+        const char *sB = smem + buf * STAGE + A_BYTES;
+        const int c = 2 * s + kg;
+        const int col0 = wn * WTN + ni * 32;
+        if constexpr (IS_E2M1) {
+            const int row = col0 + lr;
+            const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + (2 * s + kg) * 4);
+            const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
+            const unsigned short sh = (unsigned short)(((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd);
+            f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
+        } else if constexpr (BKMAJ) {
+            const int row = col0 + lr;
+            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+        } else {
+            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
+            u32x2 lo, hi;
+            if constexpr (!IS_I8) {
+                lo = lds_tr16<KSUB * s * RB>(a);
+                hi = lds_tr16<KSUB * s * RB + 4 * RB>(a);
             } else {
-                const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
-                u32x2 lo, hi;
-                if constexpr (!IS_I8) {
-                    lo = lds_tr16<KSUB * s * RB>(a);
-                    hi = lds_tr16<KSUB * s * RB + 4 * RB>(a);
-                } else {
-                    lo = lds_tr8<KSUB * s * RB>(a);
-                    hi = lds_tr8<KSUB * s * RB + 8 * RB>(a);
-                }
-                f.b[ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                lo = lds_tr8<KSUB * s * RB>(a);
+                hi = lds_tr8<KSUB * s * RB + 8 * RB>(a);
             }
+            f.b[ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
+    };
+    auto read_frag = [&](int buf, auto s_tag, Frag &f, int g) {
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) read_a(buf, s_tag, mi, f);
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) read_b(buf, s_tag, ni, f, g);
     };
     // The transposing reads are invisible to the compiler's wait insertion:
     // wait for all LDS reads, then tie the B registers to that point so the
@@ -376,33 +381,33 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[ni]) : : "memory");
         }
     };
+    auto mfma1 = [&](const Frag &f, int mi, int ni) {
+        if constexpr (PATH == P_F16 || PATH == P_E2M1)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8, f.a[mi]), __builtin_bit_cast(half8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+        else if constexpr (PATH == P_BF16)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, f.a[mi]), __builtin_bit_cast(bf16x8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+        else
+            acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                __builtin_bit_cast(intx4, f.a[mi]), __builtin_bit_cast(intx4, f.b[ni]), acc[mi][ni], 0, 0, 0);
+    };
     auto mfmas = [&](const Frag &f) {
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni) {
-                if constexpr (PATH == P_F16 || PATH == P_E2M1)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(half8, f.a[mi]), __builtin_bit_cast(half8, f.b[ni]),
-                        acc[mi][ni], 0, 0, 0);
-                else if constexpr (PATH == P_BF16)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f.a[mi]), __builtin_bit_cast(bf16x8, f.b[ni]),
-                        acc[mi][ni], 0, 0, 0);
-                else
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        __builtin_bit_cast(intx4, f.a[mi]), __builtin_bit_cast(intx4, f.b[ni]),
-                        acc[mi][ni], 0, 0, 0);
-            }
+            for (int ni = 0; ni < FN; ++ni) mfma1(f, mi, ni);
     };
-    // A final half step runs its second substep on zero fragments (0 x 0 adds
-    // nothing), so the loop body has no branch around MFMAs: a branch there
-    // makes the compiler copy every accumulator on each step.
-    auto zero = [&](Frag &f) {
+    // A final half step runs its second substep on zeroed fragments (0 x 0 adds
+    // nothing): the fragments are ANDed with a uniform mask, so the loop body has
+    // no branch at all - a branch near the MFMAs makes the compiler copy every
+    // accumulator on each step.
+    auto keep_if = [&](Frag &f, bool keep) {
+        const unsigned m = keep ? ~0u : 0u;
 #pragma unroll
-        for (int mi = 0; mi < FM; ++mi) f.a[mi] = u32x4{0u, 0u, 0u, 0u};
+        for (int mi = 0; mi < FM; ++mi) f.a[mi] &= m;
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni) f.b[ni] = u32x4{0u, 0u, 0u, 0u};
+        for (int ni = 0; ni < FN; ++ni) f.b[ni] &= m;
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -458,7 +463,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
             tie(f0);
             tie(f1);
-            if (st >= nfull) zero(f1);   // final half step: substep 1 adds 0 x 0
+            keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
             bar();
             // compute phase
             mfmas(f0);
@@ -466,6 +471,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             bar();
             buf = buf + 1 == NBUF ? 0 : buf + 1;
         }
+        // (every fragment read in this loop is consumed in its own step; settling
+        // here keeps the rule that no transposing read is left in flight)
+        settle(f0);
+        settle(f1);
         if (!lag) bar();
     } else {
 #pragma unroll
@@ -479,11 +488,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             mfmas(f0);
             wait_vm_barrier<(NBUF - 2) * LPS>();
             settle(f1);
-            if (st >= nfull) zero(f1);   // final half step: substep 1 adds 0 x 0
+            keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
             load_stage(st + NBUF);
             read_frag((st + 1) % NBUF, S0{}, f0, g0 + st + 1);
             mfmas(f1);
         }
+        // The last read-ahead is never used, but the compiler does not know that
+        // the transposing reads land later: wait for them and keep their
+        // registers allocated until then, or the epilogue may reuse a register
+        // that an in-flight read still overwrites.
+        settle(f0);
     }
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
