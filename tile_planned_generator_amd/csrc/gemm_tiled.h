@@ -342,11 +342,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const int c = 2 * s + kg;
         const int col0 = wn * WTN + ni * 32;
         if constexpr (IS_E2M1) {
+            // raw: the code word and the scale's bits; decode_b turns them into
+            // the fp16 operand (in the MFMA phase, off the LDS-bound one)
             const int row = col0 + lr;
             const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + (2 * s + kg) * 4);
             const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
-            const unsigned short sh = (unsigned short)(((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd);
-            f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
+            const unsigned sh = ((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd & 0xffffu;
+            f.b[ni] = u32x4{codes, sh, 0u, 0u};
         } else if constexpr (BKMAJ) {
             const int row = col0 + lr;
             f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
@@ -379,6 +381,17 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[ni]) : : "memory");
+        }
+    };
+    // e2m1: decode the raw B fragments read by read_b (nothing to do otherwise)
+    auto decode_b = [&](Frag &f) {
+        if constexpr (IS_E2M1) {
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni) {
+                const unsigned codes = f.b[ni].x;
+                const unsigned short sh = (unsigned short)f.b[ni].y;
+                f.b[ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
+            }
         }
     };
     auto mfma1 = [&](const Frag &f, int mi, int ni) {
@@ -466,7 +479,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
             bar();
             // compute phase
+            decode_b(f0);
             mfmas(f0);
+            decode_b(f1);
             mfmas(f1);
             bar();
             buf = buf + 1 == NBUF ? 0 : buf + 1;
@@ -485,12 +500,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const int buf = st % NBUF;
             settle(f0);
             read_frag(buf, S1{}, f1, g0 + st);
+            decode_b(f0);
             mfmas(f0);
             wait_vm_barrier<(NBUF - 2) * LPS>();
             settle(f1);
             keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
             load_stage(st + NBUF);
             read_frag((st + 1) % NBUF, S0{}, f0, g0 + st + 1);
+            decode_b(f1);
             mfmas(f1);
         }
         // The last read-ahead is never used, but the compiler does not know that

@@ -176,16 +176,17 @@ DG_DEV floatx4 load4_f32(const void *p, int type, int64_t idx)
     return *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(p) + idx);
 }
 
+// Output stores are non-temporal: C is written once and not read back here.
 DG_DEV void store4_f32(void *p, int type, int64_t idx, floatx4 v)
 {
     if (type == T_F16)
-        *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(p) + idx) =
-            half4v{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        __builtin_nontemporal_store(half4v{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w},
+                                    reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(p) + idx));
     else if (type == T_BF16)
-        *reinterpret_cast<bf16x4v *>(reinterpret_cast<__bf16 *>(p) + idx) =
-            bf16x4v{(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+        __builtin_nontemporal_store(bf16x4v{(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w},
+                                    reinterpret_cast<bf16x4v *>(reinterpret_cast<__bf16 *>(p) + idx));
     else
-        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(p) + idx) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(p) + idx));
 }
 
 // epi_store_f on four consecutive columns j .. j+3 (the same arithmetic per element)
@@ -234,7 +235,7 @@ DG_DEV void epi_store4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc)
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = (int)((uint32_t)v[c] + (uint32_t)e.ibeta * (uint32_t)d[c]);
     }
-    *reinterpret_cast<intx4 *>(reinterpret_cast<int32_t *>(e.C) + i * e.ldc + j) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<intx4 *>(reinterpret_cast<int32_t *>(e.C) + i * e.ldc + j));
 }
 
 // Linear workgroup id -> tile index, keeping each accelerator die (XCD) on a
