@@ -453,10 +453,55 @@ __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a)
     }
 }
 
+// Few slices (lanes == 1) and N a multiple of 4: each thread sums four
+// consecutive outputs of one row with 16-byte loads of every slice, in slice
+// order, and stores them through the four-column epilogue when the output,
+// D and bias allow it (else one element at a time).
+__global__ void __launch_bounds__(256) reduce4_kernel(ReduceArgs a)
+{
+    const int64_t MN = (int64_t)a.M * a.N;
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (idx >= MN) return;
+    const int i = (int)(idx / a.N), j = (int)(idx - (int64_t)i * a.N);
+    const bool vec = epi_vec_ok(a.epi, false, nullptr, a.N);
+    if (a.is_int) {
+        const int32_t *w = reinterpret_cast<const int32_t *>(a.ws) + idx;
+        intx4 acc = intx4{0, 0, 0, 0};
+        for (int k = 0; k < a.split_k; ++k) {
+            const intx4 v = __builtin_nontemporal_load(reinterpret_cast<const intx4 *>(w + (int64_t)k * MN));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = (int)((uint32_t)acc[c] + (uint32_t)v[c]);
+        }
+        if (vec) {
+            epi_store4_i(a.epi, i, j, acc);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) epi_store_i(a.epi, i, j + c, acc[c]);
+        }
+    } else {
+        const float *w = reinterpret_cast<const float *>(a.ws) + idx;
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < a.split_k; ++k)
+            acc += __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(w + (int64_t)k * MN));
+        if (vec) {
+            epi_store4_f(a.epi, i, j, acc);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) epi_store_f(a.epi, i, j + c, acc[c]);
+        }
+    }
+}
+
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
     if (a.lanes < 1 || a.lanes > 64 || (a.lanes & (a.lanes - 1))) return hipErrorInvalidValue;
     const int64_t MN = (int64_t)a.M * a.N;
+    if (a.lanes == 1 && (a.N & 3) == 0 && ((uintptr_t)a.ws & 15) == 0) {
+        const int64_t grid4 = (MN / 4 + 255) / 256;
+        if (grid4 > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)grid4, 1, 1), dim3(256, 1, 1), 0, s, a);
+        return hipGetLastError();
+    }
     const int64_t grid = (MN * a.lanes + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid, 1, 1), dim3(256, 1, 1), 0, s, a);
