@@ -68,6 +68,18 @@ constexpr int tiled_min_loads_per_wave(int a_nl, int b_nl, int s_nl, int nw)
 constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 64 : 32; }
 constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
 
+// Sustained fraction of the published MFMA rate one K step of a tiled variant
+// reaches on MI355X, measured with every variant forced on the 4096^3 and
+// 2048x2048x8192 workloads (fp16; int8 and e2m1 relative to it).  It folds in
+// what a peak-rate model leaves out: the engine clock under MFMA load (about
+// 1.9-2.0 GHz, not 2.4), the LDS-bound fragment reads and the barriers.
+constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
+{
+    const double base = waves == 8 ? 0.46
+                      : (bm * bn >= 256 * 128 ? 0.37 : (bm * bn >= 128 * 128 ? 0.30 : 0.15));
+    return base * (path == 2 /*P_I8*/ ? 0.95 : (path == 3 /*P_E2M1*/ ? 0.87 : 1.0));
+}
+
 // LDS bytes of one stage (one K step) of a tiled variant.  A and a
 // K-contiguous B take 64 bytes per row (per column of B), a row-major B 64 bytes
 // per column (BN columns of a 32-k or 64-k step); e2m1 B takes 16 bytes of codes

@@ -241,9 +241,14 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             const int64_t wgs = tiles * S_eff;
             const int64_t rounds = ceil_div(wgs, (int64_t)d.cu_count * wg_per_cu);
             const int W = (int)std::min<int64_t>(wg_per_cu, ceil_div(wgs, d.cu_count));
-            const double t_mfma = 2.0 * s.bm * s.bn * BKE / mfma_ops_per_clk_cu(pr.path);
-            const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + (s.bm + s.bn) * 128.0) / 128.0;
-            const double t_l2 = (s.bm + s.bn) * 128.0 / 64.0;
+            // MFMA time of one K step at the published rate, stretched by the
+            // variant's measured sustained efficiency (catalogue.h); the LDS and
+            // L2 terms only matter for variants that are not MFMA-bound.
+            const double t_mfma = 2.0 * s.bm * s.bn * BKE / mfma_ops_per_clk_cu(pr.path) /
+                                  tiled_step_efficiency(s.path, s.bm, s.bn, waves);
+            const double stage = tiled_stage_bytes(s.path, s.bm, s.bn);
+            const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + stage) / 128.0;
+            const double t_l2 = stage / 64.0;
             // A K step waits for loads issued one step earlier.  When an operand is
             // streamed with almost no reuse across workgroups (one or two tile rows
             // or columns), those loads come from HBM and the step is bound by DRAM
@@ -256,7 +261,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             double floor_bytes = pr.M * pr.K * (pr.path == P_I8 ? 1.0 : 2.0) +
                                  pr.K * pr.N * (pr.path == P_I8 ? 1.0 : (pr.path == P_E2M1 ? 0.5 : 2.0));
             const double out_bytes = (double)pr.M * pr.N * elt_bytes(pr.out_type) * (pr.beta_nz ? 2 : 1);
-            double est = std::max(t_comp, hbm_us(floor_bytes, d)) + 0.5 * hbm_us(out_bytes, d) + LAUNCH_US;
+            // the epilogue stores after the K loop, at about 70 % of HBM bandwidth
+            double est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + LAUNCH_US;
             if (S_eff > 1) est += hbm_us((double)S_eff * pr.M * pr.N * 4 * 2 + out_bytes, d) + LAUNCH_US;
             c.est_us = est;
             c.roof_us = roofline_us(pr, d);
