@@ -249,36 +249,41 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // Steps past the last one issue the same loads over empty ranges: they only
     // write zeros into a stage nobody reads again, and keep every wave's count
     // of outstanding loads the same at each barrier.
-    auto load_stage = [&](int j, int part = -1) {
+    // Load i of step j: the A loads first, then B, then the e2m1 scales.
+    auto load_one = [&](int j, int i) {
         const bool real = j < nsteps;
         const int k0 = real ? kbeg + j * BKE : 0;
         char *sb = smem + (j % NBUF) * STAGE;
-        const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(Abase + (int64_t)k0 * ESZ, real ? a_bytes - (uint32_t)(k0 * ESZ) : 0u);
-        if (part != 1) {
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                if (A_NL % NW == 0 || i * NW + wave < A_NL)   // wave-uniform
-                    buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
+        if (i < A_LD) {
+            if (A_NL % NW == 0 || i * NW + wave < A_NL) {   // wave-uniform
+                const __amdgpu_buffer_rsrc_t rA =
+                    make_rsrc(Abase + (int64_t)k0 * ESZ, real ? a_bytes - (uint32_t)(k0 * ESZ) : 0u);
+                buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
+            }
+        } else if (i < A_LD + B_LD) {
+            const int q = i - A_LD;
+            if (B_NL % NW == 0 || q * NW + wave < B_NL) {   // wave-uniform
+                uint32_t kb;
+                if constexpr (IS_E2M1) kb = (uint32_t)(k0 >> 1);
+                else if constexpr (BKMAJ) kb = (uint32_t)(k0 * ESZ);
+                else kb = (uint32_t)k0 * ldb_b;
+                const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + kb, real ? b_bytes - kb : 0u);
+                buf_ld16_lds(rB, ob[q], sb + A_BYTES + (q * NW + wave) * 1024);
+            }
+        } else if constexpr (IS_E2M1) {
+            const int q = i - A_LD - B_LD;
+            if (S_NL % NW == 0 || q * NW + swave < S_NL) {   // wave-uniform
+                const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sbase, real ? s_bytes : 0u);
+                buf_ld4_lds(rS, (os[q] + 2 * (uint32_t)(k0 >> 5)) & ~3u,
+                            sb + A_BYTES + B_TILE + (q * NW + swave) * 256);
+            }
         }
-        if (part == 0) return;
-        uint32_t kb;
-        if constexpr (IS_E2M1) kb = (uint32_t)(k0 >> 1);
-        else if constexpr (BKMAJ) kb = (uint32_t)(k0 * ESZ);
-        else kb = (uint32_t)k0 * ldb_b;
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + kb, real ? b_bytes - kb : 0u);
+    };
+    // All loads of step j (part 0: only A; part 1: only B and the scales).
+    auto load_stage = [&](int j, int part = -1) {
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            if (B_NL % NW == 0 || i * NW + wave < B_NL)   // wave-uniform
-                buf_ld16_lds(rB, ob[i], sb + A_BYTES + (i * NW + wave) * 1024);
-        if constexpr (IS_E2M1) {
-            const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sbase, real ? s_bytes : 0u);
-            const uint32_t gb = 2 * (uint32_t)(k0 >> 5);
-#pragma unroll
-            for (int i = 0; i < S_LD; ++i)
-                if (S_NL % NW == 0 || i * NW + swave < S_NL)   // wave-uniform
-                    buf_ld4_lds(rS, (os[i] + gb) & ~3u, sb + A_BYTES + B_TILE + (i * NW + swave) * 256);
-        }
+        for (int i = 0; i < A_LD + B_LD + S_LD; ++i)
+            if (part < 0 || (part == 0) == (i < A_LD)) load_one(j, i);
     };
 
     using AccT = typename std::conditional<IS_I8, intx16, floatx16>::type;
@@ -442,10 +447,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         // its memory phase.  Stage st is read by the first group between barriers
         // 2st+1 and 2st+2 and by the second between 2st+2 and 2st+3, so its buffer
         // may be refilled by any phase that starts at or after barrier 2st+3.
-        // With five stages the loads of stage st+4 are issued in the compute
-        // phase of step st, between the MFMAs (into the buffer of stage st-1);
-        // with four, the loads of stage st+3 in the memory phase.  Either way
-        // two later stages stay in flight at each wait.
+        // The memory phase of step st issues the loads of stage st+NBUF-1, into
+        // the buffer of stage st-1, and its wait leaves the NBUF-2 stages after
+        // stage st+1 in flight.
         const bool lag = wave >= 4;
         auto bar = [] {
             __builtin_amdgcn_sched_barrier(0);
@@ -464,19 +468,22 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
         bar();
         if (lag) bar();
-        int buf = 0;
-        for (int st = 0; st < nsteps; ++st) {
+        // One step; the last one (LAST) issues no loads and masks its second
+        // substep when it is a half step.
+        auto step = [&](int st, auto last_tag) {
+            constexpr bool LAST = decltype(last_tag)::value;
+            const int buf = st % NBUF;
             // memory phase: the fragment reads of stage st, with the loads of
             // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
             // to different units)
             read_frag(buf, S0{}, f0, g0 + st);
-            load_stage(st + AHEAD, 0);
+            if constexpr (!LAST) load_stage(st + AHEAD, 0);
             read_frag(buf, S1{}, f1, g0 + st);
-            load_stage(st + AHEAD, 1);
+            if constexpr (!LAST) load_stage(st + AHEAD, 1);
             __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
             tie(f0);
             tie(f1);
-            keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
+            if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
             bar();
             // compute phase
             decode_b(f0);
@@ -484,37 +491,76 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             decode_b(f1);
             mfmas(f1);
             bar();
-            buf = buf + 1 == NBUF ? 0 : buf + 1;
-        }
+        };
+        for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
+        // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
+        step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
         // (every fragment read in this loop is consumed in its own step; settling
         // here keeps the rule that no transposing read is left in flight)
         settle(f0);
         settle(f1);
         if (!lag) bar();
     } else {
+        // Four waves, one per SIMD: each wave hides its own LDS reads and buffer
+        // loads behind its MFMAs, so the instruction order is fixed by hand
+        // (sched_barrier after every MFMA).  The fragment reads of the next
+        // substep go between the first two thirds of the MFMAs, so the last third
+        // covers their latency and the wait before the barrier finds them done;
+        // the loads of stage st+NBUF go between the rest.
+        constexpr int NM = FM * FN, NRD = FM + FN, NLD = A_LD + B_LD + S_LD;
+        constexpr int QR = NM >= 3 ? 2 * NM / 3 : NM;
+        auto read_slot = [](int r) { return r * QR / NRD; };
+        auto load_slot = [](int i) {
+            const int q = QR + i * (NM - QR) / NLD;
+            return q < NM ? q : NM - 1;
+        };
+        auto read_item = [&](int buf, auto s_tag, int r, Frag &f, int g) {
+            if (r < FM) read_a(buf, s_tag, r, f);
+            else read_b(buf, s_tag, r - FM, f, g);
+        };
+        // One step; the last one (LAST) issues no loads and no reads ahead, needs
+        // no barrier, and masks its second substep when it is a half step.
+        auto step = [&](int st, auto last_tag) {
+            constexpr bool LAST = decltype(last_tag)::value;
+            const int buf = st % NBUF;
+            const int nxt = (st + 1) % NBUF;
+            settle(f0);
+            decode_b(f0);
+#pragma unroll
+            for (int q = 0; q < NM; ++q) {
+                mfma1(f0, q / FN, q % FN);
+#pragma unroll
+                for (int r = 0; r < NRD; ++r)
+                    if (read_slot(r) == q) read_item(buf, S1{}, r, f1, g0 + st);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (!LAST) wait_vm_barrier<(NBUF - 2) * LPS>();
+            settle(f1);
+            if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
+            decode_b(f1);
+#pragma unroll
+            for (int q = 0; q < NM; ++q) {
+                mfma1(f1, q / FN, q % FN);
+                if constexpr (!LAST) {
+#pragma unroll
+                    for (int r = 0; r < NRD; ++r)
+                        if (read_slot(r) == q) read_item(nxt, S0{}, r, f0, g0 + st + 1);
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i)
+                        if (load_slot(i) == q) load_one(st + NBUF, i);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) load_stage(j);
         wait_vm_barrier<(NBUF - 1) * LPS>();
         read_frag(0, S0{}, f0, g0);
-        for (int st = 0; st < nsteps; ++st) {
-            const int buf = st % NBUF;
-            settle(f0);
-            read_frag(buf, S1{}, f1, g0 + st);
-            decode_b(f0);
-            mfmas(f0);
-            wait_vm_barrier<(NBUF - 2) * LPS>();
-            settle(f1);
-            keep_if(f1, st < nfull);   // a final half step: substep 1 adds 0 x 0
-            load_stage(st + NBUF);
-            read_frag((st + 1) % NBUF, S0{}, f0, g0 + st + 1);
-            decode_b(f1);
-            mfmas(f1);
-        }
-        // The last read-ahead is never used, but the compiler does not know that
-        // the transposing reads land later: wait for them and keep their
-        // registers allocated until then, or the epilogue may reuse a register
-        // that an in-flight read still overwrites.
-        settle(f0);
+        for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
+        // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
+        step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
+        // (the last step reads nothing ahead, and settle(f1) waited for its reads:
+        // no transposing read is in flight when the epilogue reuses registers)
     }
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
