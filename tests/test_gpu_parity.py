@@ -268,8 +268,7 @@ def test_every_tiled_variant_on_a_ragged_problem(h):
                              ("e2m1", "e2m1_4096x4096x4096", True)):
         ktail = {"i8": 7 * 64 + 32, "e2m1": 8 * 32}.get(path, 7 * 32 + 16)
         w = synth.make(name, M=290, N=272, K=ktail)
-        for bm, bn, nw in ((128, 256, 4), (256, 256, 8), (256, 256, 4), (256, 128, 4), (128, 128, 4),
-                           (64, 64, 4)):
+        for bm, bn, nw in ((128, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4)):
             for s in (1, 2):
                 o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
                                     force_path=dg.DG_PATH_TILED, force_waves=nw)
@@ -342,7 +341,7 @@ def test_k_zero_and_empty(h):
     run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=0))
     run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=40, N=64, K=0))
     # every loop shape with an empty K range (eight-wave and four-wave tiles)
-    for bm, bn, nw in ((256, 256, 8), (256, 256, 4), (128, 128, 4)):
+    for bm, bn, nw in ((256, 256, 8), (128, 256, 4), (128, 128, 4)):
         o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_path=dg.DG_PATH_TILED,
                             force_waves=nw)
         run(h, synth.make("f16_256x256x256_alpha_beta_d", M=300, N=260, K=0), opts=o)

@@ -16,7 +16,6 @@ namespace dg {
 #define DG_TILE_SHAPES(X, path, kmaj) \
     X(path, kmaj, 128, 256, 2, 2)     \
     X(path, kmaj, 256, 256, 2, 4)     \
-    X(path, kmaj, 256, 256, 2, 2)     \
     X(path, kmaj, 256, 128, 2, 2)     \
     X(path, kmaj, 128, 128, 2, 2)     \
     X(path, kmaj, 64, 64, 2, 2)
@@ -77,7 +76,6 @@ constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
 constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
 {
     const double base = waves == 8 ? 0.48
-                      : bm * bn >= 256 * 256 ? 0.42
                       : bm * bn >= 256 * 128 ? 0.40
                       : bm * bn >= 128 * 128 ? 0.30 : 0.15;
     return base * (path == 2 /*P_I8*/ ? 0.95 : (path == 3 /*P_E2M1*/ ? 0.87 : 1.0));

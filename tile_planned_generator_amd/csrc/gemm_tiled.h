@@ -399,16 +399,21 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             }
         }
     };
+    // The B fragment goes in as the MFMA's first operand and the A fragment as
+    // its second (each lane holds 8 consecutive k of one column of B, or of one
+    // row of A, which is what either operand slot takes), so a block accumulates
+    // the transposed product: lane l holds row lr of the block and, in registers
+    // 4j .. 4j+3, its columns 8j + 4kg .. 8j + 4kg + 3.
     auto mfma1 = [&](const Frag &f, int mi, int ni) {
         if constexpr (PATH == P_F16 || PATH == P_E2M1)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(half8, f.a[mi]), __builtin_bit_cast(half8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+                __builtin_bit_cast(half8, f.b[ni]), __builtin_bit_cast(half8, f.a[mi]), acc[mi][ni], 0, 0, 0);
         else if constexpr (PATH == P_BF16)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, f.a[mi]), __builtin_bit_cast(bf16x8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, f.b[ni]), __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
         else
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                __builtin_bit_cast(intx4, f.a[mi]), __builtin_bit_cast(intx4, f.b[ni]), acc[mi][ni], 0, 0, 0);
+                __builtin_bit_cast(intx4, f.b[ni]), __builtin_bit_cast(intx4, f.a[mi]), acc[mi][ni], 0, 0, 0);
     };
     auto mfmas = [&](const Frag &f) {
 #pragma unroll
@@ -564,7 +569,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     }
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
-    // and stores them four columns per lane, row-contiguously.
+    // (a 16-byte write per four columns of a row: the blocks are transposed) and
+    // stores them four columns per lane, row-contiguously.  Storing the
+    // transposed blocks straight from registers instead (32 rows of 32 bytes per
+    // store) took 2-4x longer.
     constexpr int RP = WTN + 4;   // padded row pitch (elements) of the staging area
     static_assert(NW * 32 * RP * 4 <= LDS_BYTES, "epilogue staging");
     __syncthreads();   // every wave is done with the last K stage
@@ -572,13 +580,25 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     using Vec4 = typename std::conditional<IS_I8, intx4, floatx4>::type;
     ScalarT *sE = reinterpret_cast<ScalarT *>(smem) + wave * 32 * RP;
     constexpr int LPR = WTN / 4;    // lanes per row (4 columns each)
-    constexpr int RPI = 64 / LPR;   // rows per iteration
+    constexpr int RPI = 64 / LPR;   // rows per read
+    constexpr int NIT = 32 / RPI;   // reads per 32 rows
     const int er = lane / LPR, ec = (lane % LPR) * 4;
     const bool vec_ok = epi_vec_ok(p.epi, p.split_k > 1, p.ws, N);
+    constexpr int EB = NIT < 4 ? NIT : 4;   // rows per batch (a larger batch makes the float epilogues spill)
+    using DVec4 = typename std::conditional<IS_I8, intx4, floatx4>::type;
+    // This lane's four columns are the same in every row: the bias is loaded once.
+    const int col = n0 + wn * WTN + ec;
+    const bool vec_col = vec_ok && col + 3 < N;
+    const int mode = p.split_k > 1 ? 0 : (p.epi.d_read || p.epi.kind != E_NONE ? 2 : 1);
+    floatx4 bias4 = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (vec_col && p.split_k == 1) {
+        if constexpr (IS_I8) bias4 = epi_bias4_i(p.epi, col);
+        else bias4 = epi_bias4_f(p.epi, col);
+    }
     // The store code (with the whole epilogue inlined) is too large to unroll FM
     // times, and a rolled loop must not index the accumulators at run time (that
-    // demotes them all to private memory): the rolled loop stages block mi through
-    // copies with constant indices instead.
+    // demotes them all to private memory): the rolled loop stages row block mi
+    // through copies with constant indices instead.
 #pragma unroll 1
     for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
@@ -587,43 +607,109 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
                 for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        sE[(8 * (v >> 2) + 4 * kg + (v & 3)) * RP + ni * 32 + lr] = acc[m][ni][v];
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<Vec4 *>(sE + lr * RP + ni * 32 + 8 * j + 4 * kg) =
+                            Vec4{acc[m][ni][4 * j], acc[m][ni][4 * j + 1], acc[m][ni][4 * j + 2],
+                                 acc[m][ni][4 * j + 3]};
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Rows go in batches of EB: the batch's LDS reads (and D loads) are issued
+        // before its stores, so their latencies overlap.  Three separate bodies:
+        // split-K partials, the plain alpha * acc, and the full epilogue.  The
+        // plain one carries no code for D, bias or activation (the smaller code
+        // alone saved several microseconds per launch), and only the full one
+        // loads from memory inside the loop: a load waited for after a store waits
+        // for that store too.
         const int row0 = m0 + wm * WTM + mi * 32;
-        const int col = n0 + wn * WTN + ec;
-#pragma unroll 1
-        for (int it = 0; it < 32 / RPI; ++it) {
-            const int r = it * RPI + er;
-            const int row = row0 + r;
-            const Vec4 x = *reinterpret_cast<const Vec4 *>(sE + r * RP + ec);
-            if (row < M) {
-                if (vec_ok && col + 3 < N) {
-                    if (p.split_k > 1)
-                        *reinterpret_cast<Vec4 *>(reinterpret_cast<ScalarT *>(p.ws) +
-                                                  ((int64_t)split * M + row) * N + col) = x;
-                    else if constexpr (IS_I8)
-                        epi_store4_i(p.epi, row, col, x);
-                    else
-                        epi_store4_f(p.epi, row, col, x);
-                } else {
+        auto batch = [&](auto mode_tag, int it0) {
+            constexpr int MODE = decltype(mode_tag)::value;
+            Vec4 x[EB];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (col + e < N) {
-                            if (p.split_k > 1)
-                                reinterpret_cast<ScalarT *>(p.ws)[((int64_t)split * M + row) * N + col + e] = x[e];
-                            else if constexpr (IS_I8)
-                                epi_store_i(p.epi, row, col + e, x[e]);
+            for (int u = 0; u < EB; ++u)
+                x[u] = *reinterpret_cast<const Vec4 *>(sE + ((it0 + u) * RPI + er) * RP + ec);
+            DVec4 d[EB];
+#pragma unroll
+            for (int u = 0; u < EB; ++u) d[u] = DVec4{0, 0, 0, 0};
+            if constexpr (MODE == 2) {
+                if (p.epi.d_read) {
+#pragma unroll
+                    for (int u = 0; u < EB; ++u) {
+                        const int row = min(row0 + (it0 + u) * RPI + er, M - 1);
+                        if (vec_col) {
+                            if constexpr (IS_I8)
+                                d[u] = *reinterpret_cast<const intx4 *>(reinterpret_cast<const int32_t *>(p.epi.D) +
+                                                                        (int64_t)row * p.epi.ldd + col);
                             else
-                                epi_store_f(p.epi, row, col + e, x[e]);
+                                d[u] = load4_f32(p.epi.D, p.epi.out_type, (int64_t)row * p.epi.ldd + col);
                         }
                     }
                 }
             }
+#pragma unroll
+            for (int u = 0; u < EB; ++u) {
+                const int row = row0 + (it0 + u) * RPI + er;
+                if (row >= M) continue;
+                if constexpr (MODE == 0) {
+                    ScalarT *w = reinterpret_cast<ScalarT *>(p.ws) + ((int64_t)split * M + row) * N;
+                    if (vec_col) {
+                        *reinterpret_cast<Vec4 *>(w + col) = x[u];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col + e < N) w[col + e] = x[u][e];
+                    }
+                } else if constexpr (MODE == 1) {
+                    const int64_t c0 = (int64_t)row * p.epi.ldc + col;
+                    if constexpr (IS_I8) {
+                        intx4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (int)((uint32_t)p.epi.ialpha * (uint32_t)x[u][e]);
+                        if (vec_col) {
+                            __builtin_nontemporal_store(v, reinterpret_cast<intx4 *>(
+                                                               reinterpret_cast<int32_t *>(p.epi.C) + c0));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < N) reinterpret_cast<int32_t *>(p.epi.C)[c0 + e] = v[e];
+                        }
+                    } else {
+                        const floatx4 v = p.epi.alpha * x[u];
+                        if (vec_col) {
+                            store4_f32(p.epi.C, p.epi.out_type, c0, v);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < N) store_f32(p.epi.C, p.epi.out_type, c0 + e, v[e]);
+                        }
+                    }
+                } else {
+                    if (vec_col) {
+                        if constexpr (IS_I8)
+                            epi_out4_i(p.epi, row, col, x[u], d[u], bias4);
+                        else
+                            epi_out4_f(p.epi, row, col, x[u], d[u], bias4);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (col + e < N) {
+                                if constexpr (IS_I8)
+                                    epi_store_i(p.epi, row, col + e, x[u][e]);
+                                else
+                                    epi_store_f(p.epi, row, col + e, x[u][e]);
+                            }
+                        }
+                    }
+                }
+            }
+        };
+#pragma unroll 1
+        for (int it0 = 0; it0 < NIT; it0 += EB) {
+            if (mode == 0) batch(std::integral_constant<int, 0>{}, it0);
+            else if (mode == 1) batch(std::integral_constant<int, 1>{}, it0);
+            else batch(std::integral_constant<int, 2>{}, it0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

@@ -189,26 +189,43 @@ DG_DEV void store4_f32(void *p, int type, int64_t idx, floatx4 v)
         __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(p) + idx));
 }
 
-// epi_store_f on four consecutive columns j .. j+3 (the same arithmetic per element)
-DG_DEV void epi_store4_f(const EpiArgs &e, int64_t i, int64_t j, floatx4 acc)
+// epi_store_f on four consecutive columns j .. j+3 (the same arithmetic per
+// element), on values already loaded: d holds D's four values (used when D is
+// read), b the bias's four values (used by the bias kinds).
+DG_DEV void epi_out4_f(const EpiArgs &e, int64_t i, int64_t j, floatx4 acc, floatx4 d, floatx4 b)
 {
     floatx4 v = e.alpha * acc;
-    if (e.d_read) v += e.beta * load4_f32(e.D, e.out_type, i * e.ldd + j);
-    if (e.kind == E_BIAS || e.kind == E_BIAS_GELU) v += load4_f32(e.bias, e.bias_type, j);
+    if (e.d_read) v += e.beta * d;
+    if (e.kind == E_BIAS || e.kind == E_BIAS_GELU) v += b;
     if (e.kind == E_GELU || e.kind == E_BIAS_GELU)
         v = floatx4{gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)};
     store4_f32(e.C, e.out_type, i * e.ldc + j, v);
 }
 
-// epi_store_i on four consecutive columns j .. j+3 (the same arithmetic per element)
-DG_DEV void epi_store4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc)
+// The bias's four values at columns j .. j+3 for the float epilogue (zeros when
+// the kind has no bias).
+DG_DEV floatx4 epi_bias4_f(const EpiArgs &e, int64_t j)
+{
+    if (e.kind == E_BIAS || e.kind == E_BIAS_GELU) return load4_f32(e.bias, e.bias_type, j);
+    return floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+DG_DEV void epi_store4_f(const EpiArgs &e, int64_t i, int64_t j, floatx4 acc)
+{
+    const floatx4 d = e.d_read ? load4_f32(e.D, e.out_type, i * e.ldd + j) : floatx4{0.f, 0.f, 0.f, 0.f};
+    epi_out4_f(e, i, j, acc, d, epi_bias4_f(e, j));
+}
+
+// epi_store_i on four consecutive columns j .. j+3 (the same arithmetic per
+// element), on values already loaded: d holds D's four values (used when D is
+// read), b the requantisation bias's four values (used when there is a bias).
+DG_DEV void epi_out4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc, intx4 d, floatx4 b)
 {
     if (e.kind == E_RQ_I8 || e.kind == E_RQ_F16) {
         floatx4 v;
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = __fmul_rn((float)acc[c], e.rq_scale);
         if (e.bias) {
-            const floatx4 b = *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(e.bias) + j);
 #pragma unroll
             for (int c = 0; c < 4; ++c) v[c] = __fadd_rn(v[c], b[c]);
         }
@@ -231,11 +248,25 @@ DG_DEV void epi_store4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc)
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = (int)((uint32_t)e.ialpha * (uint32_t)acc[c]);
     if (e.d_read) {
-        const intx4 d = *reinterpret_cast<const intx4 *>(reinterpret_cast<const int32_t *>(e.D) + i * e.ldd + j);
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = (int)((uint32_t)v[c] + (uint32_t)e.ibeta * (uint32_t)d[c]);
     }
     __builtin_nontemporal_store(v, reinterpret_cast<intx4 *>(reinterpret_cast<int32_t *>(e.C) + i * e.ldc + j));
+}
+
+// The requantisation bias's four values at columns j .. j+3 (zeros without one).
+DG_DEV floatx4 epi_bias4_i(const EpiArgs &e, int64_t j)
+{
+    if ((e.kind == E_RQ_I8 || e.kind == E_RQ_F16) && e.bias)
+        return *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(e.bias) + j);
+    return floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+DG_DEV void epi_store4_i(const EpiArgs &e, int64_t i, int64_t j, intx4 acc)
+{
+    const intx4 d = e.d_read ? *reinterpret_cast<const intx4 *>(reinterpret_cast<const int32_t *>(e.D) + i * e.ldd + j)
+                             : intx4{0, 0, 0, 0};
+    epi_out4_i(e, i, j, acc, d, epi_bias4_i(e, j));
 }
 
 // Linear workgroup id -> tile index, keeping each accelerator die (XCD) on a
