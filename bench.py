@@ -253,6 +253,29 @@ def cpu_baseline(budget_s=12.0):
                       f"({rows}x4096x4096 multiply-adds, int64 accumulation), {dt:.2f} s"}
 
 
+def stage_breakdown(h, p, launches=5):
+    """Per-stage s_memtime ticks of the headline kernel from the library's stage
+    clock (dg_set_stage_clock), on untimed launches after the timed ones: medians
+    and maxima over the workgroups of the last launch, and the span from the first
+    workgroup's entry to the last one's end."""
+    import torch
+    from tile_planned_generator_amd import dg
+    grid = p.info.grid
+    buf = torch.zeros(grid * 8, dtype=torch.int64, device="cuda:0")
+    h.set_stage_clock(buf)
+    try:
+        for _ in range(launches):
+            p.launch(0)
+        torch.cuda.synchronize()
+    finally:
+        h.set_stage_clock(None)
+    s = dg.stage_cycles(buf.cpu().numpy(), grid)
+    tot = s["prologue"]["median"] + s["k_loop"]["median"] + s["epilogue"]["median"]
+    s["k_loop_frac"] = round(s["k_loop"]["median"] / max(1, tot), 4)
+    s["unit"] = "s_memtime ticks per workgroup"
+    return s
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +319,12 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["i8"],
                 "unit": "TOP/s", "frac": round(achieved / PEAK["i8"], 4),
                 "traffic": recorded_traffic(HEADLINE), "launch_ms": round(ms_launch, 6)}
+    stages = stage_breakdown(h, p)
+    # the stage clock's tick rate in this kernel (its span over the launch
+    # duration), and the per-workgroup stages converted to microseconds with it
+    tick = stages["span"] / (ms_launch * 1e-3)
+    stages["tick_ghz"] = round(tick / 1e9, 3)
+    stages["us"] = {k: round(stages[k]["median"] / tick * 1e6, 2) for k in ("prologue", "k_loop", "epilogue")}
     del p
     torch.cuda.empty_cache()
 
@@ -329,6 +358,7 @@ def main():
                    "kernel": head["kernel"], "tile": head["tile"], "split_k": head["split_k"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "stages": stages,
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "workloads": workloads,
     }

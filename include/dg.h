@@ -238,6 +238,27 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
                   const dg_epilogue *epi, const dg_plan_opts *opts,
                   void *workspace, size_t workspace_bytes, dg_stream_t stream);
 
+/* Stage clock: the analogue of the generator's profile option, which reads the
+ * clock inside the generated kernel and reports the cycles of each kernel stage
+ * ([generator] section 3.2, the practical notes after the launch code).
+ * While `buf` is set, every tiled-path launch through `h` has each workgroup w
+ * (w = blockIdx.y * gridDim.x + blockIdx.x, for w < entries / 8) write 8
+ * uint64 entries at buf[8w .. 8w+7]:
+ *   0 kernel entry, 1 K-loop start, 2 K-loop end, 3 epilogue end (stores issued)
+ *     - values of the s_memtime counter read by the workgroup's first wave (each
+ *     die counts on its own, so only stamps from one die compare);
+ *   4 HW_ID register (CU, shader array, shader engine), 5 XCC_ID (die),
+ *   6 K steps of the workgroup's slice, 7 blockIdx.x | blockIdx.y << 32.
+ *   h        a live device handle
+ *   buf      device memory owned by the caller, NULL to switch the clock off
+ *   entries  uint64 entries buf holds (>= 0); workgroups past entries / 8 write
+ *            nothing
+ * Skinny-path and reduce launches write nothing.  The setting belongs to the
+ * handle: launches on several threads through one handle share it.  Errors:
+ * DG_ERR_INVALID_STATE (handle NULL, destroyed or offline), DG_ERR_INVALID_ARG
+ * (entries < 0, or buf NULL with entries > 0). */
+dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries);
+
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char *dg_last_error(void);
 

@@ -12,6 +12,8 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from tile_planned_generator_amd import dg
@@ -236,8 +238,11 @@ def test_offline_and_destroyed_handles_are_invalid_state():
     s = dg.dg_gemm(h.h, 16, 16, 16, C.byref(dt), C.byref(lay), 16, 16, None, 0, None, 16,
                    C.byref(one), C.byref(zero), None, None, None, 0, None)
     assert s == dg.DG_ERR_INVALID_STATE and "offline" in dg.dg_last_error()
+    # the stage clock needs a device handle, and a consistent buffer size
+    assert dg.dg_set_stage_clock(h.h, None, 0) == dg.DG_ERR_INVALID_STATE
     raw = C.c_void_p(h.h.value)
     h.close()
+    assert dg.dg_set_stage_clock(raw, None, 0) == dg.DG_ERR_INVALID_STATE
     info = dg.dg_plan_info()
     s = dg.dg_plan(raw, 16, 16, 16, C.byref(dt), C.byref(lay), 0, 0, None, C.byref(info))
     assert s == dg.DG_ERR_INVALID_STATE
@@ -301,3 +306,19 @@ def test_planner_uses_the_compiled_resource_usage(off):
         o = dg.dg_plan_opts(force_m_tile=256, force_waves=nw)
         p = off.plan(2048, 2048, 2048, opts=o)
         assert p.kernel_name.decode().endswith(suffix) and p.waves_per_wg == nw
+
+
+def test_stage_cycles_summary():
+    # four workgroups on two dies whose counters are offset: the span is per die
+    r = np.zeros((4, 8), dtype=np.int64)
+    r[:, 0] = [0, 10, 10**9, 10**9 + 30]
+    r[:, 1] = r[:, 0] + [5, 7, 5, 5]
+    r[:, 2] = r[:, 1] + 100
+    r[:, 3] = r[:, 2] + [20, 20, 40, 20]
+    r[:, 5] = [0, 0, 1, 1]
+    r[:, 6] = 4
+    s = dg.stage_cycles(r, 4)
+    assert s["prologue"] == {"median": 5, "max": 7}
+    assert s["k_loop"] == {"median": 100, "max": 100}
+    assert s["epilogue"] == {"median": 20, "max": 40}
+    assert s["span"] == 155 and s["k_steps"] == 4

@@ -21,6 +21,8 @@ struct dg_handle_s {
     dg_device_desc desc;
     int device;   // -1: offline (planner only)
     std::unordered_map<std::string, Candidate> cache;
+    uint64_t *clk = nullptr;    // stage clock buffer (dg_set_stage_clock), or null
+    int64_t clk_entries = 0;
 };
 
 namespace {
@@ -275,6 +277,16 @@ dg_status dg_destroy(dg_handle_t h)
     return DG_OK;
 }
 
+dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries)
+{
+    if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+    if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: nothing is launched");
+    if (entries < 0 || (!buf && entries > 0)) return fail(DG_ERR_INVALID_ARG, "stage clock: bad buffer size");
+    h->clk = buf;
+    h->clk_entries = buf ? entries : 0;
+    return ok();
+}
+
 dg_status dg_plan(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
                   int32_t group_k, int32_t epi_kind, const dg_plan_opts *opts, dg_plan_info *out)
 {
@@ -416,6 +428,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             ta.group_m = 4;
             ta.ws = workspace;
             ta.epi = ea;
+            ta.clk = reinterpret_cast<unsigned long long *>(h->clk);
+            ta.clk_wgs = h->clk ? h->clk_entries / 8 : 0;
             he = launch_tiled(c.kernel_id, ta, c.grid_x, c.grid_y, st);
         } else {
             SkinnyArgs sa{};

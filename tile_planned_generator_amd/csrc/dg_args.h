@@ -43,6 +43,8 @@ struct TiledArgs {
     int tiles_m, tiles_n, group_m;
     void *ws;                     // split partials [split][M][N] (fp32 or int32)
     EpiArgs epi;
+    unsigned long long *clk;      // stage clock: 8 entries per workgroup, or null
+    int64_t clk_wgs;              // workgroups the stage-clock buffer holds
 };
 
 // Skinny split-K streaming GEMM (small M).

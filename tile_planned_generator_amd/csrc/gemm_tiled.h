@@ -148,6 +148,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int LPS = tiled_min_loads_per_wave(A_NL, B_NL, S_NL, NW);   // fewest loads a wave issues per stage
     static_assert(3 * LPS < 64, "vmcnt range");
 
+    // Stage clock (the generator's profile option): s_memtime stamps at kernel
+    // entry, loop start, loop end and kernel end, taken by wave 0 when a buffer
+    // is given.
+    const bool clk_on = p.clk != nullptr;
+    unsigned long long ck0 = 0, ck1 = 0, ck2 = 0;
+    if (clk_on) ck0 = __builtin_amdgcn_s_memtime();
+
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(DG_LDS char *)smem;
 
@@ -497,6 +504,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             mfmas(f1);
             bar();
         };
+        if (clk_on) ck1 = __builtin_amdgcn_s_memtime();
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
@@ -561,12 +569,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         for (int j = 0; j < NBUF; ++j) load_stage(j);
         wait_vm_barrier<(NBUF - 1) * LPS>();
         read_frag(0, S0{}, f0, g0);
+        if (clk_on) ck1 = __builtin_amdgcn_s_memtime();
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
         // (the last step reads nothing ahead, and settle(f1) waited for its reads:
         // no transposing read is in flight when the epilogue reuses registers)
     }
+
+    if (clk_on) ck2 = __builtin_amdgcn_s_memtime();
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
     // (a 16-byte write per four columns of a row: the blocks are transposed) and
@@ -714,6 +725,26 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // Stage clock record of this workgroup (8 entries, written by lanes 0-7 of
+    // wave 0 with vector stores): the four stamps, the hardware placement
+    // (HW_ID: CU, shader array and engine; XCC_ID: die), the K steps, and the
+    // workgroup's grid coordinates.  The end stamp follows the issue of the last
+    // store, not its completion.
+    if (clk_on) {
+        const unsigned long long ck3 = __builtin_amdgcn_s_memtime();
+        const long long wg = (long long)blockIdx.y * gridDim.x + blockIdx.x;
+        if (wave == 0 && lane < 8 && wg < p.clk_wgs) {
+            const unsigned hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+            const unsigned xcc_id = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+            unsigned long long v = lane == 0 ? ck0 : lane == 1 ? ck1 : lane == 2 ? ck2 : ck3;
+            if (lane == 4) v = hw_id;
+            if (lane == 5) v = xcc_id;
+            if (lane == 6) v = (unsigned long long)nsteps;
+            if (lane == 7) v = (unsigned long long)blockIdx.x | ((unsigned long long)blockIdx.y << 32);
+            p.clk[wg * 8 + lane] = v;
+        }
     }
 }
 

@@ -84,7 +84,7 @@ class dg_plan_info(C.Structure):
 
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
-           "dg_plan_candidates", "dg_gemm", "dg_last_error", "dg_status_str")
+           "dg_plan_candidates", "dg_gemm", "dg_set_stage_clock", "dg_last_error", "dg_status_str")
 
 _lib = None
 
@@ -112,6 +112,7 @@ def load():
         "dg_gemm": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), P, P, P, i32,
                      P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t,
                      P], S),
+        "dg_set_stage_clock": ([H, P, i64], S),
         "dg_last_error": ([], C.c_char_p),
         "dg_status_str": ([C.c_int], C.c_char_p),
     }
@@ -150,6 +151,10 @@ def dg_plan_candidates(*a):
 
 def dg_gemm(*a):
     return load().dg_gemm(*a)
+
+
+def dg_set_stage_clock(h, buf, entries):
+    return load().dg_set_stage_clock(h, buf, entries)
 
 
 def dg_last_error():
@@ -213,6 +218,14 @@ class Handle:
         if self.h:
             check(dg_destroy(self.h))
             self.h = C.c_void_p()
+
+    def set_stage_clock(self, buf):
+        """Record per-workgroup stage clocks of tiled launches into ``buf`` (a
+        device uint64/int64 tensor, 8 entries per workgroup), or stop (None)."""
+        if buf is None:
+            check(dg_set_stage_clock(self.h, None, 0))
+        else:
+            check(dg_set_stage_clock(self.h, C.c_void_p(buf.data_ptr()), buf.numel()))
 
     def __del__(self):
         try:
@@ -306,3 +319,20 @@ class Handle:
                       C.byref(be), C.byref(epi), C.byref(opts) if opts is not None else None,
                       ws_ptr, ws_bytes, stream))
         return info
+
+
+def stage_cycles(rec, wgs):
+    """Summarise stage-clock records ([wgs][8] int64, as written by
+    dg_set_stage_clock): per-workgroup ticks of the prologue (entry to K-loop
+    start), the K loop and the epilogue, as medians and maxima, plus the span
+    from the earliest entry to the latest end.  Each die (XCC) counts on its own
+    clock, so the span is taken per die and the largest is reported."""
+    import numpy as np
+    r = np.asarray(rec, dtype=np.int64).reshape(-1, 8)[:wgs]
+    pro, loop, epi = r[:, 1] - r[:, 0], r[:, 2] - r[:, 1], r[:, 3] - r[:, 2]
+    out = {}
+    for name, v in (("prologue", pro), ("k_loop", loop), ("epilogue", epi)):
+        out[name] = {"median": int(np.median(v)), "max": int(v.max())}
+    out["span"] = int(max(r[r[:, 5] == x, 3].max() - r[r[:, 5] == x, 0].min() for x in np.unique(r[:, 5])))
+    out["k_steps"] = int(np.median(r[:, 6]))
+    return out
