@@ -458,7 +458,14 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             ra.M = (int)M;
             ra.N = (int)N;
             ra.is_int = pr.path == P_I8;
-            ra.lanes = c.split_k <= 8 ? 1 : (c.split_k <= 32 ? 4 : 16);
+            // runs per output: enough threads to keep loads in flight (about 64K),
+            // at most 16 and at most the slices; few slices need no runs
+            {
+                const int64_t groups = std::max<int64_t>(1, M * N / 4);
+                int runs = 1;
+                while (runs < 16 && runs * 2 <= c.split_k && groups * runs < 65536) runs *= 2;
+                ra.lanes = c.split_k <= 8 ? 1 : runs;
+            }
             ra.epi = ea;
             he = launch_reduce(ra, st);
             if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));

@@ -492,15 +492,98 @@ __global__ void __launch_bounds__(256) reduce4_kernel(ReduceArgs a)
     }
 }
 
+// Many slices and N a multiple of 4: R = lanes runs of slices per group of four
+// consecutive outputs.  A workgroup holds 256 / R groups; thread (run r, group
+// g) sums slices [r*C, (r+1)*C) of its four outputs in ascending order, with
+// 16-byte loads that are contiguous across the threads of a run, and the R run
+// sums are then added in run order through LDS.  The order of every addition is
+// fixed, so the result does not depend on timing.
+__global__ void __launch_bounds__(256) reduce_runs_kernel(ReduceArgs a)
+{
+    const int R = a.lanes, G = 256 / R;
+    const int t = threadIdx.x, g = t % G, r = t / G;
+    const int64_t MN = (int64_t)a.M * a.N;
+    const int64_t o4 = ((int64_t)blockIdx.x * G + g) * 4;
+    const bool ok = o4 < MN;
+    const int S = a.split_k;
+    const int C = (S + R - 1) / R;
+    const int s0 = min(S, r * C), s1 = min(S, s0 + C);
+    __shared__ floatx4 part[256];
+    if (a.is_int) {
+        const int32_t *w = reinterpret_cast<const int32_t *>(a.ws) + (ok ? o4 : 0);
+        intx4 acc = intx4{0, 0, 0, 0};
+        for (int s = s0; s < s1; s += 8) {
+            intx4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = (ok && s + u < s1)
+                           ? __builtin_nontemporal_load(reinterpret_cast<const intx4 *>(w + (int64_t)(s + u) * MN))
+                           : intx4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = (int)((uint32_t)acc[c] + (uint32_t)v[u][c]);
+        }
+        part[t] = __builtin_bit_cast(floatx4, acc);
+        __syncthreads();
+        if (r != 0 || !ok) return;
+        for (int q = 1; q < R; ++q) {
+            const intx4 v = __builtin_bit_cast(intx4, part[q * G + g]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = (int)((uint32_t)acc[c] + (uint32_t)v[c]);
+        }
+        const int i = (int)(o4 / a.N), j = (int)(o4 - (int64_t)i * a.N);
+        if (epi_vec_ok(a.epi, false, nullptr, a.N)) {
+            epi_store4_i(a.epi, i, j, acc);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) epi_store_i(a.epi, i, j + c, acc[c]);
+        }
+    } else {
+        const float *w = reinterpret_cast<const float *>(a.ws) + (ok ? o4 : 0);
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int s = s0; s < s1; s += 8) {
+            floatx4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = (ok && s + u < s1)
+                           ? __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(w + (int64_t)(s + u) * MN))
+                           : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        part[t] = acc;
+        __syncthreads();
+        if (r != 0 || !ok) return;
+        for (int q = 1; q < R; ++q) acc += part[q * G + g];
+        const int i = (int)(o4 / a.N), j = (int)(o4 - (int64_t)i * a.N);
+        if (epi_vec_ok(a.epi, false, nullptr, a.N)) {
+            epi_store4_f(a.epi, i, j, acc);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) epi_store_f(a.epi, i, j + c, acc[c]);
+        }
+    }
+}
+
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
     if (a.lanes < 1 || a.lanes > 64 || (a.lanes & (a.lanes - 1))) return hipErrorInvalidValue;
     const int64_t MN = (int64_t)a.M * a.N;
-    if (a.lanes == 1 && (a.N & 3) == 0 && ((uintptr_t)a.ws & 15) == 0) {
-        const int64_t grid4 = (MN / 4 + 255) / 256;
-        if (grid4 > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)grid4, 1, 1), dim3(256, 1, 1), 0, s, a);
-        return hipGetLastError();
+    if ((a.N & 3) == 0 && ((uintptr_t)a.ws & 15) == 0) {
+        if (a.lanes == 1) {
+            const int64_t grid4 = (MN / 4 + 255) / 256;
+            if (grid4 > 0x7fffffff) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)grid4, 1, 1), dim3(256, 1, 1), 0, s, a);
+            return hipGetLastError();
+        }
+        if (a.lanes <= 16) {
+            const int64_t groups = 256 / a.lanes;
+            const int64_t gridr = (MN / 4 + groups - 1) / groups;
+            if (gridr > 0x7fffffff) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(reduce_runs_kernel, dim3((unsigned)gridr, 1, 1), dim3(256, 1, 1), 0, s, a);
+            return hipGetLastError();
+        }
     }
     const int64_t grid = (MN * a.lanes + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
