@@ -259,6 +259,34 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
  * (entries < 0, or buf NULL with entries > 0). */
 dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries);
 
+/* Hardware probe: the measured counterpart of dg_device_desc, the analogue of
+ * the pages' hardware query that feeds candidate generation ([overview]
+ * section 4.1, stage 1; [generator] section 3.2, step 1).  dg_probe enqueues
+ * one probe kernel on `stream`; the caller times it and derives the rate
+ * (tile_planned_generator_amd/probe.py writes the results as a JSON device
+ * description).
+ *   DG_PROBE_STREAM  reads `bytes` (a multiple of 16) of device memory `buf`
+ *                    with 16-byte non-temporal loads on `grid` workgroups of
+ *                    256 threads; `out`: device uint32[grid] (a checksum)
+ *   DG_PROBE_MFMA    `grid` workgroups of 4 waves, each wave `param` rounds of
+ *                    8 independent 32x32x16 fp16 MFMAs (2*32*32*16 flops each);
+ *                    `out`: device float[grid]
+ *   DG_PROBE_LDS     one wave, 1024 dword LDS reads with lane l at word
+ *                    l * param (1 <= param <= 16384); `out`: device uint64[2],
+ *                    out[0] = s_memtime ticks of the reads
+ * Errors: DG_ERR_INVALID_STATE (handle NULL, destroyed or offline; wrong current
+ * device), DG_ERR_INVALID_ARG (NULL out, NULL buf for the stream probe, bad
+ * size, grid or param), DG_ERR_HIP (launch failure). */
+typedef enum { DG_PROBE_STREAM = 0, DG_PROBE_MFMA = 1, DG_PROBE_LDS = 2 } dg_probe_kind;
+dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, int32_t param, void *out,
+                   int32_t grid, dg_stream_t stream);
+
+/* Replace the description a handle plans with (for instance one measured by the
+ * probe), and drop its cached plans.  Errors: DG_ERR_INVALID_STATE (handle NULL
+ * or destroyed), DG_ERR_INVALID_ARG (desc NULL or a non-positive field, as for
+ * dg_create_offline). */
+dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc);
+
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char *dg_last_error(void);
 

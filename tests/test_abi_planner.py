@@ -322,3 +322,31 @@ def test_stage_cycles_summary():
     assert s["k_loop"] == {"median": 100, "max": 100}
     assert s["epilogue"] == {"median": 20, "max": 40}
     assert s["span"] == 155 and s["k_steps"] == 4
+
+
+def test_probe_description_round_trip():
+    # a probe result (JSON dict) becomes the description an offline handle plans with
+    from tile_planned_generator_amd import probe
+    base = dg.default_device_desc()
+    d = {"arch": "gfx950", "desc": {f: getattr(base, f) for f in probe.DESC_FIELDS}}
+    d["desc"].update(cu_count=128, hbm_gbps=6500.0)
+    desc = probe.load_desc(d)
+    assert desc.cu_count == 128 and desc.hbm_gbps == 6500.0 and desc.arch == b"gfx950"
+    assert desc.lds_bytes_per_cu == base.lds_bytes_per_cu
+    h = dg.Handle(offline=dg.default_device_desc())
+    full = h.plan(1, 4096, 131072, "bf16", "bf16", "bf16")
+    h.set_device_desc(desc)          # replaces the description, drops cached plans
+    half = h.plan(1, 4096, 131072, "bf16", "bf16", "bf16")
+    assert half.est_us > full.est_us  # fewer CUs and less bandwidth: a slower estimate
+    bad = probe.load_desc(d)
+    bad.hbm_gbps = 0.0
+    assert dg.dg_set_device_desc(h.h, C.byref(bad)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_set_device_desc(h.h, None) == dg.DG_ERR_INVALID_ARG
+    # the probe kernels need a device handle
+    assert dg.dg_probe(h.h, dg.DG_PROBE_LDS, None, 0, 1, None, 1, None) == dg.DG_ERR_INVALID_STATE
+    # the shipped MI355X description (written by the probe on the device) plans too
+    shipped = probe.load_desc(os.path.join(ROOT, "tile_planned_generator_amd", "devices", "mi355x.json"))
+    assert shipped.cu_count == 256 and 5000 < shipped.hbm_gbps < 8000
+    h.set_device_desc(shipped)
+    assert h.plan(4096, 4096, 4096, "i8", "i8", "i32").split_k == 1
+    h.close()

@@ -277,6 +277,56 @@ dg_status dg_destroy(dg_handle_t h)
     return DG_OK;
 }
 
+namespace {
+bool desc_valid(const dg_device_desc *d)
+{
+    return d && d->cu_count > 0 && d->simd_per_cu > 0 && d->lds_bytes_per_cu > 0 && d->lds_bytes_per_wg > 0 &&
+           d->vgpr_per_lane > 0 && d->max_waves_per_simd > 0 && d->clock_ghz > 0 && d->hbm_gbps > 0;
+}
+}  // namespace
+
+dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (!desc_valid(desc)) return fail(DG_ERR_INVALID_ARG, "device description is NULL or has a non-positive field");
+        h->desc = *desc;
+        h->cache.clear();
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_set_device_desc");
+    }
+}
+
+dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, int32_t param, void *out,
+                   int32_t grid, dg_stream_t stream)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: nothing is launched");
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+            return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
+        if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
+        if (kind == DG_PROBE_STREAM) {
+            if (!buf || bytes == 0 || bytes % 16 || grid <= 0)
+                return fail(DG_ERR_INVALID_ARG, "stream probe: buf, a multiple of 16 bytes and grid > 0");
+        } else if (kind == DG_PROBE_MFMA) {
+            if (param < 0 || grid <= 0) return fail(DG_ERR_INVALID_ARG, "MFMA probe: param >= 0 and grid > 0");
+        } else if (kind == DG_PROBE_LDS) {
+            if (param < 1 || param > 16384) return fail(DG_ERR_INVALID_ARG, "LDS probe: 1 <= param <= 16384");
+        } else {
+            return fail(DG_ERR_INVALID_ARG, "unknown probe kind");
+        }
+        const hipError_t he = launch_probe(kind, const_cast<void *>(buf), bytes, param, out, grid,
+                                           reinterpret_cast<hipStream_t>(stream));
+        if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("probe launch: ") + hipGetErrorString(he));
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_probe");
+    }
+}
+
 dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries)
 {
     if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");

@@ -25,4 +25,7 @@ hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int grid_x, int grid_
 // Split-K reduction and epilogue.
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
+// Hardware probe kernels (dg_probe): kind 0 stream read, 1 MFMA, 2 LDS banks.
+hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s);
+
 }  // namespace dg

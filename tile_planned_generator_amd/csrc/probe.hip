@@ -1,0 +1,121 @@
+// probe.hip - hardware probe kernels: the measured half of the device
+// description the planner plans with ([overview] section 4.1, stage 1: the
+// hardware-aware input to candidate generation; [generator] section 3.2,
+// step 1: the per-GPU hardware description).  Each kernel measures one thing;
+// the host side (dg_probe in api.cpp, tile_planned_generator_amd/probe.py)
+// times it and turns the time into a rate.
+#include <hip/hip_runtime.h>
+
+#include "kcommon.h"
+#include "launch.h"
+
+namespace dg {
+
+// Streams `n16` 16-byte chunks from `buf` with non-temporal loads: workgroup w
+// reads its own contiguous share, 256 consecutive chunks (4 KB) per load round
+// and eight rounds in flight, and folds them into one word per workgroup so
+// that no load is dead.
+__global__ void __launch_bounds__(256) probe_stream_kernel(const u32x4 *buf, int64_t n16, unsigned *sink)
+{
+    unsigned acc = 0;
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t beg = (int64_t)blockIdx.x * per;
+    const int64_t end = beg + per < n16 ? beg + per : n16;
+    int64_t i = beg + threadIdx.x;
+    for (; i + 7 * 256 < end; i += 8 * 256) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < end; i += 256) {
+        const u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, off, 64);
+    __shared__ unsigned w[4];
+    if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = w[0] ^ w[1] ^ w[2] ^ w[3];
+}
+
+// Back-to-back independent 32x32x16 fp16 MFMAs: `iters` rounds of 8 per wave.
+__global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float *sink)
+{
+    floatx16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    half8 a, b;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        a[v] = (_Float16)((threadIdx.x & 7) * 0.001f);
+        b[v] = (_Float16)(v * 0.01f);
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[i][v];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    __shared__ float w[4];
+    if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = w[0] + w[1] + w[2] + w[3];
+}
+
+// One wave: 1024 dword LDS reads in which lane l reads word l * stride (plus a
+// multiple of 256 words that changes per read and keeps the bank of any bank
+// count up to 256), modulo the 16384 words of a 64 KB array; writes the
+// s_memtime ticks they took.  Reads of lanes that fall in one bank are
+// serialised, so the ticks grow with the number of lanes per bank.
+__global__ void __launch_bounds__(64) probe_lds_kernel(int stride, unsigned long long *ticks)
+{
+    __shared__ unsigned lds[16384];
+    const int lane = threadIdx.x;
+    for (int i = lane; i < 16384; i += 64) lds[i] = (unsigned)i * 2654435761u;
+    __syncthreads();
+    const unsigned idx = ((unsigned)lane * (unsigned)stride) & 16383u;
+    unsigned acc = 0;
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int r = 0; r < 64; ++r) {
+        unsigned v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = lds[(idx + (unsigned)(r * 16 + u) * 256u) & 16383u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every read of the round is done
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    if (lane == 0) ticks[0] = t1 - t0;
+    if (acc == 0x12345678u) ticks[1] = acc;   // keeps the reads live
+}
+
+hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s)
+{
+    if (kind == 0) {
+        if (bytes % 16 || grid <= 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(probe_stream_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<const u32x4 *>(buf),
+                           (int64_t)(bytes / 16), reinterpret_cast<unsigned *>(out));
+    } else if (kind == 1) {
+        if (param < 0 || grid <= 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(256), 0, s, param, reinterpret_cast<float *>(out));
+    } else if (kind == 2) {
+        if (param < 1 || param > 16384) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(probe_lds_kernel, dim3(1), dim3(64), 0, s, param,
+                           reinterpret_cast<unsigned long long *>(out));
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dg

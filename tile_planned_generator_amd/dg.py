@@ -21,6 +21,7 @@ DG_EPI_NONE, DG_EPI_BIAS, DG_EPI_GELU_ERF, DG_EPI_BIAS_GELU_ERF, DG_EPI_REQUANT_
     DG_EPI_REQUANT_F16 = range(6)
 DG_UNIT_AUTO, DG_UNIT_MFMA, DG_UNIT_VALU = 0, 1, 2
 DG_PATH_AUTO, DG_PATH_TILED, DG_PATH_SKINNY = 0, 1, 2
+DG_PROBE_STREAM, DG_PROBE_MFMA, DG_PROBE_LDS = 0, 1, 2
 
 EPI = {"none": DG_EPI_NONE, "bias": DG_EPI_BIAS, "gelu_erf": DG_EPI_GELU_ERF,
        "bias_gelu_erf": DG_EPI_BIAS_GELU_ERF, "requant_i8": DG_EPI_REQUANT_I8,
@@ -84,7 +85,8 @@ class dg_plan_info(C.Structure):
 
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
-           "dg_plan_candidates", "dg_gemm", "dg_set_stage_clock", "dg_last_error", "dg_status_str")
+           "dg_plan_candidates", "dg_gemm", "dg_set_stage_clock", "dg_probe", "dg_set_device_desc",
+           "dg_last_error", "dg_status_str")
 
 _lib = None
 
@@ -113,6 +115,8 @@ def load():
                      P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t,
                      P], S),
         "dg_set_stage_clock": ([H, P, i64], S),
+        "dg_probe": ([H, i32, P, C.c_size_t, i32, P, i32, P], S),
+        "dg_set_device_desc": ([H, C.POINTER(dg_device_desc)], S),
         "dg_last_error": ([], C.c_char_p),
         "dg_status_str": ([C.c_int], C.c_char_p),
     }
@@ -155,6 +159,14 @@ def dg_gemm(*a):
 
 def dg_set_stage_clock(h, buf, entries):
     return load().dg_set_stage_clock(h, buf, entries)
+
+
+def dg_probe(h, kind, buf, nbytes, param, out, grid, stream):
+    return load().dg_probe(h, kind, buf, nbytes, param, out, grid, stream)
+
+
+def dg_set_device_desc(h, desc):
+    return load().dg_set_device_desc(h, desc)
 
 
 def dg_last_error():
@@ -218,6 +230,10 @@ class Handle:
         if self.h:
             check(dg_destroy(self.h))
             self.h = C.c_void_p()
+
+    def set_device_desc(self, desc):
+        """Plan with ``desc`` (a dg_device_desc, e.g. probe.load_desc(path)) from now on."""
+        check(dg_set_device_desc(self.h, C.byref(desc)))
 
     def set_stage_clock(self, buf):
         """Record per-workgroup stage clocks of tiled launches into ``buf`` (a
