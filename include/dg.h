@@ -132,7 +132,16 @@ typedef struct {
     int32_t unit;             /* dg_unit: MFMA (matrix cores) or VALU (vector FMA)  */
     int32_t lds_limit_bytes;  /* LDS budget per workgroup (0 = device maximum)      */
     float target_occupancy;   /* minimum waves per SIMD as a fraction of 8 (0 = 0.125) */
-    int32_t pad_k;            /* reserved: must be 0 (K tails must be MFMA-aligned) */
+    int32_t pad_k;            /* 1: K need not be a multiple of the MFMA depth (16 for
+                                 16-bit inputs, 32 for int8): the planned kernels take the
+                                 aligned part of K and write partial sums, a tail kernel
+                                 adds the last K % depth products as one more partial,
+                                 and the split-K reduction applies the epilogue (the
+                                 pages' padding-aware kernel for such K, [overview]
+                                 section 3.5, third lesson; section 5.1, case B).
+                                 Leading dimensions must still be 16-byte multiples;
+                                 e2m1 is not supported (DG_ERR_UNSUPPORTED).  0: such a
+                                 K is DG_ERR_ALIGNMENT. */
     int32_t force_waves;      /* waves per workgroup of the tiled path (0 = free)    */
 } dg_plan_opts;
 

@@ -225,7 +225,7 @@ def test_unsupported_and_invalid(off):
     assert _status(off.plan, 64, 64, 64, "f16", "f16", "f16", epilogue="requant_i8")[0] == \
         dg.DG_ERR_UNSUPPORTED
     assert _status(off.plan, -1, 64, 64)[0] == dg.DG_ERR_INVALID_ARG
-    assert _status(off.plan, 64, 64, 64, opts=dg.dg_plan_opts(pad_k=1))[0] == dg.DG_ERR_UNSUPPORTED
+    assert _status(off.plan, 64, 64, 64, opts=dg.dg_plan_opts(pad_k=2))[0] == dg.DG_ERR_INVALID_ARG
     # leading dimension smaller than the matrix, or not 16-byte rows
     assert _status(off.plan, 64, 64, 64, lda=32)[0] == dg.DG_ERR_INVALID_ARG
     assert _status(off.plan, 64, 64, 64, ldb=68)[0] == dg.DG_ERR_ALIGNMENT
@@ -350,3 +350,25 @@ def test_probe_description_round_trip():
     h.set_device_desc(shipped)
     assert h.plan(4096, 4096, 4096, "i8", "i8", "i32").split_k == 1
     h.close()
+
+
+def test_pad_k_plans(off):
+    # an aligned K: pad_k changes nothing
+    a = off.plan(512, 512, 1024, opts=dg.dg_plan_opts(pad_k=1))
+    b = off.plan(512, 512, 1024)
+    assert a.split_k == b.split_k and a.workspace_bytes == b.workspace_bytes
+    # K = 1000 (f16, 8 past a multiple of 16): the aligned part's slices plus one
+    # tail slice, all reduced from the workspace
+    # (leading dimensions stay 16-byte multiples: A's rows are padded)
+    for (M, N, K, lda, a_t, c_t, unit) in ((512, 512, 1000, 1000, "f16", "f16", 16),
+                                            (1, 4096, 4100, 4104, "bf16", "bf16", 16),
+                                            (300, 208, 100, 112, "i8", "i32", 32), (64, 64, 7, 8, "f16", "f16", 16)):
+        info = off.plan(M, N, K, a_t, a_t, c_t, opts=dg.dg_plan_opts(pad_k=1), lda=lda)
+        main = off.plan(M, N, K - K % unit, a_t, a_t, c_t) if K >= unit else None
+        slices = (main.split_k if main else 0) + 1
+        assert info.split_k == slices
+        assert info.workspace_bytes == slices * M * N * 4
+        assert info.est_us > (main.est_us if main else 0)
+    # e2m1 K must stay whole groups
+    s, _ = _status(off.plan, 64, 64, 48, "f16", "e2m1", "f16", opts=dg.dg_plan_opts(pad_k=1))
+    assert s == dg.DG_ERR_UNSUPPORTED

@@ -336,6 +336,27 @@ def test_int_alpha_beta_d(h):
     run(h, w, alpha=3, beta=-2)
 
 
+def test_pad_k(h):
+    # K not a multiple of the MFMA depth: the aligned part runs as planned, a tail
+    # kernel adds the rest as one more partial slice, the reduction applies the
+    # epilogue.  Rows are padded to 16-byte leading dimensions.
+    o = dg.dg_plan_opts(pad_k=1)
+    # tiled f16, 7 full steps + 8, bias + GELU (applied by the reduction)
+    run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=300, N=264, K=7 * 32 + 8), opts=o, pad=8)
+    # tiled f16 with a K split, then the tail
+    run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=512, N=512, K=2048 + 8),
+        opts=dg.dg_plan_opts(pad_k=1, force_split_k=4, force_path=dg.DG_PATH_TILED), pad=8)
+    # skinny bf16 (VALU at M=1, MFMA at M=16)
+    run(h, synth.make("bf16_1x4096x131072", M=1, N=1000, K=4100), opts=o, pad=8)
+    run(h, synth.make("bf16_16x4096x131072", M=16, N=512, K=1004), opts=o, pad=8)
+    # int8, bit-exact, K = 3 * 32 + 4, B row- and column-major
+    w = synth.make("i8_4096x4096x4096", M=300, N=200, K=100)
+    run(h, w, opts=o, pad=16)
+    run(h, w, opts=o, pad=16, b_colmajor=True)
+    # fp16 with alpha, beta * D and only a tail (K < 16)
+    run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=7), opts=o, pad=8)
+
+
 def test_k_zero_and_empty(h):
     # K = 0: the sum is empty and C = act(alpha*0 + beta*D + bias)
     run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=0))

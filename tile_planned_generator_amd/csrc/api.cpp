@@ -66,7 +66,7 @@ int elt_size(int e) { return (e == T_F16 || e == T_BF16) ? 2 : (e == T_I8 ? 1 : 
 
 // Validate a problem description and build the planner's view of it.
 dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
-                   int32_t group_k, int32_t epi_kind, int beta_nz, Problem &pr)
+                   int32_t group_k, int32_t epi_kind, int beta_nz, int pad_k, Problem &pr)
 {
     if (!dt) return fail(DG_ERR_INVALID_ARG, "dtypes is NULL");
     if (M < 0 || N < 0 || K < 0) return fail(DG_ERR_INVALID_ARG, "negative size");
@@ -112,9 +112,14 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
         return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
     // alignment: K in whole MFMA steps, rows on 16-byte boundaries
     const int ksub = (path == P_I8 || path == P_E2M1) ? 32 : 16;
-    if (K % ksub)
-        return fail(DG_ERR_ALIGNMENT, "K dimension not aligned to the MFMA depth (" + std::to_string(ksub) +
-                                          "); padding (pad_k) is not supported");
+    int64_t k_pad = 0;
+    if (K % ksub) {
+        if (!pad_k)
+            return fail(DG_ERR_ALIGNMENT, "K dimension not aligned to the MFMA depth (" + std::to_string(ksub) +
+                                              "); set pad_k to add the tail separately");
+        if (path == P_E2M1) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs K in whole 32-element groups");
+        k_pad = K % ksub;
+    }
     if (path == P_E2M1 && group_k != 32) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs group_k == 32");
     const int esz = path == P_I8 ? 1 : 2;
     if (K > 0) {   // with K == 0 neither A nor B is read
@@ -127,7 +132,8 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
     }
     pr.M = M;
     pr.N = N;
-    pr.K = K;
+    pr.K = K - k_pad;   // the aligned part; pad_k adds the rest as one more partial slice
+    pr.k_pad = k_pad;
     pr.path = path;
     pr.b_kmajor = L.b == DG_COL_MAJOR;
     pr.out_type = elt_of(dt->c);
@@ -147,16 +153,33 @@ dg_plan_opts opts_or_default(const dg_plan_opts *o)
 std::string cache_key(const Problem &p, const dg_plan_opts &o)
 {
     char k[256];
-    std::snprintf(k, sizeof k, "%lld,%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
-                  (long long)p.M, (long long)p.N, (long long)p.K, p.path, p.b_kmajor, p.out_type, p.epi,
+    std::snprintf(k, sizeof k, "%lld,%lld,%lld+%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
+                  (long long)p.M, (long long)p.N, (long long)p.K, (long long)p.k_pad, p.path, p.b_kmajor,
+                  p.out_type, p.epi,
                   p.beta_nz, o.force_m_tile, o.force_n_tile, o.force_k_tile, o.force_split_k, o.force_path,
                   o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k, o.force_waves);
     return k;
 }
 
+// pad_k: the plan of the aligned part, plus one partial slice for the K tail;
+// the partials are then reduced, with the epilogue, by the split-K reduction.
+void add_tail(const Problem &pr, const dg_device_desc &d, Candidate &c)
+{
+    if (!pr.k_pad) return;
+    c.k_pad = (int)pr.k_pad;
+    if (pr.K == 0) {   // no aligned part: the tail is the only slice, no main launch
+        c.split_k = 0;
+        c.grid_y = 0;
+    }
+    const int64_t slices = c.split_k + 1;
+    c.ws_bytes = slices * pr.M * pr.N * 4;
+    // the tail kernel and the reduce: partials written and read once, two launches
+    c.est_us += (double)(slices + 1) * pr.M * pr.N * 4 / (d.hbm_gbps * 1e3) + 2 * 4.0;
+}
+
 dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, Candidate &out)
 {
-    if (o.pad_k) return fail(DG_ERR_UNSUPPORTED, "pad_k is reserved and must be 0");
+    if (o.pad_k < 0 || o.pad_k > 1) return fail(DG_ERR_INVALID_ARG, "pad_k is 0 or 1");
     if (o.unit < DG_UNIT_AUTO || o.unit > DG_UNIT_VALU) return fail(DG_ERR_INVALID_ARG, "unknown unit");
     if (o.force_path < DG_PATH_AUTO || o.force_path > DG_PATH_SKINNY)
         return fail(DG_ERR_INVALID_ARG, "unknown path");
@@ -173,6 +196,7 @@ dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, C
     PlanResult r = plan_problem(pr, h->desc, o);
     if (r.status != DG_OK) return fail(r.status, r.message);
     out = r.pareto.front();
+    add_tail(pr, h->desc, out);
     h->cache.emplace(key, out);
     return DG_OK;
 }
@@ -343,7 +367,7 @@ dg_status dg_plan(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
     try {
         if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
         Problem pr;
-        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, pr);
+        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, opts_or_default(opts).pad_k, pr);
         if (s) return s;
         Candidate c;
         s = plan_cached(h, pr, opts_or_default(opts), c);
@@ -362,15 +386,18 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K, con
     try {
         if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
         if (cap < 0 || (cap > 0 && !out)) return fail(DG_ERR_INVALID_ARG, "bad output array");
-        Problem pr;
-        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, pr);
-        if (s) return s;
         dg_plan_opts o = opts_or_default(opts);
-        if (o.pad_k) return fail(DG_ERR_UNSUPPORTED, "pad_k is reserved and must be 0");
+        if (o.pad_k < 0 || o.pad_k > 1) return fail(DG_ERR_INVALID_ARG, "pad_k is 0 or 1");
+        Problem pr;
+        dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
+        if (s) return s;
         PlanResult r = plan_problem(pr, h->desc, o);
         if (r.status != DG_OK) return fail(r.status, r.message);
         if (count) *count = (int32_t)r.pareto.size();
-        for (int i = 0; i < cap && i < (int)r.pareto.size(); ++i) fill_info(r.pareto[i], &out[i]);
+        for (int i = 0; i < cap && i < (int)r.pareto.size(); ++i) {
+            add_tail(pr, h->desc, r.pareto[i]);
+            fill_info(r.pareto[i], &out[i]);
+        }
         return ok();
     } catch (...) {
         return fail(DG_ERR_INTERNAL, "exception in dg_plan_candidates");
@@ -395,7 +422,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         dg_epilogue E{};
         if (epi) E = *epi;
         Problem pr;
-        dg_status s = describe(M, N, K, dt, lay, group_k, E.kind, beta_nz, pr);
+        dg_status s = describe(M, N, K, dt, lay, group_k, E.kind, beta_nz, opts_or_default(opts).pad_k, pr);
         if (s) return s;
         const bool rq = E.kind == DG_EPI_REQUANT_I8 || E.kind == DG_EPI_REQUANT_F16;
         if (rq && ia != 1) return fail(DG_ERR_INVALID_ARG, "requantise epilogues need alpha == 1 (use epi->scale)");
@@ -460,7 +487,14 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         const int64_t ldb = L.ldb ? L.ldb : (pr.b_kmajor ? K : N);
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
         hipError_t he = hipSuccess;
-        if (c.family == F_TILED) {
+        // pad_k: the planned kernels cover the aligned part of K (pr.K) and write
+        // partials; a tail kernel adds the last k_pad elements as one more slice.
+        const int s_main = c.split_k;   // 0 when pad_k leaves no aligned part
+        const int s_all = s_main + (c.k_pad ? 1 : 0);
+        const int s_arg = c.k_pad ? s_all : c.split_k;   // > 1: the kernels write partials
+        if (s_main == 0) {
+            // nothing but the tail: the aligned part of K is empty
+        } else if (c.family == F_TILED) {
             TiledArgs ta{};
             ta.A = A;
             ta.B = B;
@@ -470,8 +504,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             ta.ld_scale = K / 32;
             ta.M = (int)M;
             ta.N = (int)N;
-            ta.K = (int)K;
-            ta.split_k = c.split_k;
+            ta.K = (int)pr.K;
+            ta.split_k = s_arg;
             ta.k_slice = c.k_slice;
             ta.tiles_m = (int)((M + c.m_tile - 1) / c.m_tile);
             ta.tiles_n = (int)((N + c.n_tile - 1) / c.n_tile);
@@ -491,8 +525,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             sa.ld_scale = K / 32;
             sa.M = (int)M;
             sa.N = (int)N;
-            sa.K = (int)K;
-            sa.split_k = c.split_k;
+            sa.K = (int)pr.K;
+            sa.split_k = s_arg;
             sa.k_slice = c.k_slice;
             sa.ws = workspace;
             sa.epi = ea;
@@ -501,10 +535,26 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             else he = launch_skinny_e2m1(c.kernel_id, sa, c.grid_x, c.grid_y, st);
         }
         if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
-        if (c.split_k > 1) {
+        if (c.k_pad) {
+            TailArgs tl{};
+            tl.A = A;
+            tl.B = B;
+            tl.lda = lda;
+            tl.ldb = ldb;
+            tl.M = (int)M;
+            tl.N = (int)N;
+            tl.k0 = (int)pr.K;
+            tl.k1 = (int)K;
+            tl.path = pr.path;
+            tl.b_kmajor = pr.b_kmajor;
+            tl.ws = static_cast<char *>(workspace) + (int64_t)s_main * M * N * 4;
+            he = launch_tail(tl, st);
+            if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("tail launch: ") + hipGetErrorString(he));
+        }
+        if (s_all > 1 || c.k_pad) {
             ReduceArgs ra{};
             ra.ws = workspace;
-            ra.split_k = c.split_k;
+            ra.split_k = s_all;
             ra.M = (int)M;
             ra.N = (int)N;
             ra.is_int = pr.path == P_I8;
@@ -513,8 +563,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             {
                 const int64_t groups = std::max<int64_t>(1, M * N / 4);
                 int runs = 1;
-                while (runs < 16 && runs * 2 <= c.split_k && groups * runs < 65536) runs *= 2;
-                ra.lanes = c.split_k <= 8 ? 1 : runs;
+                while (runs < 16 && runs * 2 <= s_all && groups * runs < 65536) runs *= 2;
+                ra.lanes = s_all <= 8 ? 1 : runs;
             }
             ra.epi = ea;
             he = launch_reduce(ra, st);

@@ -57,6 +57,17 @@ struct SkinnyArgs {
     EpiArgs epi;
 };
 
+// pad_k tail: ws[m][n] = sum over k in [k0, k1) of A[m][k] * B[k][n], one more
+// partial slice (fp32, or int32 for int8) for the split-K reduction.
+struct TailArgs {
+    const void *A, *B;
+    int64_t lda, ldb;
+    int M, N, k0, k1;
+    int path;                     // P_F16, P_BF16 or P_I8
+    int b_kmajor;                 // 1: B stored N x K
+    void *ws;                     // the slice [M][N]
+};
+
 // Split-K reduction: out = epilogue(sum of ws[s] over the slices s).  `lanes`
 // lanes share one output (a power of two, at most 16): lane t sums a contiguous
 // run of slices in ascending order and the runs are combined in a fixed pattern.

@@ -25,6 +25,9 @@ hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int grid_x, int grid_
 // Split-K reduction and epilogue.
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
+// pad_k: the K tail past the aligned part, as one more partial slice.
+hipError_t launch_tail(const TailArgs &a, hipStream_t s);
+
 // Hardware probe kernels (dg_probe): kind 0 stream read, 1 MFMA, 2 LDS banks.
 hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s);
 

@@ -519,7 +519,7 @@ void fill_info(const Candidate &c, dg_plan_info *o)
     o->mfma_m = c.mfma_m; o->mfma_n = c.mfma_n; o->mfma_k = c.mfma_k;
     o->m_tile = c.m_tile; o->n_tile = c.n_tile;
     o->k_main = c.k_main; o->n_main = c.n_main; o->k_tail = c.k_tail; o->n_tail = c.n_tail;
-    o->split_k = c.split_k; o->k_slice = c.k_slice;
+    o->split_k = c.split_k + (c.k_pad ? 1 : 0); o->k_slice = c.k_slice;
     o->waves_per_wg = c.waves;
     o->lds_bytes = c.lds; o->vgpr_est = c.vgpr; o->agpr_est = c.agpr;
     o->waves_per_simd = c.waves_per_simd;

@@ -20,6 +20,7 @@ struct Problem {
     int out_type;    // Elt
     int epi;         // EpiKind
     int beta_nz;     // D is read
+    int64_t k_pad = 0;   // pad_k: K elements past K (K is then the aligned part)
 };
 
 struct Candidate {
@@ -35,6 +36,7 @@ struct Candidate {
     int64_t ws_bytes;
     double est_us, roof_us;
     std::string name;
+    int k_pad = 0;   // pad_k: K elements added as one more partial slice by the tail kernel
 };
 
 struct PlanResult {

@@ -566,6 +566,44 @@ __global__ void __launch_bounds__(256) reduce_runs_kernel(ReduceArgs a)
     }
 }
 
+// pad_k tail: one thread per output, at most 31 products each (K past the
+// MFMA-aligned part), summed in ascending k.  A handful of products per output:
+// plain loads, coalesced along N for a row-major B.
+__global__ void __launch_bounds__(256) tail_kernel(TailArgs a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.M * a.N) return;
+    const int m = (int)(idx / a.N), n = (int)(idx - (int64_t)m * a.N);
+    if (a.path == P_I8) {
+        const int8_t *A = reinterpret_cast<const int8_t *>(a.A) + (int64_t)m * a.lda;
+        const int8_t *B = reinterpret_cast<const int8_t *>(a.B);
+        uint32_t acc = 0;
+        for (int k = a.k0; k < a.k1; ++k) {
+            const int8_t b = a.b_kmajor ? B[(int64_t)n * a.ldb + k] : B[(int64_t)k * a.ldb + n];
+            acc += (uint32_t)((int32_t)A[k] * (int32_t)b);
+        }
+        reinterpret_cast<int32_t *>(a.ws)[idx] = (int32_t)acc;
+    } else {
+        const unsigned short *A = reinterpret_cast<const unsigned short *>(a.A) + (int64_t)m * a.lda;
+        const unsigned short *B = reinterpret_cast<const unsigned short *>(a.B);
+        float acc = 0.f;
+        for (int k = a.k0; k < a.k1; ++k) {
+            const unsigned short b = a.b_kmajor ? B[(int64_t)n * a.ldb + k] : B[(int64_t)k * a.ldb + n];
+            acc += elt16(a.path, A[k]) * elt16(a.path, b);
+        }
+        reinterpret_cast<float *>(a.ws)[idx] = acc;
+    }
+}
+
+hipError_t launch_tail(const TailArgs &a, hipStream_t s)
+{
+    const int64_t grid = ((int64_t)a.M * a.N + 255) / 256;
+    if (grid > 0x7fffffff || a.k1 - a.k0 > 31 || a.k0 < 0) return hipErrorInvalidValue;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(tail_kernel, dim3((unsigned)grid, 1, 1), dim3(256, 1, 1), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
     if (a.lanes < 1 || a.lanes > 64 || (a.lanes & (a.lanes - 1))) return hipErrorInvalidValue;
