@@ -271,7 +271,8 @@ def stage_breakdown(h, p, launches=5):
         h.set_stage_clock(None)
     s = dg.stage_cycles(buf.cpu().numpy(), grid)
     tot = s["prologue"]["median"] + s["k_loop"]["median"] + s["epilogue"]["median"]
-    s["k_loop_frac"] = round(s["k_loop"]["median"] / max(1, tot), 4)
+    s["frac"] = {k: round(s[k]["median"] / max(1, tot), 4) for k in ("prologue", "k_loop", "epilogue")}
+    s.pop("span")   # the counters of different dies do not compare
     s["unit"] = "s_memtime ticks per workgroup"
     return s
 
@@ -320,11 +321,6 @@ def main():
                 "unit": "TOP/s", "frac": round(achieved / PEAK["i8"], 4),
                 "traffic": recorded_traffic(HEADLINE), "launch_ms": round(ms_launch, 6)}
     stages = stage_breakdown(h, p)
-    # the stage clock's tick rate in this kernel (its span over the launch
-    # duration), and the per-workgroup stages converted to microseconds with it
-    tick = stages["span"] / (ms_launch * 1e-3)
-    stages["tick_ghz"] = round(tick / 1e9, 3)
-    stages["us"] = {k: round(stages[k]["median"] / tick * 1e6, 2) for k in ("prologue", "k_loop", "epilogue")}
     del p
     torch.cuda.empty_cache()
 
