@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, loudly, where no GPU is visible; the driver selects
-    # them with -m gpu on the GPU machine, where they must run.
+    # GPU tests are skipped, loudly, where no GPU is visible; on a machine with
+    # an MI355X they are selected with -m gpu and must run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
