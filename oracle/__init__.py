@@ -40,7 +40,12 @@ def _load():
     lib.orc_gemm_int.restype = i64
     lib.orc_requant.argtypes = [i64, i64, p, C.c_float, p, i32, p]
     lib.orc_requant.restype = i32
-    for name in ("orc_f16_values", "orc_bf16_values", "orc_e2m1_values",
+    lib.orc_gemm_mx.argtypes = [i64, i64, i64, p, p, p, p, d, i32, p, i32, p, i32]
+    lib.orc_gemm_mx.restype = i32
+    lib.orc_quant_mx_e4m3.argtypes = [i64, i64, p, p, p]
+    lib.orc_quant_mx_e4m3.restype = i32
+    for name in ("orc_f16_values", "orc_bf16_values", "orc_e2m1_values", "orc_fp8e4m3_values",
+                 "orc_e8m0_values", "orc_fp8e4m3_rne_sat_array",
                  "orc_f16_rne_array", "orc_bf16_rne_array", "orc_gelu_erf_array"):
         getattr(lib, name).argtypes = [i64, p, p]
         getattr(lib, name).restype = None
@@ -88,6 +93,27 @@ def e2m1_values(codes) -> np.ndarray:
     c = _c(codes, "e2m1")
     out = np.empty(c.shape, np.float64)
     _load().orc_e2m1_values(c.size, _ptr(c), _ptr(out))
+    return out
+
+
+def fp8e4m3_values(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_fp8e4m3_values(c.size, _ptr(c), _ptr(out))
+    return out
+
+
+def e8m0_values(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e8m0_values(c.size, _ptr(c), _ptr(out))
+    return out
+
+
+def fp8e4m3_rne_sat(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_fp8e4m3_rne_sat_array(x.size, _ptr(x), _ptr(out))
     return out
 
 
@@ -179,6 +205,42 @@ def gemm_int(A, B, *, alpha=1, beta=0, D=None, nthreads=0):
     if ov < 0:
         raise ValueError("oracle rejected the arguments")
     return R, Cw, int(ov)
+
+
+def gemm_mx(A, SA, B, SB, *, alpha=1.0, bias=None, bias_kind="f16", act=0, nthreads=0):
+    """MX block-scaled GEMM in binary64, unrounded.
+
+    A: fp8 e4m3 codes M x K; SA: e8m0 codes [M][K/32]; B: e2m1 codes, logical
+    [K][N], one per byte; SB: e8m0 codes [K/32][N]; bias: [N] of ``bias_kind``;
+    act: 0 identity, 1 GELU (erf form).
+    """
+    A = np.ascontiguousarray(A, np.uint8)
+    SA = np.ascontiguousarray(SA, np.uint8)
+    B = np.ascontiguousarray(B, np.uint8)
+    SB = np.ascontiguousarray(SB, np.uint8)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or SA.shape != (M, K // 32) or SB.shape != (K // 32, N):
+        raise ValueError("operand shapes disagree")
+    bc = _c(bias, bias_kind) if bias is not None else None
+    R = np.empty((M, N), np.float64)
+    rc = _load().orc_gemm_mx(M, N, K, _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), float(alpha),
+                             KIND[bias_kind], _ptr(bc), int(act), _ptr(R), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return R
+
+
+def quant_mx(X):
+    """binary16 bits M x K -> (fp8 e4m3 codes M x K, e8m0 scale codes [M][K/32])."""
+    X = _c(X, "f16")
+    M, K = X.shape
+    codes = np.empty((M, K), np.uint8)
+    scales = np.empty((M, K // 32), np.uint8)
+    rc = _load().orc_quant_mx_e4m3(M, K, _ptr(X), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return codes, scales
 
 
 def requant(acc, *, alpha, bias=None, out="i8"):

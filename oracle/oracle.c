@@ -26,7 +26,14 @@
  *   - integer accumulation into 32 bits and round-to-nearest conversion of the
  *     integer result: [overview] section 4.3 (INT32 output, cvt.rn.f16.s32);
  *   - the 4-bit e2m1 code (sign, 2-bit exponent, 1-bit mantissa): [overview]
- *     section 2.2, second layer.
+ *     section 2.2, second layer;
+ *   - the block-scaled variant of that 4-bit scheme (fp8 e4m3 activations and
+ *     e2m1 weights, one power-of-two e8m0 scale per 32 values along K): the
+ *     pages' precision scheme ([overview] section 2.2, second layer, and the
+ *     e2m1 weight unpack of [overview] section 4.3) run on the OCP Microscaling
+ *     (MX) v1.0 element and scale formats.  The formats are that published
+ *     specification's, not the pages'; the block size 32 and the fp8
+ *     activation are this oracle's reading.
  *
  * Floating-point results are summed in binary64 with k ascending and returned
  * unrounded; the comparison rule lives in the tests.  Integer results are exact
@@ -88,6 +95,34 @@ double orc_e2m1_value(uint8_t code)
     int M = code & 1;
     double v = (E == 0) ? 0.5 * M : ldexp(1.0 + 0.5 * M, E - 1);
     return s ? -v : v;
+}
+
+/*
+ * fp8 e4m3 (OCP MX "E4M3"): bit 7 sign, bits 6..3 exponent E (bias 7), bits 2..0
+ * mantissa M.  E = 0 is the subnormal range: value = M/8 * 2^-6.  Otherwise
+ * value = (1 + M/8) * 2^(E-7), except E = 15 with M = 7, which is NaN.  There
+ * are no infinities; the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+double orc_fp8e4m3_value(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int E = (code >> 3) & 15;
+    int M = code & 7;
+    double v;
+    if (E == 15 && M == 7)
+        v = NAN;
+    else if (E == 0)
+        v = ldexp((double)M, -9);                  /* M/8 * 2^-6 */
+    else
+        v = ldexp(8.0 + (double)M, E - 10);        /* (1 + M/8) * 2^(E-7) */
+    return s ? -v : v;
+}
+
+/* e8m0 block scale (OCP MX): an 8-bit biased exponent, value 2^(code - 127);
+ * code 255 is NaN.  No sign, no mantissa. */
+double orc_e8m0_value(uint8_t code)
+{
+    return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
 }
 
 /*
@@ -250,6 +285,140 @@ int orc_gemm_real(int64_t M, int64_t N, int64_t K,
     return 0;
 }
 
+/* ------------------------------------------------------ MX block-scaled GEMM */
+
+/*
+ * r = act(alpha * sum_k a[i][k] * w[k][j] + bias[j]), all in binary64, with
+ *   a[i][k] = fp8e4m3(A[i][k]) * e8m0(SA[i][k/32])
+ *   w[k][j] = e2m1(B[k][j])    * e8m0(SB[k/32][j])
+ *
+ *   A   fp8 e4m3 codes, logical M x K row-major
+ *   SA  e8m0 codes, [M][K/32]
+ *   B   e2m1 codes, logical K x N row-major, one code per byte (low 4 bits)
+ *   SB  e8m0 codes, [K/32][N]
+ *   bias [N] of bias_kind (nullable); act 0 identity, 1 GELU (erf form)
+ *   R   out, M x N binary64, unrounded
+ *
+ * Every a and w is exact in binary64 (4- and 2-bit significands times powers of
+ * two within binary64's range), and so is every product.  Sums run with k
+ * ascending.  Returns 0, or -1 on a bad argument (K not a multiple of 32).
+ */
+int orc_gemm_mx(int64_t M, int64_t N, int64_t K,
+                const uint8_t *A, const uint8_t *SA,
+                const uint8_t *B, const uint8_t *SB,
+                double alpha, int bias_kind, const void *bias,
+                int act, double *R, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 || !R) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (K > 0 && (!A || !SA || !B || !SB)) return -1;
+    const int64_t G = K / 32;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+    double *a = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)M);
+    if (!w || !a) {
+        free(w);
+        free(a);
+        return -1;
+    }
+    int nt = set_threads(nthreads);
+    #pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            w[k * N + n] = orc_e2m1_value(B[k * N + n] & 0xf) * orc_e8m0_value(SB[(k / 32) * N + n]);
+    #pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = orc_fp8e4m3_value(A[i * K + k]) * orc_e8m0_value(SA[i * G + k / 32]);
+
+    #pragma omp parallel num_threads(nt)
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            for (int64_t n = 0; n < N; ++n) acc[n] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double ak = a[i * K + k];
+                const double *wk = w + k * N;
+                for (int64_t n = 0; n < N; ++n) acc[n] += ak * wk[n];
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double v = alpha * acc[n];
+                if (bias) v += load_real(bias_kind, bias, n);
+                if (act == 1) v = orc_gelu_erf(v);
+                R[i * N + n] = v;
+            }
+        }
+        free(acc);
+    }
+    free(w);
+    free(a);
+    return 0;
+}
+
+/*
+ * binary64 -> fp8 e4m3 code, round to nearest even, saturating: magnitudes that
+ * round past 448 give +-448 (the MX conversion clamps to the largest normal
+ * rather than producing NaN).  NaN input gives code 0x7f.
+ */
+uint8_t orc_fp8e4m3_rne_sat(double x)
+{
+    if (isnan(x)) return 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double ulp;
+    double q = fabs(round_to_format(fabs(x), 4, -6, INFINITY, &ulp));
+    if (q > 448.0) q = 448.0;
+    if (q == 0.0) return sign;
+    if (q < ldexp(1.0, -6))                        /* subnormal: q = M * 2^-9 */
+        return sign | (uint8_t)ldexp(q, 9);
+    int e;
+    double m = frexp(q, &e);                       /* q = m * 2^e, m in [0.5,1) */
+    int E = e - 1 + 7;
+    uint8_t M = (uint8_t)((m * 2.0 - 1.0) * 8.0);
+    return sign | (uint8_t)(E << 3) | M;
+}
+
+/*
+ * Quantise binary16 activations to MX fp8 e4m3 with one e8m0 scale per 32
+ * consecutive values of a row (the OCP MX v1.0 conversion):
+ *   amax  = max |x| over the block
+ *   e     = floor(log2(amax)) - 8          (8 = exponent of e4m3's largest normal)
+ *   scale = 2^e, stored as code e + 127 (clamped to 0..254); amax = 0 gives code 0
+ *   code  = fp8e4m3_rne_sat(x / scale)
+ *   X   binary16 bits, M x K row-major;  codes M x K;  scales [M][K/32]
+ * x / scale is exact (a power of two within range), so the only rounding is the
+ * conversion to e4m3.  Returns 0, or -1 on a bad argument or a non-finite input.
+ */
+int orc_quant_mx_e4m3(int64_t M, int64_t K, const uint16_t *X, uint8_t *codes, uint8_t *scales)
+{
+    if (M < 0 || K < 0 || K % 32) return -1;
+    if (M * K > 0 && (!X || !codes || !scales)) return -1;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t g = 0; g < K / 32; ++g) {
+            const uint16_t *xb = X + i * K + g * 32;
+            double amax = 0.0;
+            for (int t = 0; t < 32; ++t) {
+                double v = orc_f16_value(xb[t]);
+                if (!isfinite(v)) return -1;
+                if (fabs(v) > amax) amax = fabs(v);
+            }
+            int sc;
+            if (amax == 0.0) {
+                sc = 0;
+            } else {
+                int e2;
+                frexp(amax, &e2);                  /* amax in [2^(e2-1), 2^e2) */
+                sc = (e2 - 1) - 8 + 127;
+                if (sc < 0) sc = 0;
+                if (sc > 254) sc = 254;
+            }
+            scales[i * (K / 32) + g] = (uint8_t)sc;
+            for (int t = 0; t < 32; ++t)
+                codes[i * K + g * 32 + t] =
+                    orc_fp8e4m3_rne_sat(orc_f16_value(xb[t]) / orc_e8m0_value((uint8_t)sc));
+        }
+    return 0;
+}
+
 /* -------------------------------------------------------------- integer GEMM */
 
 /*
@@ -345,6 +514,21 @@ void orc_bf16_values(int64_t n, const uint16_t *h, double *out)
 void orc_e2m1_values(int64_t n, const uint8_t *c, double *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_value(c[i] & 0xf);
+}
+
+void orc_fp8e4m3_values(int64_t n, const uint8_t *c, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8e4m3_value(c[i]);
+}
+
+void orc_e8m0_values(int64_t n, const uint8_t *c, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e8m0_value(c[i]);
+}
+
+void orc_fp8e4m3_rne_sat_array(int64_t n, const double *x, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8e4m3_rne_sat(x[i]);
 }
 
 void orc_f16_rne_array(int64_t n, const double *x, uint16_t *out)

@@ -436,3 +436,146 @@ def test_generator_distributions():
     c = synth.e2m1_codes(4, 160000)
     counts = torch.bincount(c.to(torch.int64), minlength=16)
     assert counts.numel() == 16 and int(counts.min()) > 9000
+
+
+# ------------------------------------------------------- MX block-scaled path
+def _fp8_torch(codes):
+    """fp8 e4m3 values decoded by torch's float8_e4m3fn (an independent decoder)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def test_fp8e4m3_decode_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8e4m3_values(codes)
+    ref = _fp8_torch(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), codes[~nan] >= 128)
+    # the format's landmarks: 1.0, largest normal, smallest normal and subnormal
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6
+    assert got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+
+
+def test_e8m0_decode_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e8m0_values(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_fp8_rne_sat_vs_torch_and_ties():
+    z = synth.normal(71, 20000).numpy() * np.exp2(synth.int_range(72, 20000, -12, 8).numpy())
+    z = z.astype(np.float32).astype(np.float64)          # torch converts from binary32
+    inr = np.abs(z) <= 448
+    got = oracle.fp8e4m3_rne_sat(z)
+    ref = torch.from_numpy(z[inr].astype(np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    assert np.array_equal(got[inr], ref)
+    assert np.all(got[(~inr) & (z > 0)] == 0x7E) and np.all(got[(~inr) & (z < 0)] == 0xFE)
+    # ties go to the even mantissa; past the largest normal the result saturates
+    cases = [(1 + 1 / 16, 0x38), (1 + 3 / 16, 0x3A), (-(1 + 1 / 16), 0xB8), (2.0 ** -10, 0x00),
+             (3 * 2.0 ** -10, 0x02), (464.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE), (0.0, 0x00),
+             (-0.0, 0x80)]
+    for x, c in cases:
+        assert int(oracle.fp8e4m3_rne_sat(np.array([x]))[0]) == c, x
+
+
+def _mx_inputs(M, N, K, seed=601):
+    w = synth.make("mx_4096x4096x4096", M=M, N=N, K=K, seed=seed)
+    t = w.tensors
+    return t["A"].numpy(), t["SA"].numpy(), t["codes"].numpy(), t["SB"].numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (3, 5, 96), (4, 2, 128)])
+def test_mx_gemm_exact(M, N, K):
+    A, SA, Bc, SB = _mx_inputs(M, N, K)
+    R = oracle.gemm_mx(A, SA, Bc, SB)
+    av = _fp8_torch(A)
+    gold = e2m1_golden()
+    for i in range(M):
+        for j in range(N):
+            terms = [Fraction(av[i, k]) * Fraction(2) ** (int(SA[i, k // 32]) - 127) *
+                     Fraction(gold[int(Bc[k, j])]) * Fraction(2) ** (int(SB[k // 32, j]) - 127)
+                     for k in range(K)]
+            exact = sum(terms, Fraction(0))
+            mag = sum(abs(t) for t in terms)
+            assert abs(Fraction(R[i, j]) - exact) <= (K + 1) * Fraction(1, 2 ** 53) * mag
+
+
+def test_mx_scale_block_index():
+    # one non-zero product per block: the result picks exactly that block's two scales
+    K, M, N = 96, 2, 3
+    A = np.zeros((M, K), np.uint8)
+    Bc = np.zeros((K, N), np.uint8)
+    SA = np.array([[127 + g + 3 * i for g in range(K // 32)] for i in range(M)], np.uint8)
+    SB = np.array([[120 - g - 4 * j for j in range(N)] for g in range(K // 32)], np.uint8)
+    A[1, 70] = 0x40            # 2.0, in block 2
+    Bc[70, 2] = 7              # 6.0
+    R = oracle.gemm_mx(A, SA, Bc, SB)
+    assert R[1, 2] == 12.0 * 2.0 ** ((127 + 2 + 3) - 127) * 2.0 ** ((120 - 2 - 8) - 127)
+    assert np.count_nonzero(R) == 1
+
+
+def test_mx_unit_scales_reduce_to_the_e2m1_gemm():
+    # with every scale code 127 (2^0) the MX product is the e2m1 GEMM over fp16
+    # activations holding the same values (fp8 e4m3 values are exact in fp16)
+    A, SA, Bc, SB = _mx_inputs(5, 7, 96, seed=9)
+    SA[:] = 127
+    SB[:] = 127
+    a16 = torch.from_numpy(_fp8_torch(A)).to(torch.float16).view(torch.int16).numpy() \
+        .view(np.uint16)
+    bias = bits16(synth.to_storage(synth.uniform(5, 7, -1, 1), torch.float16))
+    R = oracle.gemm_mx(A, SA, Bc, SB, alpha=0.5, bias=bias, act=1)
+    ones = np.full((3, 7), 0x3C00, np.uint16)
+    ref = oracle.gemm_real(a16, Bc, a_kind="f16", b_kind="e2m1", scale=ones, group_k=32,
+                           alpha=0.5, bias=bias, act=1)
+    assert np.array_equal(R, ref)
+
+
+def test_mx_quantiser_definition():
+    w = synth.make("mxq_4096x4096", M=16, K=256)
+    X = bits16(w.tensors["X"])
+    X[3, 32:64] = 0                      # an all-zero block
+    codes, scales = oracle.quant_mx(X)
+    xv = oracle.f16_values(X)
+    assert codes.shape == X.shape and scales.shape == (16, 8)
+    assert scales[3, 1] == 0 and np.all(codes[3, 32:64] == 0)
+    for i in range(16):
+        for g in range(8):
+            blk = xv[i, 32 * g:32 * g + 32]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            s = 2.0 ** (int(scales[i, g]) - 127)
+            # the block maximum lands in the top binade of e4m3, [2^8, 2^9)
+            assert 256 <= amax / s < 512
+            q = blk / s
+            ref = torch.from_numpy(np.clip(q, -448, 448).astype(np.float32)) \
+                .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            big = np.abs(q) > 448
+            ref[big] = np.where(q[big] > 0, 0x7E, 0xFE)
+            assert np.array_equal(codes[i, 32 * g:32 * g + 32], ref), (i, g)
+    # values already on the grid come back unchanged: fp8 values times one power
+    # of two, with the block maximum 448 * 2^-5
+    v = _fp8_torch(synth.fp8_codes(73, 32).numpy())
+    v = np.where(np.abs(v) > 448, 0, v) * 2.0 ** -5
+    v[0] = 448 * 2.0 ** -5
+    vb = oracle.f16_rne(v).reshape(1, 32)
+    c2, s2 = oracle.quant_mx(vb)
+    assert int(s2[0, 0]) == 127 - 5
+    assert np.array_equal(_fp8_torch(c2[0]) * 2.0 ** -5, oracle.f16_values(vb)[0])
+
+
+def test_mx_generators():
+    c = synth.fp8_codes(5, 254 * 400)
+    counts = torch.bincount(c.to(torch.int64), minlength=256)
+    assert int(counts[0x7F]) == 0 and int(counts[0xFF]) == 0
+    others = torch.cat([counts[:0x7F], counts[0x80:0xFF]])
+    assert others.numel() == 254 and int(others.min()) > 300
+    r = synth.int_range(6, 70000, 112, 118)
+    assert int(r.min()) == 112 and int(r.max()) == 118
+    assert int(torch.bincount(r.to(torch.int64) - 112).min()) > 9000

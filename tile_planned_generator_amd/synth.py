@@ -102,6 +102,21 @@ def e2m1_codes(seed, n, device="cpu") -> torch.Tensor:
                     torch.uint8, device)
 
 
+def int_range(seed, n, lo, hi, device="cpu") -> torch.Tensor:
+    """Integers uniform over [lo, hi] (the high 32 bits of each draw, modulo the
+    range; the bias of the modulus is below 2^-24 for the small ranges used)."""
+    span = hi - lo + 1
+    return _chunked(n, lambda s, m: (_srl(splitmix64(seed, m, device, s), 32) % span + lo)
+                    .to(torch.int32), torch.int32, device)
+
+
+def fp8_codes(seed, n, device="cpu") -> torch.Tensor:
+    """8-bit codes uniform over the 254 codes whose low seven bits are not all ones
+    (in fp8 e4m3 those two codes are NaN), one per uint8."""
+    return _chunked(n, lambda s, m: (lambda u: (u + (u >= 127).to(torch.int64)).to(torch.uint8))(
+        _srl(splitmix64(seed, m, device, s), 32) % 254), torch.uint8, device)
+
+
 def to_storage(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
     """binary64 -> binary32 -> 16-bit storage type (each step nearest-even)."""
     return x.to(torch.float32).to(dtype)
@@ -136,6 +151,8 @@ WORKLOADS = {
     "e2m1_1x4096x4096": ("e2m1", 1, 4096, 4096, 501, 1.0, 0.0, "none", "f16"),
     "e2m1_4096x4096x4096": ("e2m1", 4096, 4096, 4096, 502, 1.0, 0.0, "none", "f16"),
     "f16_4096x4096x4096": ("f16", 4096, 4096, 4096, 901, 1.0, 0.0, "none", "f16"),
+    "mx_4096x4096x4096": ("mx", 4096, 4096, 4096, 601, 1.0, 0.0, "none", "f16"),
+    "mxq_4096x4096": ("mxq", 4096, 0, 4096, 602, 1.0, 0.0, "none", "u8"),
 }
 
 
@@ -173,6 +190,21 @@ def make(name: str, device="cpu", M=None, N=None, K=None, seed=None) -> Workload
         t["codes"] = e2m1_codes(_sid(seed, TID_B), K * N, device).view(K, N)
         t["scale"] = to_storage(uniform(_sid(seed, TID_SCALE), G * N, 0.01, 0.1, device),
                                 torch.float16).view(G, N)
+    elif path == "mx":
+        # fp8 e4m3 activation codes with e8m0 scales 2^-15..2^-9 per 32 values of a
+        # row, e2m1 weight codes with e8m0 scales 2^-8..2^-4 per 32 values of a
+        # column: products stay near 1e-2 and the K sums well inside fp16's range.
+        G = K // 32
+        t["A"] = fp8_codes(_sid(seed, TID_A), M * K, device).view(M, K)
+        t["SA"] = int_range(_sid(seed, TID_D), M * G, 112, 118, device).to(torch.uint8).view(M, G)
+        t["codes"] = e2m1_codes(_sid(seed, TID_B), K * N, device).view(K, N)
+        t["SB"] = int_range(_sid(seed, TID_SCALE), G * N, 119, 123, device).to(torch.uint8).view(G, N)
+    elif path == "mxq":
+        # fp16 activations for the MX quantiser: normal values times a per-row
+        # magnitude 2^u, u uniform in [-6, 6], so blocks take many scale codes
+        z = normal(_sid(seed, TID_A), M * K, device).view(M, K)
+        u = int_range(_sid(seed, TID_SCALE), M, -6, 6, device).to(torch.float64)
+        t["X"] = to_storage(z * torch.pow(2.0, u).view(M, 1), torch.float16)
     else:
         raise KeyError(name)
     return w
