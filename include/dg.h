@@ -68,7 +68,11 @@ typedef enum {
     DG_ERR_INTERNAL = 9
 } dg_status;
 
-typedef enum { DG_F16 = 0, DG_BF16 = 1, DG_F32 = 2, DG_I8 = 3, DG_I32 = 4, DG_E2M1 = 5 } dg_dtype;
+/* DG_F8E4M3: OCP MX fp8 e4m3 (sign, 4-bit exponent with bias 7, 3-bit mantissa;
+ * largest finite 448, codes 0x7f and 0xff NaN).  DG_E8M0: OCP MX block scale, an
+ * unsigned byte c meaning 2^(c - 127) (255 is NaN). */
+typedef enum { DG_F16 = 0, DG_BF16 = 1, DG_F32 = 2, DG_I8 = 3, DG_I32 = 4, DG_E2M1 = 5,
+               DG_F8E4M3 = 6, DG_E8M0 = 7 } dg_dtype;
 
 /* DG_ROW_MAJOR: for A, M x K with K contiguous; for B, K x N with N contiguous.
  * DG_COL_MAJOR: for B only, stored N x K with K contiguous (the e2m1 layout). */
@@ -93,6 +97,9 @@ typedef enum { DG_PATH_AUTO = 0, DG_PATH_TILED = 1, DG_PATH_SKINNY = 2 } dg_path
  *   a=BF16 b=BF16 c=BF16|F32 compute=F32
  *   a=I8   b=I8   c=I32      compute=I32   (c=I8 / F16 with the requantise epilogues)
  *   a=F16  b=E2M1 c=F16|F32  compute=F32   (b_scale: one fp16 per group_k codes)
+ *   a=F8E4M3 b=E2M1 c=F16|F32 compute=F32  (the MX path: e8m0 scales on both
+ *                                           operands, dg_gemm_mx only; dg_plan
+ *                                           plans it with group_k 32)
  * D, when read, has the type of C (I32 for the int path). */
 typedef struct {
     int32_t a, b, c, compute; /* dg_dtype */
@@ -246,6 +253,58 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
                   const void *D, void *C, const void *alpha, const void *beta,
                   const dg_epilogue *epi, const dg_plan_opts *opts,
                   void *workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/* MX block-scaled GEMM: the 4-bit weight scheme of the pages (e2m1 weights with
+ * a scale per group of 32 along K, [overview] section 2.2, second layer; the
+ * in-register weight unpack of section 4.3) with the activations quantised to
+ * fp8 as well, so both operands go to gfx950's block-scaled MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4) without a decode step.  The element and
+ * scale formats are those of the OCP Microscaling (MX) v1.0 specification:
+ *   C[i][j] = act( alpha * sum_k a[i][k] * w[k][j] + bias[j] )
+ *   a[i][k] = e4m3(A[i][k]) * 2^(a_scale[i][k/32] - 127)
+ *   w[k][j] = e2m1(B[j][k]) * 2^(b_scale[j][k/32] - 127)
+ * accumulated in fp32 (products and block sums inside the MFMA, then fp32
+ * additions along K), rounded once to C's type.
+ *   A          device, fp8 e4m3 codes, M x K row-major, lda bytes (0: K); 16-byte
+ *              aligned, lda a multiple of 16
+ *   a_scale    device, e8m0 codes [M][K/32], lda_scale bytes per row (0: K/32
+ *              rounded up to a multiple of 4); 4-byte aligned, lda_scale a
+ *              multiple of 4
+ *   B          device, e2m1 codes N x K (K contiguous), two per byte with even k
+ *              in the low nibble, ldb in codes (0: K, a multiple of 32); 16-byte
+ *              aligned
+ *   b_scale    device, e8m0 codes [N][K/32], ldb_scale bytes (as lda_scale)
+ *   C          device, M x N row-major, ldc elements (0: N), c_type F16 or F32
+ *   alpha      the product's multiplier
+ *   epi        NULL or DG_EPI_NONE / BIAS / GELU_ERF / BIAS_GELU_ERF (bias F16,
+ *              BF16 or F32); no beta * D term
+ *   opts, workspace, workspace_bytes, stream   as for dg_gemm
+ * K must be a multiple of 64 (DG_ERR_ALIGNMENT; pad_k is DG_ERR_UNSUPPORTED).
+ * Returns after enqueueing; errors are reported before anything is enqueued:
+ * DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_ALIGNMENT,
+ * DG_ERR_NO_CANDIDATE, DG_ERR_WORKSPACE, DG_ERR_HIP. */
+dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, const void *a_scale, int64_t lda_scale,
+                     const void *B, int64_t ldb, const void *b_scale, int64_t ldb_scale,
+                     void *C, int32_t c_type, int64_t ldc, float alpha,
+                     const dg_epilogue *epi, const dg_plan_opts *opts,
+                     void *workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/* MX quantiser for the activation operand of dg_gemm_mx: binary16 X -> fp8 e4m3
+ * codes and one e8m0 scale per 32 consecutive values of a row (the OCP MX v1.0
+ * conversion).  Per block: amax = max |x|; e = floor(log2 amax) - 8 (8 is the
+ * exponent of e4m3's largest normal); scale code e + 127 (0 when amax is 0);
+ * code = e4m3(x * 2^-e), nearest even, magnitudes above 448 saturating to 448.
+ * A block holding an infinity or a NaN gets scale code 255 and codes 0x7f.
+ *   X        device binary16, M x K row-major, ldx elements (0: K); 16-byte
+ *            aligned rows
+ *   codes    device, M x K bytes, ldq bytes per row (0: K); 16-byte aligned rows
+ *   scales   device, [M][K/32] bytes, ld_scale bytes per row (0: K/32)
+ * K must be a multiple of 32 (DG_ERR_ALIGNMENT).  Enqueues one kernel on
+ * `stream`.  Errors: DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG,
+ * DG_ERR_UNSUPPORTED, DG_ERR_ALIGNMENT, DG_ERR_HIP. */
+dg_status dg_quant_mx(dg_handle_t h, int64_t M, int64_t K, const void *X, int64_t ldx,
+                      void *codes, int64_t ldq, void *scales, int64_t ld_scale, dg_stream_t stream);
 
 /* Stage clock: the analogue of the generator's profile option, which reads the
  * clock inside the generated kernel and reports the cycles of each kernel stage

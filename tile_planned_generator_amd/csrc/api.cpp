@@ -1,6 +1,7 @@
 // api.cpp - the C ABI (include/dg.h): validation, plan cache, dispatch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -77,10 +78,13 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
     else if (dt->a == DG_BF16 && dt->b == DG_BF16) path = P_BF16;
     else if (dt->a == DG_I8 && dt->b == DG_I8) path = P_I8;
     else if (dt->a == DG_F16 && dt->b == DG_E2M1) path = P_E2M1;
+    else if (dt->a == DG_F8E4M3 && dt->b == DG_E2M1) path = P_MX;
     else return fail(DG_ERR_UNSUPPORTED, "unsupported (a, b) dtype pair");
+    const bool fp4b = path == P_E2M1 || path == P_MX;
     const bool is_int = path == P_I8;
     if (dt->compute != (is_int ? DG_I32 : DG_F32))
-        return fail(DG_ERR_UNSUPPORTED, is_int ? "int8 inputs accumulate in I32" : "16-bit and e2m1 inputs accumulate in F32");
+        return fail(DG_ERR_UNSUPPORTED, is_int ? "int8 inputs accumulate in I32" : "16-bit, e2m1 and MX inputs accumulate in F32");
+    if (path == P_MX && beta_nz) return fail(DG_ERR_UNSUPPORTED, "the MX path has no beta * D term");
     if (epi_kind < DG_EPI_NONE || epi_kind > DG_EPI_REQUANT_F16)
         return fail(DG_ERR_INVALID_ARG, "unknown epilogue kind");
     const bool rq = epi_kind == DG_EPI_REQUANT_I8 || epi_kind == DG_EPI_REQUANT_F16;
@@ -99,10 +103,10 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
     // layouts
     dg_layouts L{};
     if (lay) L = *lay;
-    else L.b = path == P_E2M1 ? DG_COL_MAJOR : DG_ROW_MAJOR;
+    else L.b = fp4b ? DG_COL_MAJOR : DG_ROW_MAJOR;
     if (L.a != DG_ROW_MAJOR) return fail(DG_ERR_UNSUPPORTED, "A must be row-major");
     if (L.b != DG_ROW_MAJOR && L.b != DG_COL_MAJOR) return fail(DG_ERR_INVALID_ARG, "unknown B layout");
-    if (path == P_E2M1 && L.b != DG_COL_MAJOR)
+    if (fp4b && L.b != DG_COL_MAJOR)
         return fail(DG_ERR_UNSUPPORTED, "e2m1 B must be column-major (N x K, K contiguous)");
     const int64_t lda = L.lda ? L.lda : K;
     const int64_t ldb = L.ldb ? L.ldb : (L.b == DG_ROW_MAJOR ? N : K);
@@ -111,20 +115,21 @@ dg_status describe(int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const d
     if (lda < K || ldb < (L.b == DG_ROW_MAJOR ? N : K) || ldc < N || ldd < N)
         return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
     // alignment: K in whole MFMA steps, rows on 16-byte boundaries
-    const int ksub = (path == P_I8 || path == P_E2M1) ? 32 : 16;
+    const int ksub = path == P_MX ? 64 : ((path == P_I8 || path == P_E2M1) ? 32 : 16);
     int64_t k_pad = 0;
     if (K % ksub) {
         if (!pad_k)
             return fail(DG_ERR_ALIGNMENT, "K dimension not aligned to the MFMA depth (" + std::to_string(ksub) +
                                               "); set pad_k to add the tail separately");
         if (path == P_E2M1) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs K in whole 32-element groups");
+        if (path == P_MX) return fail(DG_ERR_UNSUPPORTED, "the MX path needs K in whole 64-element MFMA steps");
         k_pad = K % ksub;
     }
-    if (path == P_E2M1 && group_k != 32) return fail(DG_ERR_UNSUPPORTED, "e2m1 needs group_k == 32");
-    const int esz = path == P_I8 ? 1 : 2;
+    if (fp4b && group_k != 32) return fail(DG_ERR_UNSUPPORTED, "e2m1 and MX need group_k == 32");
+    const int esz = (path == P_I8 || path == P_MX) ? 1 : 2;
     if (K > 0) {   // with K == 0 neither A nor B is read
         if ((lda * esz) % 16) return fail(DG_ERR_ALIGNMENT, "lda is not a multiple of 16 bytes");
-        if (path == P_E2M1) {
+        if (fp4b) {
             if (ldb % 32) return fail(DG_ERR_ALIGNMENT, "ldb (codes) is not a multiple of 32");
         } else if ((ldb * esz) % 16) {
             return fail(DG_ERR_ALIGNMENT, "ldb is not a multiple of 16 bytes");
@@ -413,6 +418,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
         if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: planning only");
         if (!dt || !alpha || !beta) return fail(DG_ERR_INVALID_ARG, "dtypes, alpha and beta are required");
+        if (dt->a == DG_F8E4M3)
+            return fail(DG_ERR_UNSUPPORTED, "MX operands carry scales for A: call dg_gemm_mx");
         const bool is_int = dt->compute == DG_I32;
         const int32_t ia = is_int ? *reinterpret_cast<const int32_t *>(alpha) : 0;
         const int32_t ib = is_int ? *reinterpret_cast<const int32_t *>(beta) : 0;
@@ -458,7 +465,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         if (s) return s;
         if (c.family == F_TILED) {
             const int64_t la = L.lda ? L.lda : K, lb = L.ldb ? L.ldb : (pr.b_kmajor ? K : N);
-            const int64_t ea = pr.path == P_I8 ? 1 : 2;
+            const int64_t ea = (pr.path == P_I8 || pr.path == P_MX) ? 1 : 2;
             const int64_t eb = pr.path == P_E2M1 ? 1 : ea;   // e2m1: ldb counts codes, 2 per byte
             const int64_t b_ext = pr.b_kmajor ? N * lb * eb / (pr.path == P_E2M1 ? 2 : 1) : K * lb * eb;
             if (M * la * ea >= (int64_t(1) << 32) || b_ext >= (int64_t(1) << 32))
@@ -573,6 +580,154 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         return ok();
     } catch (...) {
         return fail(DG_ERR_INTERNAL, "exception in dg_gemm");
+    }
+}
+
+dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     const void *a_scale, int64_t lda_scale, const void *B, int64_t ldb, const void *b_scale,
+                     int64_t ldb_scale, void *C, int32_t c_type, int64_t ldc, float alpha,
+                     const dg_epilogue *epi, const dg_plan_opts *opts, void *workspace, size_t workspace_bytes,
+                     dg_stream_t stream)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: planning only");
+        dg_epilogue E{};
+        if (epi) E = *epi;
+        if (E.kind == DG_EPI_REQUANT_I8 || E.kind == DG_EPI_REQUANT_F16)
+            return fail(DG_ERR_UNSUPPORTED, "requantise epilogues need the int8 path");
+        const dg_dtypes dt{DG_F8E4M3, DG_E2M1, c_type, DG_F32};
+        const int64_t G = K / 32;
+        const int64_t la = lda ? lda : K, lb = ldb ? ldb : K;
+        const int64_t lsa = lda_scale ? lda_scale : (G + 3) / 4 * 4;
+        const int64_t lsb = ldb_scale ? ldb_scale : (G + 3) / 4 * 4;
+        if (lda < 0 || ldb < 0 || lda_scale < 0 || ldb_scale < 0 || ldc < 0)
+            return fail(DG_ERR_INVALID_ARG, "negative leading dimension");
+        const dg_layouts L{DG_ROW_MAJOR, DG_COL_MAJOR, la, lb, ldc ? ldc : N, N};
+        const dg_plan_opts o = opts_or_default(opts);
+        if (o.pad_k) return fail(DG_ERR_UNSUPPORTED, "the MX path needs K in whole 64-element MFMA steps");
+        Problem pr;
+        dg_status s = describe(M, N, K, &dt, &L, 32, E.kind, 0, 0, pr);
+        if (s) return s;
+        if (lsa < G || lsb < G) return fail(DG_ERR_INVALID_ARG, "a scale leading dimension is smaller than K/32");
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+            return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
+        if (M == 0 || N == 0) return ok();
+        if (!C) return fail(DG_ERR_INVALID_ARG, "C is NULL");
+        if (K > 0 && (!A || !B || !a_scale || !b_scale))
+            return fail(DG_ERR_INVALID_ARG, "A, B and both scale arrays are required");
+        const bool has_bias_kind = E.kind == DG_EPI_BIAS || E.kind == DG_EPI_BIAS_GELU_ERF;
+        if (has_bias_kind && !E.bias) return fail(DG_ERR_INVALID_ARG, "the epilogue needs a bias");
+        if (E.bias) {
+            if (E.bias_type != DG_F16 && E.bias_type != DG_BF16 && E.bias_type != DG_F32)
+                return fail(DG_ERR_UNSUPPORTED, "bias must be F16, BF16 or F32");
+            if (!has_bias_kind) return fail(DG_ERR_CONFLICT, "a bias was given to an epilogue without a bias term");
+        }
+        if ((A && !aligned(A, 16)) || (B && !aligned(B, 16)))
+            return fail(DG_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
+        if (K > 0 && (lsa % 4 || lsb % 4 || !aligned(a_scale, 4) || !aligned(b_scale, 4)))
+            return fail(DG_ERR_ALIGNMENT, "scale arrays: 4-byte aligned pointers and leading dimensions");
+        const int osz = elt_size(pr.out_type);
+        if (!aligned(C, osz)) return fail(DG_ERR_ALIGNMENT, "C is misaligned for its type");
+        Candidate c;
+        s = plan_cached(h, pr, o, c);
+        if (s) return s;
+        if (c.family != F_TILED) return fail(DG_ERR_INTERNAL, "MX plan is not a tiled plan");
+        if (M * la >= (int64_t(1) << 32) || N * lb / 2 >= (int64_t(1) << 32) || M * lsa >= (int64_t(1) << 32) ||
+            N * lsb >= (int64_t(1) << 32))
+            return fail(DG_ERR_UNSUPPORTED, "an operand spans 4 GiB or more (32-bit offsets of the tiled path)");
+        if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
+            return fail(DG_ERR_WORKSPACE, "workspace missing or smaller than " + std::to_string(c.ws_bytes) + " bytes");
+        if (c.ws_bytes > 0 && !aligned(workspace, 16)) return fail(DG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+
+        EpiArgs ea{};
+        ea.C = C;
+        ea.bias = E.bias;
+        ea.ldc = L.ldc;
+        ea.ldd = N;
+        ea.alpha = alpha;
+        ea.kind = E.kind;
+        ea.out_type = pr.out_type;
+        ea.bias_type = elt_of(E.bias_type);
+        TiledArgs ta{};
+        ta.A = A;
+        ta.B = B;
+        ta.scale = b_scale;
+        ta.scale_a = a_scale;
+        ta.lda = la;
+        ta.ldb = lb;
+        ta.ld_scale = lsb;
+        ta.ld_scale_a = lsa;
+        ta.M = (int)M;
+        ta.N = (int)N;
+        ta.K = (int)K;
+        ta.split_k = c.split_k;
+        ta.k_slice = c.k_slice;
+        ta.tiles_m = (int)((M + c.m_tile - 1) / c.m_tile);
+        ta.tiles_n = (int)((N + c.n_tile - 1) / c.n_tile);
+        ta.group_m = 4;
+        ta.ws = workspace;
+        ta.epi = ea;
+        ta.clk = reinterpret_cast<unsigned long long *>(h->clk);
+        ta.clk_wgs = h->clk ? h->clk_entries / 8 : 0;
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        hipError_t he = launch_tiled(c.kernel_id, ta, c.grid_x, c.grid_y, st);
+        if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
+        if (c.split_k > 1) {
+            ReduceArgs ra{};
+            ra.ws = workspace;
+            ra.split_k = c.split_k;
+            ra.M = (int)M;
+            ra.N = (int)N;
+            ra.is_int = 0;
+            const int64_t groups = std::max<int64_t>(1, M * N / 4);
+            int runs = 1;
+            while (runs < 16 && runs * 2 <= c.split_k && groups * runs < 65536) runs *= 2;
+            ra.lanes = c.split_k <= 8 ? 1 : runs;
+            ra.epi = ea;
+            he = launch_reduce(ra, st);
+            if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
+        }
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_gemm_mx");
+    }
+}
+
+dg_status dg_quant_mx(dg_handle_t h, int64_t M, int64_t K, const void *X, int64_t ldx, void *codes, int64_t ldq,
+                      void *scales, int64_t ld_scale, dg_stream_t stream)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: nothing is launched");
+        if (M < 0 || K < 0 || ldx < 0 || ldq < 0 || ld_scale < 0)
+            return fail(DG_ERR_INVALID_ARG, "negative size or leading dimension");
+        if (M > INT32_MAX || K > INT32_MAX) return fail(DG_ERR_UNSUPPORTED, "sizes above 2^31-1 are not supported");
+        if (K % 32) return fail(DG_ERR_ALIGNMENT, "K is not a multiple of the 32-value scale block");
+        const int64_t lx = ldx ? ldx : K, lq = ldq ? ldq : K, ls = ld_scale ? ld_scale : K / 32;
+        if (lx < K || lq < K || ls < K / 32) return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+            return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
+        if (M == 0 || K == 0) return ok();
+        if (!X || !codes || !scales) return fail(DG_ERR_INVALID_ARG, "X, codes and scales are required");
+        if (!aligned(X, 16) || !aligned(codes, 16) || (lx * 2) % 16 || lq % 16)
+            return fail(DG_ERR_ALIGNMENT, "X and codes: 16-byte aligned pointers and rows");
+        QuantMxArgs qa{};
+        qa.X = X;
+        qa.codes = codes;
+        qa.scales = scales;
+        qa.ldx = lx;
+        qa.ldq = lq;
+        qa.ld_scale = ls;
+        qa.M = (int)M;
+        qa.K = (int)K;
+        const hipError_t he = launch_quant_mx(qa, reinterpret_cast<hipStream_t>(stream));
+        if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("quantiser launch: ") + hipGetErrorString(he));
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_quant_mx");
     }
 }
 

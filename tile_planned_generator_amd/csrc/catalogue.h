@@ -10,7 +10,7 @@
 namespace dg {
 
 // Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN)
-//   path      P_F16 / P_BF16 / P_I8 / P_E2M1
+//   path      P_F16 / P_BF16 / P_I8 / P_E2M1 / P_MX
 //   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
 //   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
 #define DG_TILE_SHAPES(X, path, kmaj) \
@@ -27,7 +27,8 @@ namespace dg {
     DG_TILE_SHAPES(X, P_BF16, 1)    \
     DG_TILE_SHAPES(X, P_I8, 0)      \
     DG_TILE_SHAPES(X, P_I8, 1)      \
-    DG_TILE_SHAPES(X, P_E2M1, 1)
+    DG_TILE_SHAPES(X, P_E2M1, 1)    \
+    DG_TILE_SHAPES(X, P_MX, 1)
 
 // Skinny VALU streaming GEMM over a row-major 16-bit B:
 // X(path, MR, LPR): up to MR rows of A; LPR lanes span one row of B (8 columns each).
@@ -65,8 +66,11 @@ constexpr int tiled_min_loads_per_wave(int a_nl, int b_nl, int s_nl, int nw)
     return m;
 }
 
-constexpr int tiled_bk_elems(int path) { return path == 2 /*P_I8*/ ? 64 : 32; }
-constexpr int tiled_ksub(int path) { return path == 2 /*P_I8*/ ? 32 : 16; }
+// k elements per K step (two MFMA substeps) and per MFMA.  MX: one
+// 32x32x64 block-scaled MFMA per substep, so a step is 128 k (two 64-byte rows
+// of fp8 A per row of the tile).
+constexpr int tiled_bk_elems(int path) { return path == 4 /*P_MX*/ ? 128 : (path == 2 /*P_I8*/ ? 64 : 32); }
+constexpr int tiled_ksub(int path) { return path == 4 /*P_MX*/ ? 64 : (path == 2 /*P_I8*/ ? 32 : 16); }
 
 // Sustained fraction of the published MFMA rate one K step of a tiled variant
 // reaches on MI355X, measured with every variant forced on the 4096^3 and
@@ -78,23 +82,27 @@ constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
     const double base = waves == 8 ? 0.48
                       : bm * bn >= 256 * 128 ? 0.40
                       : bm * bn >= 128 * 128 ? 0.30 : 0.15;
-    return base * (path == 2 /*P_I8*/ ? 0.95 : (path == 3 /*P_E2M1*/ ? 0.87 : 1.0));
+    return base * (path == 2 /*P_I8*/ ? 0.95 : (path == 3 /*P_E2M1*/ ? 0.87 : 1.0));   // MX: as fp16
 }
 
 // LDS bytes of one stage (one K step) of a tiled variant.  A and a
 // K-contiguous B take 64 bytes per row (per column of B), a row-major B 64 bytes
 // per column (BN columns of a 32-k or 64-k step); e2m1 B takes 16 bytes of codes
-// plus a 4-byte scale word per column.
+// plus a 4-byte scale word per column.  MX: two 64-byte rows of fp8 A per tile
+// row, 64 bytes of e2m1 codes per column, and one dword of four e8m0 scales per
+// row of A and per column of B.
 constexpr int tiled_stage_bytes(int path, int bm, int bn)
 {
-    return bm * 64 + (path == 3 ? bn * 20 : bn * 64);
+    return path == 4 ? bm * 128 + bn * 64 + (bm + bn) * 4 : bm * 64 + (path == 3 ? bn * 20 : bn * 64);
 }
 // LDS stages: five for the eight-wave variants when they fit gfx950's 160 KB
 // (the loads of a stage are then issued a phase later, in the MFMA phase, with
-// the same lookahead), four otherwise.
+// the same lookahead), four otherwise; MX stages are larger, so as many as fit,
+// at most four (at least three).
 constexpr int tiled_nbuf(int path, int bm, int bn, int wm, int wn)
 {
-    return wm * wn == 8 && 5 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 5 : 4;
+    return path == 4 ? (4 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 4 : 3)
+                     : (wm * wn == 8 && 5 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 5 : 4);
 }
 // The epilogue reuses the LDS to stage 32 rows of every wave's accumulators
 // (4-byte values, rows padded by 4): the allocation is the larger of the two.

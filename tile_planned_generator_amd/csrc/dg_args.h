@@ -8,7 +8,9 @@
 namespace dg {
 
 // Operand paths of the tiled kernel and the skinny kernels.
-enum Path : int { P_F16 = 0, P_BF16 = 1, P_I8 = 2, P_E2M1 = 3 };
+// P_MX: fp8 e4m3 A x e2m1 B with e8m0 block scales (one per 32 k) on both,
+// fed to the block-scaled MFMA as they are stored.
+enum Path : int { P_F16 = 0, P_BF16 = 1, P_I8 = 2, P_E2M1 = 3, P_MX = 4 };
 
 // Storage types of outputs, D and bias.
 enum Elt : int { T_F16 = 0, T_BF16 = 1, T_F32 = 2, T_I32 = 3, T_I8 = 4 };
@@ -37,7 +39,9 @@ struct EpiArgs {
 // Tiled MFMA GEMM.
 struct TiledArgs {
     const void *A, *B, *scale;
-    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1)
+    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1; ld_scale in bytes for MX)
+    const void *scale_a;          // MX: A's e8m0 scales [M][K/32]
+    int64_t ld_scale_a;           // MX: bytes between rows of scale_a (a multiple of 4)
     int M, N, K;
     int split_k, k_slice;         // K slices; every slice but the last has k_slice
     int tiles_m, tiles_n, group_m;
@@ -66,6 +70,15 @@ struct TailArgs {
     int path;                     // P_F16, P_BF16 or P_I8
     int b_kmajor;                 // 1: B stored N x K
     void *ws;                     // the slice [M][N]
+};
+
+// MX quantiser: binary16 X (M x K, ldx elements) -> fp8 e4m3 codes (ldq bytes)
+// and one e8m0 scale per 32 values of a row (ld_scale bytes).
+struct QuantMxArgs {
+    const void *X;
+    void *codes, *scales;
+    int64_t ldx, ldq, ld_scale;
+    int M, K;
 };
 
 // Split-K reduction: out = epilogue(sum of ws[s] over the slices s).  `lanes`

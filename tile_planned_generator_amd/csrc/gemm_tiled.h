@@ -34,8 +34,16 @@
 //     with the dword holding the column's fp16 group scale, and decoded to fp16
 //     when the fragment is read (v_cvt_scalef32_pk_f16_fp4 with a unit scale,
 //     then a packed fp16 multiply by the group scale).
+//   - MX (fp8 e4m3 A, e2m1 B, one e8m0 scale per 32 k on each): the operands
+//     go to the block-scaled MFMA as stored, without decoding.  A step is 128 k:
+//     two 64-byte fp8 rows per tile row (k 0-63 and 64-127 of the step, each
+//     laid out and swizzled like an int8 A row), 64 bytes of codes per column
+//     (laid out like a K-contiguous B), and one dword of four scales per row of
+//     A and per column of B.  The scale register of lane group kg covers k
+//     32kg .. +31 of one MFMA, so a lane's scale is one byte of that dword.
 //   - Accumulators stay in registers for the whole K range (32x32 blocks:
-//     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8).
+//     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8,
+//     v_mfma_scale_f32_32x32x64_f8f6f4).
 //   - The K schedule is n_main full steps then at most one half step (one
 //     substep) for the tail (the pages' variable K step, [generator] DeepGEMM
 //     article, kwkr.cn, section 2.2, first layer).
@@ -121,28 +129,33 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr bool IS_I8 = PATH == P_I8;
     constexpr bool IS_E2M1 = PATH == P_E2M1;
-    constexpr bool B_TR = !BKMAJ && !IS_E2M1;          // row-major B, transposing reads
+    constexpr bool IS_MX = PATH == P_MX;
+    constexpr bool FP4B = IS_E2M1 || IS_MX;            // B holds 4-bit codes, two per byte
+    static_assert(!IS_MX || BKMAJ, "MX codes are stored N x K");
+    constexpr bool B_TR = !BKMAJ && !FP4B;             // row-major B, transposing reads
     constexpr int BKE = tiled_bk_elems(PATH);          // k elements per step
     constexpr int KSUB = tiled_ksub(PATH);             // k elements per MFMA
     static_assert(BKE == 2 * KSUB, "two substeps per step");
     constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN);
-    constexpr int ESZ = IS_I8 ? 1 : 2;                 // bytes per element of A and of a 16-bit / int8 B
-    static_assert(BKE * ESZ == 64, "64-byte rows");
-    constexpr int A_BYTES = BM * 64;
+    constexpr int ESZ = (IS_I8 || IS_MX) ? 1 : 2;      // bytes per element of A and of a 16-bit / int8 B
+    constexpr int A_REG = IS_MX ? 2 : 1;                // 64-byte A rows per tile row and step
+    static_assert(BKE * ESZ == 64 * A_REG, "64-byte rows");
+    constexpr int A_BYTES = BM * 64;                    // one A region
+    constexpr int A_ALL = A_REG * A_BYTES;
     constexpr int B_TILE = IS_E2M1 ? BN * 16 : BN * 64;   // e2m1: BKE/2 bytes of codes per column
-    constexpr int S_BYTES = IS_E2M1 ? BN * 4 : 0;          // e2m1: one scale dword per column
-    constexpr int STAGE = A_BYTES + B_TILE + S_BYTES;
+    constexpr int S_BYTES = IS_E2M1 ? BN * 4 : (IS_MX ? (BM + BN) * 4 : 0);   // scale dwords
+    constexpr int STAGE = A_ALL + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     constexpr int LDS_BYTES = tiled_lds_bytes(PATH, BM, BN, WM, WN);
     static_assert(STAGE == tiled_stage_bytes(PATH, BM, BN), "stage size");
-    static_assert(STAGE % 1024 == 0 || IS_E2M1, "stage alignment");
+    static_assert(STAGE % 1024 == 0 || IS_E2M1 || (IS_MX && STAGE % 256 == 0), "stage alignment");
     // direct-to-LDS loads: a 16-byte load fills 1 KB (64 lanes), a dword load 256 B.
     // Load i of an operand is issued by wave i % NW (the scale loads from the
     // last wave down, to even out the per-wave counts).
-    constexpr int A_NL = A_BYTES / 1024, B_NL = B_TILE / 1024, S_NL = S_BYTES / 256;
-    static_assert(A_NL * 1024 == A_BYTES && B_NL * 1024 == B_TILE && S_NL * 256 == S_BYTES,
+    constexpr int A_NL = A_ALL / 1024, B_NL = B_TILE / 1024, S_NL = S_BYTES / 256;
+    static_assert(A_NL * 1024 == A_ALL && B_NL * 1024 == B_TILE && S_NL * 256 == S_BYTES,
                   "tile not whole loads");
     constexpr int A_LD = (A_NL + NW - 1) / NW, B_LD = (B_NL + NW - 1) / NW, S_LD = (S_NL + NW - 1) / NW;
     constexpr int LPS = tiled_min_loads_per_wave(A_NL, B_NL, S_NL, NW);   // fewest loads a wave issues per stage
@@ -185,7 +198,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 
     const int M = p.M, N = p.N;
     const uint32_t lda_b = (uint32_t)(p.lda * ESZ);
-    const uint32_t ldb_b = (uint32_t)(IS_E2M1 ? p.ldb / 2 : p.ldb * ESZ);
+    const uint32_t ldb_b = (uint32_t)(FP4B ? p.ldb / 2 : p.ldb * ESZ);
     // Operand extents, in bytes from the tile origin to the end of the last
     // valid element (a 16-byte chunk never straddles it: K and the column
     // blocks are 16-byte multiples).  The host checks they fit 32 bits.
@@ -194,7 +207,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     const char *Bbase;
     uint32_t b_bytes;
     if constexpr (BKMAJ) {
-        const int64_t rowb = IS_E2M1 ? p.K / 2 : (int64_t)p.K * ESZ;
+        const int64_t rowb = FP4B ? p.K / 2 : (int64_t)p.K * ESZ;
         Bbase = reinterpret_cast<const char *>(p.B) + (int64_t)n0 * ldb_b;
         b_bytes = (uint32_t)((N - n0 - 1) * (int64_t)ldb_b + rowb);
     } else {
@@ -217,17 +230,32 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const int64_t last = (int64_t)(N - 1) * p.ld_scale + p.K / 32;   // one past the last element
         s_bytes = (uint32_t)((smis + 2 * last + 3) & ~(int64_t)3);
     }
+    // MX scales: e8m0 bytes, row r of A at scale_a + r * ld_scale_a, column n of
+    // B at scale + n * ld_scale (both pitches multiples of 4, both pointers
+    // 4-byte aligned, K/32 bytes used per row).  Each stage fetches the dword of
+    // its four blocks; the range ends at the last row's last dword, so rows past
+    // M or N (offsets at or past the range) read zeros.
+    const char *SAbase = nullptr;
+    uint32_t sa_bytes = 0;
+    if constexpr (IS_MX) {
+        SAbase = reinterpret_cast<const char *>(p.scale_a);
+        Sbase = reinterpret_cast<const char *>(p.scale);
+        sa_bytes = (uint32_t)((M - 1) * p.ld_scale_a + ((p.K / 32 + 3) & ~3));
+        s_bytes = (uint32_t)((N - 1) * p.ld_scale + ((p.K / 32 + 3) & ~3));
+    }
 
     // ---- per-lane source offsets of this wave's direct-to-LDS loads.  Load q of
     // an operand fills LDS bytes [q * 1024, +1024) of its region; lane l writes
     // 16-byte chunk pc = q * 64 + l of it.  Rows past the operand start at or
     // beyond its extent: their loads return zeros.
+    // (MX: chunks past the first region fill the second, 64 k further on.)
     uint32_t oa[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int pc = (i * NW + wave) * 64 + lane;
+        const int pc0 = (i * NW + wave) * 64 + lane;
+        const int reg = pc0 / (BM * 4), pc = pc0 % (BM * 4);
         const int r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
-        oa[i] = r * lda_b + c * 16;
+        oa[i] = reg * 64 + r * lda_b + c * 16;
     }
     uint32_t ob[B_LD];
 #pragma unroll
@@ -249,7 +277,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
     for (int i = 0; i < S_LD; ++i) {
         const int col = (i * NW + swave) * 64 + lane;   // byte of scale (n0 + col, 0) from Sbase
-        os[i] = smis + 2 * (uint32_t)((n0 + col) * p.ld_scale);
+        if constexpr (IS_MX)   // entries [0, BM): rows of A; [BM, BM + BN): columns of B
+            os[i] = col < BM ? (uint32_t)((m0 + col) * p.ld_scale_a) : (uint32_t)((n0 + col - BM) * p.ld_scale);
+        else
+            os[i] = smis + 2 * (uint32_t)((n0 + col) * p.ld_scale);
     }
 
     // Issue the loads of step j (k0 = kbeg + j * BKE) into LDS stage j % NBUF.
@@ -265,17 +296,25 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             if (A_NL % NW == 0 || i * NW + wave < A_NL) {   // wave-uniform
                 const __amdgpu_buffer_rsrc_t rA =
                     make_rsrc(Abase + (int64_t)k0 * ESZ, real ? a_bytes - (uint32_t)(k0 * ESZ) : 0u);
-                buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);
+                buf_ld16_lds(rA, oa[i], sb + (i * NW + wave) * 1024);   // (both MX regions)
             }
         } else if (i < A_LD + B_LD) {
             const int q = i - A_LD;
             if (B_NL % NW == 0 || q * NW + wave < B_NL) {   // wave-uniform
                 uint32_t kb;
-                if constexpr (IS_E2M1) kb = (uint32_t)(k0 >> 1);
+                if constexpr (FP4B) kb = (uint32_t)(k0 >> 1);
                 else if constexpr (BKMAJ) kb = (uint32_t)(k0 * ESZ);
                 else kb = (uint32_t)k0 * ldb_b;
                 const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + kb, real ? b_bytes - kb : 0u);
-                buf_ld16_lds(rB, ob[q], sb + A_BYTES + (q * NW + wave) * 1024);
+                buf_ld16_lds(rB, ob[q], sb + A_ALL + (q * NW + wave) * 1024);
+            }
+        } else if constexpr (IS_MX) {
+            const int q = i - A_LD - B_LD;
+            if (S_NL % NW == 0 || q * NW + swave < S_NL) {   // wave-uniform
+                const bool rows = (q * NW + swave) * 64 < BM;   // wave-uniform: A's or B's scales
+                const __amdgpu_buffer_rsrc_t rS =
+                    make_rsrc(rows ? SAbase : Sbase, real ? (rows ? sa_bytes : s_bytes) : 0u);
+                buf_ld4_lds(rS, os[q] + (uint32_t)(k0 >> 5), sb + A_ALL + B_TILE + (q * NW + swave) * 256);
             }
         } else if constexpr (IS_E2M1) {
             const int q = i - A_LD - B_LD;
@@ -302,11 +341,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0;
 
-    // fragments of one k-substep: FM A blocks and FN B blocks (16 bytes per lane each)
+    // fragments of one k-substep: FM A blocks and FN B blocks (16 bytes per lane
+    // each; MX: 32 bytes of fp8 A per lane, and the lane's scale bytes of its A
+    // row and B column in the low byte of sa / sb)
+    using AFrag = typename std::conditional<IS_MX, u32x8, u32x4>::type;
     struct Frag {
-        u32x4 a[FM];
+        AFrag a[FM];
         u32x4 b[FN];
+        unsigned sa[IS_MX ? FM : 1], sb[IS_MX ? FN : 1];
     };
+    Frag f0, f1;
     // Per-lane LDS byte offsets (within a stage) of the fragment reads.
     //   A / K-major B: row `row`, logical chunk 2s + kg.
     //   row-major B (transposing reads): lane L of 16-lane group g supplies K row
@@ -324,11 +368,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             if constexpr (!IS_I8) {
                 const int col = col0 + 16 * (grp16 & 1) + 4 * (L16 & 3);
                 const int k = 8 * (grp16 >> 1) + (L16 >> 2);
-                boff[ni] = A_BYTES + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
+                boff[ni] = A_ALL + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
             } else {
                 const int col = col0 + 16 * (grp16 & 1) + 8 * (L16 & 1);
                 const int k = 16 * (grp16 >> 1) + (L16 >> 1);
-                boff[ni] = A_BYTES + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
+                boff[ni] = A_ALL + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
             }
         } else {
             boff[ni] = 0;
@@ -346,11 +390,32 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const char *sA = smem + buf * STAGE;
         const int c = 2 * s + kg;
         const int row = wm * WTM + mi * 32 + lr;
-        f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+        if constexpr (IS_MX) {
+            // Region s.  The 8-bit operand of the 32x32x64 block-scaled MFMA is
+            // not 32 consecutive k per lane: lane group kg holds k 16kg .. +15 in
+            // its first four registers and k 32 + 16kg .. +15 in its last four
+            // (the 4-bit operand holds k 32kg .. +31), and the scale of lane
+            // group kg applies to k 32kg .. +31 of both operands (probed on the
+            // GPU with one-hot operands).  So the lane reads chunks kg and kg+2.
+            // The stage's scale dword is read with substep 0 (shifted to this
+            // lane's block kg); substep 1 takes the same dword's next block pair
+            // from substep 0's fragment, which holds the same stage.
+            const char *rA = sA + s * A_BYTES + row * 64;
+            const int sw = (row >> 2) & 3;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(rA + ((kg ^ sw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
+            f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (s == 0)
+                f.sa[mi] = *reinterpret_cast<const unsigned *>(sA + A_ALL + B_TILE + row * 4) >> (8 * kg);
+            else
+                f.sa[mi] = f0.sa[mi] >> 16;
+        } else {
+            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+        }
     };
     auto read_b = [&](int buf, auto s_tag, int ni, Frag &f, int g) {
         constexpr int s = decltype(s_tag)::value;
-        const char *sB = smem + buf * STAGE + A_BYTES;
+        const char *sB = smem + buf * STAGE + A_ALL;
         const int c = 2 * s + kg;
         const int col0 = wn * WTN + ni * 32;
         if constexpr (IS_E2M1) {
@@ -362,8 +427,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const unsigned sh = ((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd & 0xffffu;
             f.b[ni] = u32x4{codes, sh, 0u, 0u};
         } else if constexpr (BKMAJ) {
+            // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
             f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+            if constexpr (IS_MX) {
+                if constexpr (s == 0)
+                    f.sb[ni] = *reinterpret_cast<const unsigned *>(sB + B_TILE + BM * 4 + row * 4) >> (8 * kg);
+                else
+                    f.sb[ni] = f0.sb[ni] >> 16;
+            }
         } else {
             const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
             u32x2 lo, hi;
@@ -418,6 +490,12 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         else if constexpr (PATH == P_BF16)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, f.b[ni]), __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
+        else if constexpr (IS_MX)
+            // first operand e2m1 (format 4, four registers used), second fp8 e4m3
+            // (format 0); each scale is the low byte of its register
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                __builtin_bit_cast(intx8, u32x8{f.b[ni].x, f.b[ni].y, f.b[ni].z, f.b[ni].w, 0u, 0u, 0u, 0u}),
+                __builtin_bit_cast(intx8, f.a[mi]), acc[mi][ni], 4, 0, 0, (int)f.sb[ni], 0, (int)f.sa[mi]);
         else
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                 __builtin_bit_cast(intx4, f.b[ni]), __builtin_bit_cast(intx4, f.a[mi]), acc[mi][ni], 0, 0, 0);
@@ -432,12 +510,20 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // nothing): the fragments are ANDed with a uniform mask, so the loop body has
     // no branch at all - a branch near the MFMAs makes the compiler copy every
     // accumulator on each step.
+    // (MX: the scales become 127, a factor of one: a scale byte past K may be the
+    // NaN code, and NaN times zero is not zero.)
     auto keep_if = [&](Frag &f, bool keep) {
         const unsigned m = keep ? ~0u : 0u;
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi) f.a[mi] &= m;
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni) f.b[ni] &= m;
+        if constexpr (IS_MX) {
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi) f.sa[mi] = (f.sa[mi] & m) | (~m & 127u);
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni) f.sb[ni] = (f.sb[ni] & m) | (~m & 127u);
+        }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -449,7 +535,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // for every wave (the loads of stages st+2 and st+3 may still be in flight)
     // and that no wave still reads stage st, whose buffer takes stage st+4.  The
     // body is branch-free.
-    Frag f0, f1;
     if constexpr (NW == 8) {
         // Eight waves: two groups of four (waves 0-3 and 4-7, one of each per
         // SIMD) alternate a memory phase (read both fragments of stage st, wait

@@ -1,5 +1,5 @@
 // gemm_tiled.hip - launcher of the tiled MFMA GEMM variants (the kernels are
-// instantiated per operand path in gemm_tiled_{f16,bf16,i8,e2m1}.hip).
+// instantiated per operand path in gemm_tiled_{f16,bf16,i8,e2m1,mx}.hip).
 #include <hip/hip_runtime.h>
 
 #include "catalogue.h"
@@ -11,6 +11,7 @@ void *tiled_kernel_ptr_f16(int id);
 void *tiled_kernel_ptr_bf16(int id);
 void *tiled_kernel_ptr_i8(int id);
 void *tiled_kernel_ptr_e2m1(int id);
+void *tiled_kernel_ptr_mx(int id);
 
 static const TiledShape k_shapes[] = {
 #define DG_TS(path, kmaj, bm, bn, wm, wn) {path, kmaj, bm, bn, wm, wn},
@@ -28,7 +29,8 @@ hipError_t launch_tiled(int id, const TiledArgs &a, int grid_x, int grid_y, hipS
     case P_F16: fn = tiled_kernel_ptr_f16(id); break;
     case P_BF16: fn = tiled_kernel_ptr_bf16(id); break;
     case P_I8: fn = tiled_kernel_ptr_i8(id); break;
-    default: fn = tiled_kernel_ptr_e2m1(id); break;
+    case P_E2M1: fn = tiled_kernel_ptr_e2m1(id); break;
+    default: fn = tiled_kernel_ptr_mx(id); break;
     }
     if (!fn) return hipErrorInvalidDeviceFunction;
     TiledArgs arg = a;

@@ -1,0 +1,25 @@
+// gemm_tiled_mx.hip - instantiates the tiled kernel variants of the mx path.
+#include "gemm_tiled.h"
+
+namespace dg {
+
+template <int PATH, int KMAJ, int BM, int BN, int WM, int WN>
+static void *pick_mx()
+{
+    if constexpr (PATH == P_MX)
+        return reinterpret_cast<void *>(gemm_tiled_kernel<PATH, KMAJ, BM, BN, WM, WN>);
+    else
+        return nullptr;
+}
+
+#define DG_PICK(path, kmaj, bm, bn, wm, wn) pick_mx<path, kmaj, bm, bn, wm, wn>(),
+
+// Kernel of catalogue entry id if it belongs to this path, else NULL.
+void *tiled_kernel_ptr_mx(int id)
+{
+    static void *const table[] = {DG_TILED_CATALOGUE(DG_PICK)};
+    const int n = (int)(sizeof(table) / sizeof(table[0]));
+    return (id >= 0 && id < n) ? table[id] : nullptr;
+}
+
+}  // namespace dg

@@ -22,6 +22,9 @@ hipError_t launch_skinny_mfma(int id, const SkinnyArgs &a, int grid_x, int grid_
 int skinny_e2m1_count();
 hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int grid_x, int grid_y, hipStream_t s);
 
+// MX quantiser: binary16 -> fp8 e4m3 codes and e8m0 block scales.
+hipError_t launch_quant_mx(const QuantMxArgs &a, hipStream_t s);
+
 // Split-K reduction and epilogue.
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 

@@ -92,14 +92,31 @@ const char *path_name(int p)
     case P_F16: return "f16";
     case P_BF16: return "bf16";
     case P_I8: return "i8";
+    case P_MX: return "mx";
     default: return "e2m1";
     }
 }
 
 int elt_bytes(int t) { return (t == T_F16 || t == T_BF16) ? 2 : (t == T_I8 ? 1 : 4); }
 
-// MFMA operations per clock per CU (2 per multiply-add): 16-bit 4096, int8 8192.
-double mfma_ops_per_clk_cu(int path) { return path == P_I8 ? 8192.0 : 4096.0; }
+// MFMA operations per clock per CU (2 per multiply-add): 16-bit 4096, int8 and
+// the fp8 x fp4 block-scaled MFMA (the fp8 rate) 8192.
+double mfma_ops_per_clk_cu(int path) { return (path == P_I8 || path == P_MX) ? 8192.0 : 4096.0; }
+
+// Bytes per element of A and of B as stored.
+double a_elt_bytes(int path) { return (path == P_I8 || path == P_MX) ? 1.0 : 2.0; }
+double b_elt_bytes(int path)
+{
+    return path == P_I8 ? 1.0 : ((path == P_E2M1 || path == P_MX) ? 0.5 : 2.0);
+}
+// Block-scale bytes: e2m1 one fp16 per 32 codes of B; MX one byte per 32
+// values of A and of B.
+double scale_bytes(const Problem &pr)
+{
+    if (pr.path == P_E2M1) return (double)pr.N * (pr.K / 32) * 2;
+    if (pr.path == P_MX) return (double)(pr.M + pr.N) * (pr.K / 32);
+    return 0.0;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -156,10 +173,8 @@ constexpr double LAUNCH_US = 2.0;
 
 double roofline_us(const Problem &pr, const dg_device_desc &d)
 {
-    const double esz_a = pr.path == P_I8 ? 1 : 2;
-    const double esz_b = pr.path == P_I8 ? 1 : (pr.path == P_E2M1 ? 0.5 : 2);
-    double bytes = pr.M * pr.K * esz_a + pr.K * pr.N * esz_b + pr.M * pr.N * elt_bytes(pr.out_type);
-    if (pr.path == P_E2M1) bytes += (double)pr.N * (pr.K / 32) * 2;
+    double bytes = pr.M * pr.K * a_elt_bytes(pr.path) + pr.K * pr.N * b_elt_bytes(pr.path) +
+                   pr.M * pr.N * elt_bytes(pr.out_type) + scale_bytes(pr);
     if (pr.beta_nz) bytes += pr.M * pr.N * elt_bytes(pr.out_type);
     const double flops = 2.0 * pr.M * pr.N * pr.K;
     const double t_mem = hbm_us(bytes, d);
@@ -183,7 +198,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
         // registers (per lane): accumulators, staging, fragments, addressing
         const int acc = FM * FN * 16;
         int stage = s.bm * 8 / NT * 4;
-        if (pr.path == P_E2M1) stage += ceil_div(s.bn * 2, NT) * 5;
+        if (pr.path == P_MX) stage = s.bm * 16 / NT * 4 + s.bn * 8 / NT * 4 + (FM + FN) * 2;
+        else if (pr.path == P_E2M1) stage += ceil_div(s.bn * 2, NT) * 5;
         else if (s.b_kmajor) stage += s.bn * 8 / NT * 4;
         else stage += (int)ceil_div(s.bn, NT) * 32;
         const int other = stage + (FM + FN) * 4 * 2 + 40;
@@ -201,7 +217,9 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
         const int min_slice = 4 * BKE;
         for (int S : split_choices(pr.K, BKE, min_slice, o.force_split_k)) {
             ++enumerated;
-            const int unit = (pr.K >= (int64_t)S * BKE) ? BKE : KSUB;
+            // (MX slices start on whole steps: a step's four scales are one
+            // aligned dword)
+            const int unit = (pr.K >= (int64_t)S * BKE || pr.path == P_MX) ? BKE : KSUB;
             int k_slice = pr.K > 0 ? slice_len(pr.K, S, unit) : 0;
             const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
             if (S_eff == 1) k_slice = (int)pr.K;   // one slice: exactly K, tail included
@@ -258,8 +276,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             const double per_step = std::max(W * std::max(t_mfma, std::max(t_lds, t_l2)), lat);
             const double steps = ceil_div(std::max(k_slice, 1), BKE);
             const double t_comp = rounds * steps * per_step / cpu;
-            double floor_bytes = pr.M * pr.K * (pr.path == P_I8 ? 1.0 : 2.0) +
-                                 pr.K * pr.N * (pr.path == P_I8 ? 1.0 : (pr.path == P_E2M1 ? 0.5 : 2.0));
+            double floor_bytes = pr.M * pr.K * a_elt_bytes(pr.path) + pr.K * pr.N * b_elt_bytes(pr.path) +
+                                 scale_bytes(pr);
             const double out_bytes = (double)pr.M * pr.N * elt_bytes(pr.out_type) * (pr.beta_nz ? 2 : 1);
             // the epilogue stores after the K loop, at about 70 % of HBM bandwidth
             double est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + LAUNCH_US;

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libdg.so")
 # ------------------------------------------------------------------ enums
 DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_ALIGNMENT, DG_ERR_NO_CANDIDATE, \
     DG_ERR_CONFLICT, DG_ERR_INVALID_STATE, DG_ERR_WORKSPACE, DG_ERR_HIP, DG_ERR_INTERNAL = range(10)
-DG_F16, DG_BF16, DG_F32, DG_I8, DG_I32, DG_E2M1 = range(6)
+DG_F16, DG_BF16, DG_F32, DG_I8, DG_I32, DG_E2M1, DG_F8E4M3, DG_E8M0 = range(8)
 DG_ROW_MAJOR, DG_COL_MAJOR = 0, 1
 DG_EPI_NONE, DG_EPI_BIAS, DG_EPI_GELU_ERF, DG_EPI_BIAS_GELU_ERF, DG_EPI_REQUANT_I8, \
     DG_EPI_REQUANT_F16 = range(6)
@@ -27,7 +27,7 @@ EPI = {"none": DG_EPI_NONE, "bias": DG_EPI_BIAS, "gelu_erf": DG_EPI_GELU_ERF,
        "bias_gelu_erf": DG_EPI_BIAS_GELU_ERF, "requant_i8": DG_EPI_REQUANT_I8,
        "requant_f16": DG_EPI_REQUANT_F16}
 DTYPE = {"f16": DG_F16, "bf16": DG_BF16, "f32": DG_F32, "i8": DG_I8, "i32": DG_I32,
-         "e2m1": DG_E2M1}
+         "e2m1": DG_E2M1, "f8e4m3": DG_F8E4M3, "e8m0": DG_E8M0}
 
 
 # ------------------------------------------------------------- structures
@@ -85,8 +85,8 @@ class dg_plan_info(C.Structure):
 
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
-           "dg_plan_candidates", "dg_gemm", "dg_set_stage_clock", "dg_probe", "dg_set_device_desc",
-           "dg_last_error", "dg_status_str")
+           "dg_plan_candidates", "dg_gemm", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
+           "dg_probe", "dg_set_device_desc", "dg_last_error", "dg_status_str")
 
 _lib = None
 
@@ -114,6 +114,9 @@ def load():
         "dg_gemm": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), P, P, P, i32,
                      P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t,
                      P], S),
+        "dg_gemm_mx": ([H, i64, i64, i64, P, i64, P, i64, P, i64, P, i64, P, i32, i64, C.c_float,
+                        C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t, P], S),
+        "dg_quant_mx": ([H, i64, i64, P, i64, P, i64, P, i64, P], S),
         "dg_set_stage_clock": ([H, P, i64], S),
         "dg_probe": ([H, i32, P, C.c_size_t, i32, P, i32, P], S),
         "dg_set_device_desc": ([H, C.POINTER(dg_device_desc)], S),
@@ -155,6 +158,14 @@ def dg_plan_candidates(*a):
 
 def dg_gemm(*a):
     return load().dg_gemm(*a)
+
+
+def dg_gemm_mx(*a):
+    return load().dg_gemm_mx(*a)
+
+
+def dg_quant_mx(*a):
+    return load().dg_quant_mx(*a)
 
 
 def dg_set_stage_clock(h, buf, entries):
@@ -255,6 +266,53 @@ class Handle:
         dt = dg_dtypes(DTYPE[a], DTYPE[b], DTYPE[c], compute)
         lay = dg_layouts(DG_ROW_MAJOR, b_layout, lda, ldb, ldc, ldd)
         return dt, lay
+
+    def quant_mx(self, X, codes, scales, stream=None):
+        """MX quantiser through dg_quant_mx: X [M, K] fp16 -> codes [M, K] uint8
+        (fp8 e4m3) and scales [M, K/32] uint8 (e8m0); rows may be padded."""
+        import torch
+        M, K = X.shape
+        for t, nm in ((X, "X"), (codes, "codes"), (scales, "scales")):
+            if t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError(f"{nm} must be a 2-D tensor with unit column stride")
+        if stream is None:
+            stream = torch.cuda.current_stream(X.device).cuda_stream
+        check(dg_quant_mx(self.h, M, K, X.data_ptr(), X.stride(0), codes.data_ptr(), codes.stride(0),
+                          scales.data_ptr(), scales.stride(0), stream))
+
+    def gemm_mx(self, A, SA, B, SB, C_out, *, alpha=1.0, bias=None, epilogue="none", K=None,
+                opts=None, workspace=None, stream=None):
+        """C_out = act(alpha * (A.B) + bias) through dg_gemm_mx.
+
+        A: [M, K] uint8 fp8 e4m3 codes; SA: [M, >= K/32] uint8 e8m0 scales;
+        B: [N, K/2] uint8 packed e2m1 codes (pack_e2m1); SB: [N, >= K/32] uint8
+        e8m0 scales.  Rows may be padded (strides are the leading dimensions).
+        Returns the plan info.
+        """
+        import torch
+        M, K_a = A.shape
+        N = B.shape[0]
+        K = K_a if K is None else K
+        for t, nm in ((A, "A"), (SA, "SA"), (B, "B"), (SB, "SB"), (C_out, "C")):
+            if t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError(f"{nm} must be a 2-D tensor with unit column stride")
+        c = _dtype_name(C_out)
+        epi = dg_epilogue(EPI[epilogue], DTYPE[_dtype_name(bias)] if bias is not None else 0,
+                          bias.data_ptr() if bias is not None else None, 1.0)
+        lda, ldb, ldc = A.stride(0), B.stride(0) * 2, C_out.stride(0)
+        info = self.plan(M, N, K, "f8e4m3", "e2m1", c, DG_COL_MAJOR, epilogue, group_k=32, opts=opts,
+                         lda=lda, ldb=ldb, ldc=ldc)
+        if workspace is None and info.workspace_bytes > 0:
+            workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=A.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device).cuda_stream
+        check(dg_gemm_mx(self.h, M, N, K, A.data_ptr(), lda, SA.data_ptr(), SA.stride(0), B.data_ptr(),
+                         ldb, SB.data_ptr(), SB.stride(0), C_out.data_ptr(), DTYPE[c], ldc, float(alpha),
+                         C.byref(epi), C.byref(opts) if opts is not None else None, ws_ptr, ws_bytes,
+                         stream))
+        return info
 
     def plan(self, M, N, K, a="f16", b="f16", c="f16", b_layout=None, epilogue="none",
              group_k=0, opts=None, **ld):
