@@ -5,7 +5,8 @@ One step is one dg_gemm call on the int8 4096^3 workload (plan from the
 handle's cache, the tiled MFMA kernel, the fused epilogue): the workload the
 headline throughput is quoted on.  The other workloads (fp16 4096^3, the bf16
 M = 1 and M = 16 long-K GEMMs, the GELU GEMM, the e2m1 GEMMs, the small alpha/beta
-GEMM) are timed after it and reported under "workloads".  Inputs are seeded
+GEMM, the MX fp8 x e2m1 GEMM through dg_gemm_mx and the MX quantiser through
+dg_quant_mx) are timed after it and reported under "workloads".  Inputs are seeded
 synthetic data drawn on the GPU and resident in HBM before any timing starts.
 
 Timing: HIP events on the stream the kernels run on (torch's current stream),
@@ -33,20 +34,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("TFLOP/s (TOPS int8) at 4096³ + GB/s at M=1 long-K, each as % of MI355X peak")
-PEAK = {"i8": 5033.2, "f16": 2516.6, "bf16": 2516.6, "e2m1": 2516.6}   # dense TOP/s / TFLOP/s
+PEAK = {"i8": 5033.2, "f16": 2516.6, "bf16": 2516.6, "e2m1": 2516.6,   # dense TOP/s / TFLOP/s
+        "mx": 5033.2}                                                  # (fp8: the MX MFMA's rate)
 HBM_PEAK = 8000.0                                                      # GB/s
 CACHE_BYTES = 576 * 10 ** 6       # 2 x (256 MB MALL + 32 MB L2)
 
 HEADLINE = "i8_4096x4096x4096"
 SECONDARY = ["f16_4096x4096x4096", "bf16_1x4096x131072", "bf16_16x4096x131072",
              "f16_2048x2048x8192_bias_gelu", "e2m1_4096x4096x4096", "e2m1_1x4096x4096",
-             "bf16_1x256x12800", "f16_256x256x256_alpha_beta_d"]
+             "bf16_1x256x12800", "f16_256x256x256_alpha_beta_d", "mx_4096x4096x4096",
+             "mxq_4096x4096"]
 
 
 def algorithmic(w):
     """(ops, bytes): 2*M*N*K, and every operand read once plus C written once."""
     M, N, K = w.M, w.N, w.K
+    if w.path == "mxq":   # quantiser: binary16 in, one code byte and 1/32 scale byte out
+        return 0, M * K * 2 + M * K + M * (K // 32)
     ops = 2 * M * N * K
+    if w.path == "mx":
+        return ops, M * K + K * N // 2 + (M + N) * (K // 32) + M * N * 2
     ea = 1 if w.path == "i8" else 2
     eb = {"i8": 1, "e2m1": 0.5}.get(w.path, 2)
     eo = {"i32": 4, "f32": 4}.get(w.out, 2)
@@ -121,6 +128,64 @@ class Prepared:
         s = self.lib.dg_gemm(*self.args[i % self.R])
         if s != 0:
             self.dg.check(s)
+
+
+class PreparedMx:
+    """Device operands of the MX workloads and a pre-marshalled dg_gemm_mx or
+    dg_quant_mx call (the same interface as Prepared)."""
+
+    def __init__(self, h, name, dev, rotate):
+        import torch
+        from tile_planned_generator_amd import dg, synth
+        self.dg = dg
+        self.w = w = synth.make(name, device=dev)
+        t = w.tensors
+        self.lib = dg.load()
+        self.h = h
+        self.stream = torch.cuda.current_stream().cuda_stream
+        M, N, K = w.M, w.N, w.K
+        G = K // 32
+        if w.path == "mxq":
+            X0 = t["X"].contiguous()
+            per = X0.numel() * 2
+            self.R = -(-CACHE_BYTES // per) if rotate and per < CACHE_BYTES else 1
+            self.Xs = [X0] + [X0.clone() for _ in range(self.R - 1)]
+            self.Qs = [torch.empty(M, K, dtype=torch.uint8, device=dev) for _ in range(self.R)]
+            self.Ss = [torch.empty(M, G, dtype=torch.uint8, device=dev) for _ in range(self.R)]
+            self.C = self.Qs[0]
+            self.info = None
+            self.fn = self.lib.dg_quant_mx
+            self.args = [(h.h, M, K, self.Xs[i].data_ptr(), K, self.Qs[i].data_ptr(), K,
+                          self.Ss[i].data_ptr(), G, self.stream) for i in range(self.R)]
+            return
+        self.A = t["A"].contiguous()
+        self.SA = t["SA"].contiguous()
+        B0 = dg.pack_e2m1(t["codes"])
+        S0 = t["SB"].t().contiguous()
+        per = B0.numel() + S0.numel()
+        self.R = -(-CACHE_BYTES // per) if rotate and per < CACHE_BYTES else 1
+        self.Bs = [B0] + [B0.clone() for _ in range(self.R - 1)]
+        self.Ss = [S0] + [S0.clone() for _ in range(self.R - 1)]
+        self.C = torch.empty(M, N, dtype=torch.float16, device=dev)
+        self.info = h.plan(M, N, K, "f8e4m3", "e2m1", "f16", dg.DG_COL_MAJOR, w.epilogue, group_k=32)
+        self.ws = (torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=dev)
+                   if self.info.workspace_bytes else None)
+        self.epi = dg.dg_epilogue(dg.EPI[w.epilogue], 0, None, 1.0)
+        self.fn = self.lib.dg_gemm_mx
+        self.args = [(h.h, M, N, K, self.A.data_ptr(), K, self.SA.data_ptr(), G, self.Bs[i].data_ptr(),
+                      K, self.Ss[i].data_ptr(), G, self.C.data_ptr(), dg.DG_F16, N, C.c_float(w.alpha),
+                      C.byref(self.epi), None, self.ws.data_ptr() if self.ws is not None else None,
+                      self.ws.numel() if self.ws is not None else 0, self.stream)
+                     for i in range(self.R)]
+
+    def launch(self, i=0):
+        s = self.fn(*self.args[i % self.R])
+        if s != 0:
+            self.dg.check(s)
+
+
+def prepare(h, name, dev, rotate):
+    return (PreparedMx if name.startswith("mx") else Prepared)(h, name, dev, rotate)
 
 
 def time_steps(p, steps, warmup, use_graph):
@@ -221,6 +286,10 @@ def report(p, ms):
     tflops = ops / (ms * 1e-3) / 1e12
     gbps = byts / (ms * 1e-3) / 1e9
     i = p.info
+    if path == "mxq":
+        return {"ms": round(ms, 6), "GB/s": round(gbps, 1), "bound": "hbm",
+                "frac_of_peak": round(gbps / HBM_PEAK, 4), "kernel": "quant_mx_kernel",
+                "algorithmic_bytes": byts}
     bound = "hbm" if p.w.M <= 16 else "mfma"
     frac = gbps / HBM_PEAK if bound == "hbm" else tflops / PEAK[path]
     return {"ms": round(ms, 6), "TFLOP/s" if path != "i8" else "TOP/s": round(tflops, 2),
@@ -328,13 +397,13 @@ def main():
     if not args.only_headline:
         chosen = [w for w in args.workloads.split(",") if w] or SECONDARY
         for name in chosen:
-            p = Prepared(h, name, dev, rotate=True)
-            small = p.info.est_us < 25
+            p = prepare(h, name, dev, rotate=True)
+            small = p.info is None or p.info.est_us < 25
             ms_w, _ = time_steps(p, max(50, args.steps // 2), args.warmup, use_graph=small)
             r = report(p, ms_w)
             if p.R > 1:
                 r["rotated_copies"] = p.R
-                pw = Prepared(h, name, dev, rotate=False)
+                pw = prepare(h, name, dev, rotate=False)
                 ms_warm, _ = time_steps(pw, max(50, args.steps // 2), args.warmup, use_graph=small)
                 r["warm"] = report(pw, ms_warm)
                 del pw

@@ -372,3 +372,72 @@ def test_pad_k_plans(off):
     # e2m1 K must stay whole groups
     s, _ = _status(off.plan, 64, 64, 48, "f16", "e2m1", "f16", opts=dg.dg_plan_opts(pad_k=1))
     assert s == dg.DG_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------- MX block-scaled path
+def _mx_dt(c=None):
+    return dg.dg_dtypes(dg.DG_F8E4M3, dg.DG_E2M1, dg.DG_F16 if c is None else c, dg.DG_F32)
+
+
+def _mx_lay():
+    return dg.dg_layouts(dg.DG_ROW_MAJOR, dg.DG_COL_MAJOR, 0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (100, 200, 320), (1, 4096, 4096), (7, 9, 64)])
+def test_mx_plans_satisfy_constraints(off, M, N, K):
+    arr = (dg.dg_plan_info * 64)()
+    cnt = C.c_int32()
+    dg.check(dg.dg_plan_candidates(off.h, M, N, K, C.byref(_mx_dt()), C.byref(_mx_lay()), 32, 0, None,
+                                   arr, 64, C.byref(cnt)))
+    assert cnt.value >= 1
+    for i in range(min(64, cnt.value)):
+        p = arr[i]
+        name = p.kernel_name.decode()
+        assert name.startswith("tiled_mx_k_"), name
+        assert p.mfma_m == 32 and p.mfma_n == 32 and p.mfma_k == 64
+        assert p.lds_bytes <= 163840 and p.vgpr_est <= 256 and p.agpr_est <= 256
+        # K steps of 128 (two block-scaled MFMAs); slices start on whole steps
+        assert p.k_main == 128 and p.k_tail in (0, 64)
+        if p.split_k > 1:
+            assert p.k_slice % 128 == 0
+        assert p.k_main * p.n_main + p.k_tail * p.n_tail == min(p.k_slice, K)
+
+
+def test_mx_errors(off):
+    info = dg.dg_plan_info()
+    # K must be whole 64-element MFMA steps; pad_k is not offered
+    assert dg.dg_plan(off.h, 64, 64, 96, C.byref(_mx_dt()), C.byref(_mx_lay()), 32, 0, None,
+                      C.byref(info)) == dg.DG_ERR_ALIGNMENT
+    o = dg.dg_plan_opts(pad_k=1)
+    assert dg.dg_plan(off.h, 64, 64, 96, C.byref(_mx_dt()), C.byref(_mx_lay()), 32, 0, C.byref(o),
+                      C.byref(info)) == dg.DG_ERR_UNSUPPORTED
+    # fp8 A with a B that is not e2m1, or a row-major e2m1 B
+    bad = dg.dg_dtypes(dg.DG_F8E4M3, dg.DG_F16, dg.DG_F16, dg.DG_F32)
+    assert dg.dg_plan(off.h, 64, 64, 128, C.byref(bad), C.byref(_mx_lay()), 32, 0, None,
+                      C.byref(info)) == dg.DG_ERR_UNSUPPORTED
+    rm = dg.dg_layouts(dg.DG_ROW_MAJOR, dg.DG_ROW_MAJOR, 0, 0, 0, 0)
+    assert dg.dg_plan(off.h, 64, 64, 128, C.byref(_mx_dt()), C.byref(rm), 32, 0, None,
+                      C.byref(info)) == dg.DG_ERR_UNSUPPORTED
+    # requantise epilogues and int outputs belong to the int8 path
+    assert dg.dg_plan(off.h, 64, 64, 128, C.byref(_mx_dt()), C.byref(_mx_lay()), 32,
+                      dg.DG_EPI_REQUANT_I8, None, C.byref(info)) == dg.DG_ERR_UNSUPPORTED
+    assert dg.dg_plan(off.h, 64, 64, 128, C.byref(_mx_dt(dg.DG_I32)), C.byref(_mx_lay()), 32, 0, None,
+                      C.byref(info)) == dg.DG_ERR_UNSUPPORTED
+    # an offline handle launches nothing
+    assert dg.dg_gemm_mx(off.h, 64, 64, 128, None, 0, None, 0, None, 0, None, 0, None, dg.DG_F16, 0,
+                         1.0, None, None, None, 0, None) == dg.DG_ERR_INVALID_STATE
+    assert dg.dg_quant_mx(off.h, 4, 64, None, 0, None, 0, None, 0, None) == dg.DG_ERR_INVALID_STATE
+    # dg_gemm does not take MX operands (no scales for A)
+    one = C.c_float(1.0)
+    assert dg.dg_gemm(off.h, 64, 64, 128, C.byref(_mx_dt()), C.byref(_mx_lay()), None, None, None, 32,
+                      None, None, C.byref(one), C.byref(one), None, None, None, 0,
+                      None) == dg.DG_ERR_INVALID_STATE
+
+
+def test_mx_plan_uses_fp8_rate_and_scale_bytes(off):
+    i8 = off.plan(4096, 4096, 4096, "i8", "i8", "i32")
+    mx = off.plan(4096, 4096, 4096, "f8e4m3", "e2m1", "f16", group_k=32)
+    f16 = off.plan(4096, 4096, 4096, "f16", "f16", "f16")
+    # the block-scaled fp8 x fp4 MFMA runs at the int8 / fp8 rate, twice fp16's
+    assert mx.est_us < 0.75 * f16.est_us
+    assert abs(mx.est_roof_fraction - i8.est_roof_fraction) < 0.25

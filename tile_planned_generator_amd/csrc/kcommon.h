@@ -18,6 +18,7 @@ typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 
 #define DG_DEV __device__ __forceinline__

@@ -12,10 +12,12 @@
 // block holding an infinity or a NaN gets the NaN scale code 255 and NaN codes
 // 0x7f.
 //
-// One thread per block: four 16-byte loads, two 16-byte code stores and one
-// scale byte; consecutive threads take consecutive blocks of a row, so a wave
-// reads and writes contiguous memory.  HBM-bound: 2 bytes read and 1 + 1/32
-// bytes written per value.
+// Four lanes share a block: each lane loads 16 contiguous bytes (8 values), so
+// one load instruction of a wave reads 1 KB of consecutive memory, the block
+// maximum is combined over the four lanes with quad permutes, and each lane
+// stores its 8 codes (8 contiguous bytes).  Each workgroup streams a contiguous
+// share of the rows with the next round's loads in flight.
+// HBM-bound: 2 bytes read and 1 + 1/32 bytes written per value.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,98 +26,144 @@
 
 namespace dg {
 
-// e4m3 code of a binary32 value v with |v| < 512 (or any v: magnitudes of 448
-// and above give 448), nearest even.  Normal range: 3 mantissa bits kept from
-// the binary32 significand with round-half-even on the 20 dropped bits (a carry
-// out of the mantissa moves to the next exponent, which the code's bit layout
-// absorbs).  Below 2^-6: the subnormal quantum is 2^-9, so the code is
-// rint(|v| * 2^9) (8 is the smallest normal, code 0x08, again by the layout).
-DG_DEV unsigned e4m3_rne_sat(float v)
+// Four e4m3 codes (one dword, first value in the low byte) of binary32 values
+// already divided by the block scale.  Clamping to +-448 first and then rounding
+// to nearest even gives what rounding then saturating gives: every magnitude in
+// (448, 464) rounds to 448 anyway, and larger ones saturate to it.  The
+// conversion instruction rounds to nearest even and keeps e4m3's subnormals.
+DG_DEV unsigned e4m3x4(float a, float b, float c, float d)
 {
-    const unsigned u = __builtin_bit_cast(unsigned, v);
-    const unsigned sign = (u >> 24) & 0x80u;
-    const float a = __builtin_fabsf(v);
-    unsigned code;
-    if (a >= 448.0f) {
-        code = 0x7eu;
-    } else if (a < 0.015625f) {
-        code = (unsigned)__builtin_rintf(a * 512.0f);
-    } else {
-        const unsigned ua = u & 0x7fffffffu;
-        const int exp = (int)(ua >> 23) - 127;          // -6 .. 8
-        const unsigned man = ua & 0x7fffffu;
-        const unsigned keep = man >> 20, rem = man & 0xfffffu;
-        const unsigned up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
-        code = ((unsigned)(exp + 7) << 3) + keep + up;
-        if (code > 0x7eu) code = 0x7eu;
-    }
-    return sign | code;
+    const float lo = -448.0f, hi = 448.0f;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi), __builtin_amdgcn_fmed3f(b, lo, hi),
+                                            0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi), __builtin_amdgcn_fmed3f(d, lo, hi), w,
+                                        true);
+    return (unsigned)w;
 }
 
-__global__ void __launch_bounds__(256) quant_mx_kernel(QuantMxArgs p)
+constexpr int QU = 4;          // chunks of 8 values per thread and round
+constexpr int QWG = 256;       // threads per workgroup
+constexpr int QGRID = 1024;    // workgroups at most (four per CU)
+
+// Row and column (in chunks) of chunk c; 32-bit division whenever the chunk
+// count fits (`narrow` is the same for the whole grid).
+DG_DEV void chunk_rc(int64_t c, int64_t cpr, bool narrow, int64_t &row, int64_t &col)
 {
-    const int G = p.K / 32;
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= (int64_t)p.M * G) return;
-    const int row = (int)(b / G), g = (int)(b - (int64_t)row * G);
-    const _Float16 *x = reinterpret_cast<const _Float16 *>(p.X) + (int64_t)row * p.ldx + g * 32;
-    u32x4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x) + i);
-    float f[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const unsigned w = raw[i][j];
-            f[8 * i + 2 * j] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
-            f[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
-        }
-    float amax = 0.0f;
-    bool finite = true;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-        const float a = __builtin_fabsf(f[t]);
-        finite = finite && a <= 65504.0f;   // false for infinities and NaN
-        amax = a > amax ? a : amax;
-    }
-    unsigned sc;
-    u32x4 out[2];
-    if (!finite) {
-        sc = 255u;
-        out[0] = out[1] = u32x4{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+    if (narrow) {
+        const uint32_t q = (uint32_t)c / (uint32_t)cpr;
+        row = q;
+        col = c - (int64_t)q * cpr;
     } else {
-        // amax is a binary32 normal (binary16 subnormals are), so its exponent
-        // field gives floor(log2 amax); e stays within -32 .. 7.
-        const int e = amax == 0.0f ? -127 : (int)(__builtin_bit_cast(unsigned, amax) >> 23) - 127 - 8;
-        sc = (unsigned)(e + 127);
-        // 2^-e as a binary32 (e >= -32: a normal power of two); amax = 0 leaves
-        // every value zero, so any factor keeps the signs
-        const float inv = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            unsigned w = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) w |= e4m3_rne_sat(f[4 * q + t] * inv) << (8 * t);
-            out[q >> 2][q & 3] = w;
-        }
+        row = c / cpr;
+        col = c - row * cpr;
     }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(p.codes) + (int64_t)row * p.ldq + g * 32);
-    __builtin_nontemporal_store(out[0], dst);
-    __builtin_nontemporal_store(out[1], dst + 1);
-    reinterpret_cast<uint8_t *>(p.scales)[(int64_t)row * p.ld_scale + g] = (uint8_t)sc;
+}
+
+// Each workgroup streams a contiguous share of the chunks (`per` chunks, a
+// multiple of QWG * QU) in rounds of QWG * QU; the loads of round r + 1 are
+// issued before round r is converted.  Chunk of thread t, round r, item j:
+// base + r * QWG * QU + j * QWG + t, so the four lanes 4q .. 4q+3 of a wave hold
+// the four chunks of one block, and a block is in range for all four or for
+// none (the chunk count is a multiple of 4): the swaps only mix lanes of one
+// block.
+__global__ void __launch_bounds__(QWG) quant_mx_kernel(QuantMxArgs p, int64_t per)
+{
+    const int64_t cpr = p.K / 8;                          // chunks per row (a multiple of 4)
+    const int64_t nch = (int64_t)p.M * cpr;
+    const bool narrow = nch + (int64_t)QWG * QU <= 0xffffffffLL;
+    const int64_t base = (int64_t)blockIdx.x * per + threadIdx.x;
+    const int64_t end = min(nch, (int64_t)(blockIdx.x + 1) * per);
+    const int rounds = (int)(per / (QWG * QU));
+    auto load = [&](int r, u32x4 (&raw)[QU]) {
+#pragma unroll
+        for (int j = 0; j < QU; ++j) {
+            const int64_t c = base + (int64_t)r * QWG * QU + j * QWG;
+            if (c < end) {
+                int64_t row, col;
+                chunk_rc(c, cpr, narrow, row, col);
+                raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    reinterpret_cast<const _Float16 *>(p.X) + row * p.ldx + col * 8));
+            } else {
+                raw[j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    u32x4 cur[QU], nxt[QU];
+    load(0, cur);
+    for (int r = 0; r < rounds; ++r) {
+        if (base + (int64_t)r * QWG * QU >= end) break;   // uniform over a block's lanes
+        if (r + 1 < rounds) load(r + 1, nxt);
+#pragma unroll
+        for (int j = 0; j < QU; ++j) {
+            const int64_t c = base + (int64_t)r * QWG * QU + j * QWG;
+            const bool live = c < end;   // uniform over the four lanes of a block
+            // The block maximum on the magnitude bits: for binary16, the order of
+            // |x| is the integer order of its low 15 bits, infinities and NaN
+            // above every finite value (0x7c00 and up), so one packed integer
+            // maximum per dword finds both the maximum and any non-finite value.
+            unsigned mx = 0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const unsigned w = cur[j][d] & 0x7fff7fffu;
+                mx = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx),
+                                                                            __builtin_bit_cast(u16x2, w)));
+            }
+            mx = max(mx & 0xffffu, mx >> 16);
+            // lanes 4q .. 4q+3: swap neighbours, then pairs (quad permutes
+            // [1,0,3,2] and [2,3,0,1], no LDS round trip)
+            mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, true));
+            mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, true));
+            if (!live) continue;
+            const bool bad = mx >= 0x7c00u;
+            const float amax = (float)__builtin_bit_cast(_Float16, (unsigned short)mx);
+            int64_t row, col;
+            chunk_rc(c, cpr, narrow, row, col);
+            unsigned sc;
+            u32x2 out;
+            if (bad) {
+                sc = 255u;
+                out = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};
+            } else {
+                // amax is a binary32 normal (binary16 subnormals are), so its
+                // exponent field gives floor(log2 amax); e stays within -32 .. 7.
+                const int e = amax == 0.0f ? -127 : (int)(__builtin_bit_cast(unsigned, amax) >> 23) - 127 - 8;
+                sc = (unsigned)(e + 127);
+                // 2^-e as a binary32 (e >= -32: a normal power of two); amax = 0
+                // leaves every value zero, so any factor keeps the signs
+                const float inv = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
+                float f[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const unsigned w = cur[j][d];
+                    f[2 * d] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu)) * inv;
+                    f[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)) * inv;
+                }
+                out = u32x2{e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
+            }
+            __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(
+                reinterpret_cast<uint8_t *>(p.codes) + row * p.ldq + col * 8));
+            if ((col & 3) == 0) reinterpret_cast<uint8_t *>(p.scales)[row * p.ld_scale + col / 4] = (uint8_t)sc;
+        }
+#pragma unroll
+        for (int j = 0; j < QU; ++j) cur[j] = nxt[j];
+    }
 }
 
 hipError_t launch_quant_mx(const QuantMxArgs &a, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)a.M * (a.K / 32);
-    if (blocks == 0) return hipSuccess;
-    const int64_t grid = (blocks + 255) / 256;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t chunks = (int64_t)a.M * (a.K / 8);
+    if (chunks == 0) return hipSuccess;
+    constexpr int64_t R = (int64_t)QWG * QU;              // chunks per workgroup round
+    int64_t grid = (chunks + R - 1) / R;
+    if (grid > QGRID) grid = QGRID;
+    const int64_t per = ((chunks + grid - 1) / grid + R - 1) / R * R;
+    grid = (chunks + per - 1) / per;
+    if (per / R > 0x7fffffff) return hipErrorInvalidValue;
     QuantMxArgs arg = a;
-    void *args[] = {&arg};
+    int64_t per_arg = per;
+    void *args[] = {&arg, &per_arg};
     hipError_t e = hipLaunchKernel(reinterpret_cast<void *>(quant_mx_kernel), dim3((unsigned)grid, 1, 1),
-                                   dim3(256, 1, 1), args, 0, s);
+                                   dim3(QWG, 1, 1), args, 0, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
