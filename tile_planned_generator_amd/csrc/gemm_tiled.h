@@ -582,11 +582,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             tie(f1);
             if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
             bar();
-            // compute phase
+            // compute phase, at raised wave priority so that the SIMD's other
+            // wave (in its memory phase) does not delay the MFMA issue
+            __builtin_amdgcn_s_setprio(1);
             decode_b(f0);
             mfmas(f0);
             decode_b(f1);
             mfmas(f1);
+            __builtin_amdgcn_s_setprio(0);
             bar();
         };
         if (clk_on) ck1 = __builtin_amdgcn_s_memtime();

@@ -152,6 +152,23 @@ std::vector<int> split_choices(int64_t K, int unit, int min_slice, int force)
     return s;
 }
 
+// K splits for the streaming kernels: the powers of two, plus the counts that
+// give the grid (grid_x column blocks per slice) about 3/4, one and two
+// workgroups per CU.
+std::vector<int> split_choices_grid(int64_t K, int unit, int min_slice, int force, int64_t grid_x, int cus)
+{
+    std::vector<int> s = split_choices(K, unit, min_slice, force);
+    if (force > 0 || grid_x <= 0) return s;
+    for (double f : {0.75, 1.0, 2.0}) {
+        const int v = (int)std::ceil(f * cus / (double)grid_x);
+        if (v > 1 && v <= 1024 && K / v >= min_slice && K / v >= unit &&
+            std::find(s.begin(), s.end(), v) == s.end())
+            s.push_back(v);
+    }
+    std::sort(s.begin(), s.end());
+    return s;
+}
+
 // Slice length: a multiple of `unit`; the last slice takes what is left.
 int slice_len(int64_t K, int S, int unit) { return (int)round_up(ceil_div(K, S), unit); }
 
@@ -307,9 +324,25 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
 
     // `cols_per_wave`: columns one wave streams; waves past N idle, and a partly
     // filled wave counts for the share of its lanes that have columns.
-    auto finish = [&](Candidate &c, double b_bytes, double valu_lane_ops, int cols_per_wave) {
-        const double waves_active = c.grid_y * (double)pr.N / cols_per_wave;
-        const double eff = std::min(1.0, waves_active / (d.cu_count * 8.0));
+    // `by_wg`: the stream's rate is set by its workgroups rather than its waves
+    // (the long-K kernels, whose workgroups each keep deep double-buffered loads
+    // in flight).  Measured on MI355X (bf16, N = 4096, K = 131072): HBM is
+    // saturated from about 3/4 of the CUs with one workgroup each; a grid
+    // between one and two workgroups per CU leaves the CUs with two as the
+    // critical path (the time of a full second round); splits beyond that only
+    // add partial sums.
+    auto finish = [&](Candidate &c, double b_bytes, double valu_lane_ops, int cols_per_wave, bool by_wg = false) {
+        double eff;
+        if (by_wg) {
+            const double wgs = (double)c.grid_x * c.grid_y;
+            const double rounds = std::ceil(wgs / d.cu_count);
+            eff = wgs <= d.cu_count ? std::min(1.0, wgs / (0.75 * d.cu_count)) : wgs / (rounds * d.cu_count);
+            // the share of the workgroups' columns that exist (four waves each)
+            eff *= std::min(1.0, (double)pr.N / ((double)c.grid_x * 4 * cols_per_wave));
+        } else {
+            const double waves_active = c.grid_y * (double)pr.N / cols_per_wave;
+            eff = std::min(1.0, waves_active / (d.cu_count * 8.0));
+        }
         const double t_mem = hbm_us(b_bytes, d) / (0.92 * std::max(eff, 1e-3));
         const double t_valu = valu_lane_ops / (d.cu_count * 64.0 * cpu);
         double est = std::max(t_mem, t_valu) + hbm_us(out_bytes, d) + LAUNCH_US;
@@ -327,7 +360,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
             if (s.path != pr.path || s.mr < pr.M || (s.mr > 1 && s.mr / 2 >= pr.M)) continue;
             const int rpi = 64 / s.lpr;
             const int wcols = s.lpr * 8;
-            for (int S : split_choices(pr.K, 16, 64, o.force_split_k)) {
+            for (int S : split_choices_grid(pr.K, 16, 64, o.force_split_k, ceil_div(pr.N, 4 * wcols), d.cu_count)) {
                 ++enumerated;
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 16) : 0;
                 const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
@@ -361,7 +394,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
                 finish(c, (double)pr.K * pr.N * 2 + pr.M * pr.K * 2.0,
-                       (double)s.mr * pr.K * pr.N * 1.3 + (double)pr.K * pr.N, wcols);
+                       (double)s.mr * pr.K * pr.N * 1.3 + (double)pr.K * pr.N, wcols, true);
                 char nm[64];
                 std::snprintf(nm, sizeof nm, "skinny_valu_%s_mr%d_lpr%d", path_name(pr.path), s.mr, s.lpr);
                 c.name = nm;
@@ -375,7 +408,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
         const int nm_ = (int)(sizeof(k_mfma_paths) / sizeof(k_mfma_paths[0]));
         for (int id = 0; id < nm_; ++id) {
             if (k_mfma_paths[id] != pr.path) continue;
-            for (int S : split_choices(pr.K, 32, 256, o.force_split_k)) {
+            for (int S : split_choices_grid(pr.K, 32, 256, o.force_split_k, ceil_div(pr.N, 512), d.cu_count)) {
                 ++enumerated;
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 32) : 0;
                 const int S_eff = pr.K > 0 ? (int)ceil_div(pr.K, std::max(1, k_slice)) : 1;
@@ -406,7 +439,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 c.grid_y = S_eff;
                 c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
                 finish(c, (double)pr.K * pr.N * 2 + 16.0 * pr.K * 2 * c.grid_x,
-                       (double)pr.K * pr.N * 0.6, 128);
+                       (double)pr.K * pr.N * 0.6, 128, true);
                 char nm[64];
                 std::snprintf(nm, sizeof nm, "skinny_mfma_%s", path_name(pr.path));
                 c.name = nm;
