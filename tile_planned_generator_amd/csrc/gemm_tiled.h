@@ -351,6 +351,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         unsigned sa[IS_MX ? FM : 1], sb[IS_MX ? FN : 1];
     };
     Frag f0, f1;
+    // e2m1: substep 1's code word and the step's scale, taken by substep 0's read
+    unsigned e2_next[IS_E2M1 ? FN : 1], e2_sh[IS_E2M1 ? FN : 1];
     // Per-lane LDS byte offsets (within a stage) of the fragment reads.
     //   A / K-major B: row `row`, logical chunk 2s + kg.
     //   row-major B (transposing reads): lane L of 16-lane group g supplies K row
@@ -420,12 +422,24 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const int col0 = wn * WTN + ni * 32;
         if constexpr (IS_E2M1) {
             // raw: the code word and the scale's bits; decode_b turns them into
-            // the fp16 operand (in the MFMA phase, off the LDS-bound one)
+            // the fp16 operand (in the MFMA phase, off the LDS-bound one).  Substep
+            // 0 reads the column's whole 16-byte chunk (dword 2s + kg is substep
+            // s's word for lane group kg): the 16 lanes of a read phase then cover
+            // 256 contiguous bytes, where single-dword reads of 16-byte slots put
+            // columns r and r + 16 in one bank.  Substep 1 takes its word and the
+            // step's scale (one group per step) from that read; it always follows
+            // substep 0 of the same stage.
             const int row = col0 + lr;
-            const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + (2 * s + kg) * 4);
-            const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
-            const unsigned sh = ((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd & 0xffffu;
-            f.b[ni] = u32x4{codes, sh, 0u, 0u};
+            if constexpr (s == 0) {
+                const u32x4 raw = *reinterpret_cast<const u32x4 *>(sB + row * 16);
+                const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
+                const unsigned sh = ((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd & 0xffffu;
+                f.b[ni] = u32x4{kg ? raw.y : raw.x, sh, 0u, 0u};
+                e2_next[ni] = kg ? raw.w : raw.z;
+                e2_sh[ni] = sh;
+            } else {
+                f.b[ni] = u32x4{e2_next[ni], e2_sh[ni], 0u, 0u};
+            }
         } else if constexpr (BKMAJ) {
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
