@@ -246,3 +246,34 @@ def test_quant_then_gemm_end_to_end(h):
     R = oracle.gemm_mx(rc, rs, w["codes"].numpy(), w["SB"].numpy())
     st = check_fp(Cd, R, "f16")
     say(f"  {st}")
+
+
+# ---------------------------------------------------------------- random sweep
+def _mx_cases(n=16, seed=20261203):
+    """Seeded random MX problems: ragged M and N, K in whole 64-element steps
+    (half steps included), planner-chosen or forced K splits and tiles, every
+    epilogue, fp16 or fp32 output, tight or padded leading dimensions."""
+    rng = np.random.default_rng(seed)
+    tiles = [(0, 0, 0), (256, 256, 8), (128, 256, 4), (256, 128, 4), (128, 128, 4), (64, 64, 4)]
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 3, 17, 64, 100, 257, 513]))
+        N = int(rng.integers(1, 80)) * 8 + int(rng.choice([0, 0, 3]))
+        K = int(rng.integers(1, 40)) * 64
+        split = int(rng.choice([0, 0, 2, 3]))
+        bm, bn, w = tiles[int(rng.integers(0, len(tiles)))]
+        epi = ["none", "bias", "gelu_erf", "bias_gelu_erf"][int(rng.integers(0, 4))]
+        out_t = torch.float32 if rng.random() < 0.25 else torch.float16
+        pad = int(rng.choice([0, 0, 12]))
+        alpha = float(rng.choice([1.0, 0.75]))
+        out.append((M, N, K, split, bm, bn, w, epi, out_t, pad, alpha, seed + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _mx_cases(), ids=lambda c: "{}x{}x{}-s{}-t{}x{}-{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], c[7]))
+def test_gemm_mx_random_problem(h, case):
+    M, N, K, split, bm, bn, w, epi, out_t, pad, alpha, seed = case
+    o = dg.dg_plan_opts(force_split_k=split, force_m_tile=bm, force_n_tile=bn, force_waves=w,
+                        force_path=dg.DG_PATH_TILED if split or bm else 0)
+    run_mx(h, M, N, K, seed=seed, pad=pad, opts=o, out=out_t, alpha=alpha, epilogue=epi)
