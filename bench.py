@@ -343,6 +343,18 @@ def stage_breakdown(h, p, launches=5):
     s["frac"] = {k: round(s[k]["median"] / max(1, tot), 4) for k in ("prologue", "k_loop", "epilogue")}
     s.pop("span")   # the counters of different dies do not compare
     s["unit"] = "s_memtime ticks per workgroup"
+    # The s_memtime counter runs at the MFMA clock (a 32x32x32 int8 MFMA issues
+    # every 32 ticks back to back), and its rate over the K loop's real time is
+    # the clock the loop ran at.  MFMA cycles one SIMD owes per K step: the
+    # tile's 32x32 blocks times the step's MFMA depths times the cycles of one
+    # MFMA (32 for int8 32x32x32), over the CU's 4 SIMDs.
+    i = p.info
+    per_step = (i.m_tile // 32) * (i.n_tile // 32) * (i.k_main // i.mfma_k) * 32 / 4
+    if s["k_loop"]["median"] > 0:
+        s["k_loop_mfma_busy"] = round(per_step * s["k_steps"] / s["k_loop"]["median"], 4)
+    if s.get("tick_ghz"):
+        s["k_loop_clock_ghz"] = s["tick_ghz"]
+        s["k_loop_peak_at_clock"] = round(PEAK["i8"] * s["tick_ghz"] / 2.4, 1)
     return s
 
 

@@ -315,7 +315,12 @@ dg_status dg_quant_mx(dg_handle_t h, int64_t M, int64_t K, const void *X, int64_
  *   0 kernel entry, 1 K-loop start, 2 K-loop end, 3 epilogue end (stores issued)
  *     - values of the s_memtime counter read by the workgroup's first wave (each
  *     die counts on its own, so only stamps from one die compare);
- *   4 HW_ID register (CU, shader array, shader engine), 5 XCC_ID (die),
+ *   4 HW_ID register (CU, shader array, shader engine) in bits 0-31, and in
+ *     bits 32-63 the low 32 bits of the s_memrealtime counter (a constant
+ *     100 MHz clock) at K-loop start;
+ *   5 XCC_ID (die) in bits 0-31, and in bits 32-63 the low 32 bits of
+ *     s_memrealtime at K-loop end (so entry 2 - entry 1 over the real-time
+ *     difference is the rate s_memtime ticks at during the K loop);
  *   6 K steps of the workgroup's slice, 7 blockIdx.x | blockIdx.y << 32.
  *   h        a live device handle
  *   buf      device memory owned by the caller, NULL to switch the clock off

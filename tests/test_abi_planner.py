@@ -322,6 +322,14 @@ def test_stage_cycles_summary():
     assert s["k_loop"] == {"median": 100, "max": 100}
     assert s["epilogue"] == {"median": 20, "max": 40}
     assert s["span"] == 155 and s["k_steps"] == 4
+    assert s["k_loop_us"] is None and s["tick_ghz"] is None     # no real-time stamps
+    # real-time stamps (100 MHz) in the high halves of entries 4 and 5, one of
+    # them across the 32-bit wrap: 100 ticks over 40 ns and 50 ns
+    r[:, 4] = np.array([10, 20, 2**32 - 2, 30], dtype=np.int64) << 32
+    r[:, 5] = (np.array([14, 25, 3, 34], dtype=np.int64) << 32) | np.array([0, 0, 1, 1])
+    s = dg.stage_cycles(r, 4)
+    assert s["span"] == 155                                         # dies still from the low halves
+    assert s["k_loop_us"] == 0.045 and s["tick_ghz"] == 2.25
 
 
 def test_probe_description_round_trip():

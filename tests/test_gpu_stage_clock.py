@@ -34,7 +34,14 @@ def test_stage_clock_records(h, bm, bn, nw, split):  # noqa: F811
     assert (rec != SENTINEL).all()
     t = rec[:, :4]
     assert (np.diff(t, axis=1) >= 0).all()             # entry <= loop start <= loop end <= end
-    assert (rec[:, 5] >= 0).all() and (rec[:, 5] < 8).all()   # die (XCC) index
+    die = rec[:, 5] & 0xFFFFFFFF
+    assert (die >= 0).all() and (die < 8).all()        # die (XCC) index
+    # real time of the K loop (100 MHz counter in the high halves of 4 and 5):
+    # positive, and the s_memtime rate over it a plausible engine clock
+    rt = (((rec[:, 5] >> 32) & 0xFFFFFFFF) - ((rec[:, 4] >> 32) & 0xFFFFFFFF)) % (1 << 32)
+    assert (rt > 0).all()
+    ghz = (rec[:, 2] - rec[:, 1]) / (rt * 10.0)
+    assert (ghz > 0.3).all() and (ghz < 3.0).all(), ghz
     # K steps: a step is 32 k; the slices are k_slice long but the last
     steps = {-(-min(info.k_slice, w.K - s * info.k_slice) // 32) for s in range(info.split_k)}
     assert set(rec[:, 6].tolist()) <= steps
@@ -44,6 +51,7 @@ def test_stage_clock_records(h, bm, bn, nw, split):  # noqa: F811
     assert sorted((x + y * gx).tolist()) == list(range(grid))
     s = dg.stage_cycles(rec, grid)
     assert s["k_loop"]["median"] > 0 and s["span"] >= s["k_loop"]["max"]
+    assert s["k_loop_us"] > 0 and 0.3 < s["tick_ghz"] < 3.0
 
     # clock off: the buffer stays as it is
     buf.fill_(SENTINEL)

@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // entry, loop start, loop end and kernel end, taken by wave 0 when a buffer
     // is given.
     const bool clk_on = p.clk != nullptr;
-    unsigned long long ck0 = 0, ck1 = 0, ck2 = 0;
+    unsigned long long ck0 = 0, ck1 = 0, ck2 = 0, rt1 = 0, rt2 = 0;   // rt: s_memrealtime (100 MHz)
     if (clk_on) ck0 = __builtin_amdgcn_s_memtime();
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -606,7 +606,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             __builtin_amdgcn_s_setprio(0);
             bar();
         };
-        if (clk_on) ck1 = __builtin_amdgcn_s_memtime();
+        if (clk_on) {
+            ck1 = __builtin_amdgcn_s_memtime();
+            rt1 = __builtin_amdgcn_s_memrealtime();
+        }
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
@@ -671,7 +674,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         for (int j = 0; j < NBUF; ++j) load_stage(j);
         wait_vm_barrier<(NBUF - 1) * LPS>();
         read_frag(0, S0{}, f0, g0);
-        if (clk_on) ck1 = __builtin_amdgcn_s_memtime();
+        if (clk_on) {
+            ck1 = __builtin_amdgcn_s_memtime();
+            rt1 = __builtin_amdgcn_s_memrealtime();
+        }
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
@@ -679,7 +685,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         // no transposing read is in flight when the epilogue reuses registers)
     }
 
-    if (clk_on) ck2 = __builtin_amdgcn_s_memtime();
+    if (clk_on) {
+        ck2 = __builtin_amdgcn_s_memtime();
+        rt2 = __builtin_amdgcn_s_memrealtime();
+    }
 
     // ---- epilogue: each wave stages 32 rows of its accumulators in LDS at a time
     // (a 16-byte write per four columns of a row: the blocks are transposed) and
@@ -831,9 +840,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 
     // Stage clock record of this workgroup (8 entries, written by lanes 0-7 of
     // wave 0 with vector stores): the four stamps, the hardware placement
-    // (HW_ID: CU, shader array and engine; XCC_ID: die), the K steps, and the
-    // workgroup's grid coordinates.  The end stamp follows the issue of the last
-    // store, not its completion.
+    // (HW_ID: CU, shader array and engine; XCC_ID: die) with the low 32 bits of
+    // the real-time counter at K-loop start and end in their high halves, the K
+    // steps, and the workgroup's grid coordinates.  The end stamp follows the
+    // issue of the last store, not its completion.
     if (clk_on) {
         const unsigned long long ck3 = __builtin_amdgcn_s_memtime();
         const long long wg = (long long)blockIdx.y * gridDim.x + blockIdx.x;
@@ -841,8 +851,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const unsigned hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);
             const unsigned xcc_id = __builtin_amdgcn_s_getreg((31 << 11) | 20);
             unsigned long long v = lane == 0 ? ck0 : lane == 1 ? ck1 : lane == 2 ? ck2 : ck3;
-            if (lane == 4) v = hw_id;
-            if (lane == 5) v = xcc_id;
+            if (lane == 4) v = hw_id | ((rt1 & 0xffffffffull) << 32);
+            if (lane == 5) v = xcc_id | ((rt2 & 0xffffffffull) << 32);
             if (lane == 6) v = (unsigned long long)nsteps;
             if (lane == 7) v = (unsigned long long)blockIdx.x | ((unsigned long long)blockIdx.y << 32);
             p.clk[wg * 8 + lane] = v;

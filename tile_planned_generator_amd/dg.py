@@ -400,13 +400,21 @@ def stage_cycles(rec, wgs):
     dg_set_stage_clock): per-workgroup ticks of the prologue (entry to K-loop
     start), the K loop and the epilogue, as medians and maxima, plus the span
     from the earliest entry to the latest end.  Each die (XCC) counts on its own
-    clock, so the span is taken per die and the largest is reported."""
+    clock, so the span is taken per die and the largest is reported.  The K
+    loop's real time comes from the 100 MHz counter in the high halves of
+    entries 4 and 5; `k_loop_us` is its median and `tick_ghz` the median rate of
+    the s_memtime counter over it (None when the records hold no real time)."""
     import numpy as np
     r = np.asarray(rec, dtype=np.int64).reshape(-1, 8)[:wgs]
     pro, loop, epi = r[:, 1] - r[:, 0], r[:, 2] - r[:, 1], r[:, 3] - r[:, 2]
     out = {}
     for name, v in (("prologue", pro), ("k_loop", loop), ("epilogue", epi)):
         out[name] = {"median": int(np.median(v)), "max": int(v.max())}
-    out["span"] = int(max(r[r[:, 5] == x, 3].max() - r[r[:, 5] == x, 0].min() for x in np.unique(r[:, 5])))
+    die = r[:, 5] & 0xFFFFFFFF
+    out["span"] = int(max(r[die == x, 3].max() - r[die == x, 0].min() for x in np.unique(die)))
     out["k_steps"] = int(np.median(r[:, 6]))
+    rt = (((r[:, 5] >> 32) & 0xFFFFFFFF) - ((r[:, 4] >> 32) & 0xFFFFFFFF)) % (1 << 32)
+    ok = rt > 0
+    out["k_loop_us"] = round(float(np.median(rt[ok])) / 100.0, 3) if ok.any() else None
+    out["tick_ghz"] = round(float(np.median(loop[ok] / (rt[ok] * 10.0))), 4) if ok.any() else None
     return out
