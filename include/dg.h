@@ -228,6 +228,30 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K,
                              int32_t epi_kind, const dg_plan_opts *opts,
                              dg_plan_info *out, int32_t cap, int32_t *count);
 
+/* Plan for every K in [K_min, K_max] at once: the pages' range constraint
+ * (K_min / K_max in the declaration instead of one K, so that one compact
+ * kernel serves every layer whose K falls in the range, [overview] section 6,
+ * the second stage of the service case).  K is sampled at both ends and at the
+ * doublings between them; each compiled kernel variant of the problem's path
+ * (tile and wave grid, or the streaming path) is planned at every sample, and
+ * the variant whose largest ratio of estimated time to the best plan of that K
+ * is smallest wins (ties: fewer LDS bytes, then catalogue order).
+ *   opts         as for dg_plan, with tile, waves and path left free
+ *   range_opts   out: the options that pin the chosen variant; pass them to
+ *                dg_gemm (or dg_plan) for any K of the range, where the planner
+ *                still chooses the K split and schedule of that K
+ *   out          nullable: the plan of the chosen variant at K_max
+ *   worst_ratio  nullable: the chosen variant's largest estimated-time ratio
+ * Errors: DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG (range_opts NULL, K_min < 0
+ * or K_min > K_max), DG_ERR_CONFLICT (a forced tile, wave count or path), and
+ * what dg_plan returns at either end of the range (DG_ERR_ALIGNMENT for an
+ * unaligned end without pad_k); DG_ERR_NO_CANDIDATE when no variant is valid
+ * for every sample. */
+dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int64_t K_max,
+                        const dg_dtypes *dt, const dg_layouts *lay, int32_t group_k,
+                        int32_t epi_kind, const dg_plan_opts *opts, dg_plan_opts *range_opts,
+                        dg_plan_info *out, double *worst_ratio);
+
 /* Enqueue C = act(alpha*(A.B) + beta*D + bias) on `stream` (the kernel argument
  * list of the pages' launch, A, B, C, alpha, beta, m, n, k, [generator] section
  * 3.2, step 4, plus the precision, layout and epilogue description).

@@ -449,3 +449,76 @@ def test_mx_plan_uses_fp8_rate_and_scale_bytes(off):
     # the block-scaled fp8 x fp4 MFMA runs at the int8 / fp8 rate, twice fp16's
     assert mx.est_us < 0.75 * f16.est_us
     assert abs(mx.est_roof_fraction - i8.est_roof_fraction) < 0.25
+
+
+# ------------------------------------------------------------------ K ranges
+def _range_samples(K_min, K_max, unit):
+    """The K samples dg_plan_range documents: both ends and the doublings between."""
+    ks = [K_min]
+    k = max(unit, K_min) * 2
+    while k < K_max:
+        ks.append(k // unit * unit)
+        k *= 2
+    if K_max != K_min:
+        ks.append(K_max)
+    return ks
+
+
+def _variants(off, path_b, bm_list=((128, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4))):
+    out = [dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=bm, force_n_tile=bn, force_waves=w)
+           for bm, bn, w in bm_list]
+    out.append(dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K_min,K_max,a,c", [(2048, 2048, 1024, 8192, "f16", "f16"),
+                                                 (4096, 4096, 128, 512, "i8", "i32"),
+                                                 (16, 4096, 128, 4096, "bf16", "bf16"),
+                                                 (300, 200, 96, 1000, "f16", "f16")])
+def test_plan_range_minimises_the_worst_ratio(off, M, N, K_min, K_max, a, c):
+    # brute force over every variant: plan each sample with the variant pinned
+    unit = 32 if a == "i8" else 16
+    K_max = K_max // unit * unit
+    ks = _range_samples(K_min, K_max, unit)
+    best = [off.plan(M, N, k, a, a, c).est_us for k in ks]
+    worst = {}
+    for v in _variants(off, a):
+        try:
+            worst[(v.force_path, v.force_m_tile, v.force_n_tile, v.force_waves)] = max(
+                off.plan(M, N, k, a, a, c, opts=v).est_us / b for k, b in zip(ks, best))
+        except dg.DGError:
+            pass
+    ro, info, w = off.plan_range(M, N, K_min, K_max, a, a, c)
+    key = (ro.force_path, ro.force_m_tile, ro.force_n_tile, ro.force_waves)
+    assert key in worst and abs(worst[key] - w) < 1e-9
+    assert w <= min(worst.values()) + 1e-9 and w >= 1.0 - 1e-12
+    # the pinned variant plans every K of the range (on the MFMA depth)
+    for k in range(K_min, K_max + 1, max(unit, (K_max - K_min) // 23 // unit * unit)):
+        p = off.plan(M, N, k, a, a, c, opts=ro)
+        assert p.kernel_name.decode() == info.kernel_name.decode() or ro.force_path == dg.DG_PATH_SKINNY
+
+
+def test_plan_range_of_one_k_is_the_plan(off):
+    for M, N, K in ((4096, 4096, 4096), (1, 4096, 131072), (600, 520, 256)):
+        ro, info, w = off.plan_range(M, N, K, K)
+        assert info.kernel_name.decode() == off.plan(M, N, K).kernel_name.decode() and w == 1.0
+
+
+def test_plan_range_errors(off):
+    dt, lay = dg.Handle.problem("f16", "f16", "f16")
+    ro, info, w = dg.dg_plan_opts(), dg.dg_plan_info(), C.c_double()
+    args = lambda kmin, kmax, o=None, r=C.byref(ro): (off.h, 256, 256, kmin, kmax, C.byref(dt), C.byref(lay), 0, 0,
+                                                      C.byref(o) if o is not None else None, r, C.byref(info),
+                                                      C.byref(w))
+    assert dg.dg_plan_range(*args(512, 128)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_plan_range(*args(-16, 128)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_plan_range(*args(128, 512, r=None)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_plan_range(*args(128, 500)) == dg.DG_ERR_ALIGNMENT
+    # with pad_k any K, but rows keep 16-byte leading dimensions (lda = 512 here)
+    dt2, lay2 = dg.Handle.problem("f16", "f16", "f16", lda=512)
+    assert dg.dg_plan_range(off.h, 256, 256, 128, 500, C.byref(dt2), C.byref(lay2), 0, 0,
+                            C.byref(dg.dg_plan_opts(pad_k=1)), C.byref(ro), C.byref(info), C.byref(w)) == dg.DG_OK
+    assert dg.dg_plan_range(*args(128, 500, dg.dg_plan_opts(pad_k=1))) == dg.DG_ERR_ALIGNMENT
+    assert dg.dg_plan_range(*args(128, 512, dg.dg_plan_opts(force_m_tile=128))) == dg.DG_ERR_CONFLICT
+    assert dg.dg_plan_range(None, 1, 1, 16, 32, C.byref(dt), C.byref(lay), 0, 0, None, C.byref(ro), None,
+                            None) == dg.DG_ERR_INVALID_STATE

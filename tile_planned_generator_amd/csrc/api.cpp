@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -9,6 +10,7 @@
 #include <set>
 #include <string>
 #include <unordered_map>
+#include <vector>
 
 #include "../../include/dg.h"
 #include "catalogue.h"
@@ -381,6 +383,106 @@ dg_status dg_plan(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         return ok();
     } catch (...) {
         return fail(DG_ERR_INTERNAL, "exception in dg_plan");
+    }
+}
+
+dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int64_t K_max, const dg_dtypes *dt,
+                        const dg_layouts *lay, int32_t group_k, int32_t epi_kind, const dg_plan_opts *opts,
+                        dg_plan_opts *range_opts, dg_plan_info *out, double *worst_ratio)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (!range_opts) return fail(DG_ERR_INVALID_ARG, "range_opts is NULL");
+        if (K_min < 0 || K_max < K_min) return fail(DG_ERR_INVALID_ARG, "K range must satisfy 0 <= K_min <= K_max");
+        const dg_plan_opts o = opts_or_default(opts);
+        if (o.force_m_tile || o.force_n_tile || o.force_waves || o.force_path)
+            return fail(DG_ERR_CONFLICT, "a K range plan chooses the variant: leave tile, waves and path free");
+        // every K of the range must be a valid problem; both ends decide that
+        // (alignment and leading dimensions only tighten as K grows or shrinks)
+        Problem lo, hi;
+        dg_status s = describe(M, N, K_min, dt, lay, group_k, epi_kind, 0, o.pad_k, lo);
+        if (s) return s;
+        s = describe(M, N, K_max, dt, lay, group_k, epi_kind, 0, o.pad_k, hi);
+        if (s) return s;
+        // K samples: both ends and the doublings between them, on the MFMA depth
+        // (any K with pad_k)
+        const int64_t unit = o.pad_k ? 1 : (hi.path == P_MX ? 64 : ((hi.path == P_I8 || hi.path == P_E2M1) ? 32 : 16));
+        std::vector<int64_t> ks{K_min};
+        for (int64_t k = std::max<int64_t>(unit, K_min) * 2; k < K_max; k *= 2) ks.push_back(k / unit * unit);
+        if (K_max != K_min) ks.push_back(K_max);
+        std::vector<double> best(ks.size());
+        for (size_t i = 0; i < ks.size(); ++i) {
+            Problem pr;
+            s = describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
+            if (s) return s;
+            PlanResult r = plan_problem(pr, h->desc, o);
+            if (r.status != DG_OK) return fail(r.status, r.message);
+            best[i] = r.pareto.front().est_us;
+        }
+        // candidate variants: each compiled tiled shape of the path, and the
+        // streaming path with its split left to the planner
+        struct Var {
+            dg_plan_opts opt;
+            double worst;
+            int lds;
+        };
+        std::vector<Var> vars;
+        const TiledShape shapes[] = {
+#define DG_TS(path, kmaj, bm, bn, wm, wn) {path, kmaj, bm, bn, wm, wn},
+            DG_TILED_CATALOGUE(DG_TS)
+#undef DG_TS
+        };
+        std::vector<dg_plan_opts> tries;
+        for (const TiledShape &t : shapes) {
+            if (t.path != hi.path || t.b_kmajor != hi.b_kmajor) continue;
+            dg_plan_opts v = o;
+            v.force_path = DG_PATH_TILED;
+            v.force_m_tile = t.bm;
+            v.force_n_tile = t.bn;
+            v.force_waves = t.wm * t.wn;
+            tries.push_back(v);
+        }
+        {
+            dg_plan_opts v = o;
+            v.force_path = DG_PATH_SKINNY;
+            tries.push_back(v);
+        }
+        for (const dg_plan_opts &v : tries) {
+            double worst = 0;
+            int lds = 0;
+            bool ok = true;
+            for (size_t i = 0; i < ks.size() && ok; ++i) {
+                Problem pr;
+                describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
+                PlanResult r = plan_problem(pr, h->desc, v);
+                if (r.status != DG_OK) {
+                    ok = false;
+                    break;
+                }
+                worst = std::max(worst, r.pareto.front().est_us / std::max(best[i], 1e-9));
+                lds = std::max(lds, r.pareto.front().lds);
+            }
+            if (ok) vars.push_back(Var{v, worst, lds});
+        }
+        if (vars.empty()) return fail(DG_ERR_NO_CANDIDATE, "No valid candidate found after pruning for every K of the range");
+        // the smallest worst-case ratio to the best plan of each K; then fewer
+        // LDS bytes; then catalogue order (deterministic)
+        size_t bi = 0;
+        for (size_t i = 1; i < vars.size(); ++i) {
+            const Var &a = vars[i], &b = vars[bi];
+            if (a.worst < b.worst - 1e-12 || (std::abs(a.worst - b.worst) <= 1e-12 && a.lds < b.lds)) bi = i;
+        }
+        *range_opts = vars[bi].opt;
+        if (worst_ratio) *worst_ratio = vars[bi].worst;
+        if (out) {
+            Candidate c;
+            s = plan_cached(h, hi, vars[bi].opt, c);
+            if (s) return s;
+            fill_info(c, out);
+        }
+        return ok();
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_plan_range");
     }
 }
 

@@ -85,7 +85,7 @@ class dg_plan_info(C.Structure):
 
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
-           "dg_plan_candidates", "dg_gemm", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
+           "dg_plan_candidates", "dg_plan_range", "dg_gemm", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
            "dg_probe", "dg_set_device_desc", "dg_last_error", "dg_status_str")
 
 _lib = None
@@ -111,6 +111,9 @@ def load():
         "dg_plan_candidates": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), i32,
                                 i32, C.POINTER(dg_plan_opts), C.POINTER(dg_plan_info), i32,
                                 C.POINTER(i32)], S),
+        "dg_plan_range": ([H, i64, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), i32, i32,
+                           C.POINTER(dg_plan_opts), C.POINTER(dg_plan_opts), C.POINTER(dg_plan_info),
+                           C.POINTER(C.c_double)], S),
         "dg_gemm": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), P, P, P, i32,
                      P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t,
                      P], S),
@@ -154,6 +157,10 @@ def dg_plan(*a):
 
 def dg_plan_candidates(*a):
     return load().dg_plan_candidates(*a)
+
+
+def dg_plan_range(*a):
+    return load().dg_plan_range(*a)
 
 
 def dg_gemm(*a):
@@ -323,6 +330,20 @@ class Handle:
         check(dg_plan(self.h, M, N, K, C.byref(dt), C.byref(lay), group_k or (32 if b == "e2m1" else 0),
                       EPI[epilogue], C.byref(opts) if opts is not None else None, C.byref(info)))
         return info
+
+    def plan_range(self, M, N, K_min, K_max, a="f16", b="f16", c="f16", b_layout=None, epilogue="none",
+                   group_k=0, opts=None, **ld):
+        """dg_plan_range: (options pinning the variant for every K in the range,
+        plan info at K_max, worst estimated-time ratio)."""
+        if b_layout is None:
+            b_layout = DG_COL_MAJOR if b == "e2m1" else DG_ROW_MAJOR
+        dt, lay = self.problem(a, b, c, b_layout, **ld)
+        ro, info, worst = dg_plan_opts(), dg_plan_info(), C.c_double()
+        check(dg_plan_range(self.h, M, N, K_min, K_max, C.byref(dt), C.byref(lay),
+                            group_k or (32 if b in ("e2m1",) else 0), EPI[epilogue],
+                            C.byref(opts) if opts is not None else None, C.byref(ro), C.byref(info),
+                            C.byref(worst)))
+        return ro, info, worst.value
 
     def candidates(self, M, N, K, a="f16", b="f16", c="f16", b_layout=None, epilogue="none",
                    group_k=0, opts=None, cap=64, **ld):
