@@ -393,6 +393,21 @@ def test_errors_on_device_handle(h):
     assert e.value.status == dg.DG_ERR_ALIGNMENT
 
 
+def test_operand_of_4_gib_is_refused_by_the_tiled_path(h):
+    # The tiled kernels address operands with 32-bit offsets: an A of exactly
+    # 4 GiB (32 rows of 2^26 fp16) is refused before anything is launched (the
+    # operands are real allocations, so even a launch would stay inside them).
+    K = 1 << 26
+    A = torch.empty(32, K, dtype=torch.float16, device=DEV)
+    B = torch.empty(K, 16, dtype=torch.float16, device=DEV)
+    Cd = torch.empty(32, 16, dtype=torch.float16, device=DEV)
+    with pytest.raises(dg.DGError) as e:
+        h.gemm(A, B, Cd, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_TILED))
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED and "4 GiB" in str(e.value)
+    del A, B, Cd
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------ full-size workloads
 def _sample(n, k, seed):
     g = torch.Generator().manual_seed(seed)
