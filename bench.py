@@ -80,7 +80,7 @@ class Prepared:
         self.A = t["A"].contiguous()
         if w.path == "e2m1":
             B0 = dg.pack_e2m1(t["codes"])
-            S0 = dg.scales_nk(t["scale"])
+            S0 = dg.scales_gn(t["scale"])
             b_bytes = B0.numel() + S0.numel() * 2
         else:
             B0 = t["B"].contiguous()

@@ -258,7 +258,10 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
  *   A       device, M x K (lda)
  *   B       device, K x N row-major (ldb) or N x K column-major (ldb); e2m1: two
  *           codes per byte, even k in the low nibble, N x K column-major
- *   b_scale e2m1 only: device fp16, [N][K/group_k] (column n's scales contiguous)
+ *   b_scale e2m1 only: device fp16, group-major [K/group_k][ldsc] with ldsc = N
+ *           rounded up to even (scale of group g, column n at g * ldsc + n: a
+ *           K step's scales for consecutive columns are contiguous); 4-byte
+ *           aligned
  *   group_k e2m1 only: 32
  *   D       device, M x N (ldd); read only when *beta != 0, may be NULL otherwise
  *   C       device, M x N (ldc)

@@ -61,7 +61,7 @@ def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, ro
     scale = None
     if w.path == "e2m1":
         Bd = to_dev(dg.pack_e2m1(t["codes"]), pad)
-        scale = dg.scales_nk(t["scale"]).to(DEV)
+        scale = dg.scales_gn(t["scale"]).to(DEV)
         layout = dg.DG_COL_MAJOR
     elif b_colmajor:
         Bd = to_dev(t["B"].t().contiguous(), pad)
@@ -167,7 +167,7 @@ def test_e2m1_one_hot_decode_is_exact(h):
     gold = oracle.e2m1_values(codes.numpy()) * sc.double().numpy()[np.arange(K) // 32]
     for opts in (dg.dg_plan_opts(force_path=dg.DG_PATH_TILED), None):
         Cd = torch.empty(M, N, dtype=torch.float16, device=DEV)
-        h.gemm(A.to(DEV), dg.pack_e2m1(codes).to(DEV), Cd, b_scale=dg.scales_nk(sc).to(DEV),
+        h.gemm(A.to(DEV), dg.pack_e2m1(codes).to(DEV), Cd, b_scale=dg.scales_gn(sc).to(DEV),
                opts=opts)
         torch.cuda.synchronize()
         assert np.array_equal(Cd.cpu().double().numpy(), gold)
@@ -175,7 +175,7 @@ def test_e2m1_one_hot_decode_is_exact(h):
     for k in (0, 1, 33, 62):
         Cd = torch.empty(1, N, dtype=torch.float32, device=DEV)
         h.gemm(A[k:k + 1].contiguous().to(DEV), dg.pack_e2m1(codes).to(DEV), Cd,
-               b_scale=dg.scales_nk(sc).to(DEV))
+               b_scale=dg.scales_gn(sc).to(DEV))
         torch.cuda.synchronize()
         assert np.array_equal(Cd.cpu().double().numpy()[0], gold[k])
 

@@ -556,8 +556,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         if ((A && !aligned(A, 16)) || (B && !aligned(B, 16)))
             return fail(DG_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
         const int osz = elt_size(pr.out_type);
-        if (!aligned(C, osz) || (D && !aligned(D, osz)) || (b_scale && !aligned(b_scale, 2)))
-            return fail(DG_ERR_ALIGNMENT, "C, D or b_scale is misaligned for its type");
+        if (!aligned(C, osz) || (D && !aligned(D, osz)) || (b_scale && !aligned(b_scale, 4)))
+            return fail(DG_ERR_ALIGNMENT, "C or D is misaligned for its type, or b_scale is not 4-byte aligned");
         dg_layouts L{};
         if (lay) L = *lay;
         // plan
@@ -570,7 +570,8 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             const int64_t ea = (pr.path == P_I8 || pr.path == P_MX) ? 1 : 2;
             const int64_t eb = pr.path == P_E2M1 ? 1 : ea;   // e2m1: ldb counts codes, 2 per byte
             const int64_t b_ext = pr.b_kmajor ? N * lb * eb / (pr.path == P_E2M1 ? 2 : 1) : K * lb * eb;
-            if (M * la * ea >= (int64_t(1) << 32) || b_ext >= (int64_t(1) << 32))
+            if (M * la * ea >= (int64_t(1) << 32) || b_ext >= (int64_t(1) << 32) ||
+                (pr.path == P_E2M1 && (K / 32) * (N + (N & 1)) * 2 >= (int64_t(1) << 32)))
                 return fail(DG_ERR_UNSUPPORTED, "an operand spans 4 GiB or more (32-bit offsets of the tiled path)");
         }
         if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
@@ -610,7 +611,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             ta.scale = b_scale;
             ta.lda = lda;
             ta.ldb = ldb;
-            ta.ld_scale = K / 32;
+            ta.ld_scale = N + (N & 1);   // e2m1 scales: group rows of N rounded up to even
             ta.M = (int)M;
             ta.N = (int)N;
             ta.K = (int)pr.K;
@@ -631,7 +632,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             sa.scale = b_scale;
             sa.lda = lda;
             sa.ldb = ldb;
-            sa.ld_scale = K / 32;
+            sa.ld_scale = N + (N & 1);
             sa.M = (int)M;
             sa.N = (int)N;
             sa.K = (int)pr.K;

@@ -39,7 +39,8 @@ struct EpiArgs {
 // Tiled MFMA GEMM.
 struct TiledArgs {
     const void *A, *B, *scale;
-    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1; ld_scale in bytes for MX)
+    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1; e2m1 scales: elements per group
+                                  // row; MX: bytes per column)
     const void *scale_a;          // MX: A's e8m0 scales [M][K/32]
     int64_t ld_scale_a;           // MX: bytes between rows of scale_a (a multiple of 4)
     int M, N, K;

@@ -31,7 +31,8 @@
 //     direct-to-LDS load and would wait for all of them before each read.  Their
 //     completion is awaited explicitly, tied to the fragment registers.
 //   - e2m1 codes are staged packed (two per byte), 16 bytes per column and step,
-//     with the dword holding the column's fp16 group scale, and decoded to fp16
+//     with the column's fp16 group scale (the step's scales are contiguous in
+//     the group-major scale array: whole-dword loads), and decoded to fp16
 //     when the fragment is read (v_cvt_scalef32_pk_f16_fp4 with a unit scale,
 //     then a packed fp16 multiply by the group scale).
 //   - MX (fp8 e4m3 A, e2m1 B, one e8m0 scale per 32 k on each): the operands
@@ -143,7 +144,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int A_BYTES = BM * 64;                    // one A region
     constexpr int A_ALL = A_REG * A_BYTES;
     constexpr int B_TILE = IS_E2M1 ? BN * 16 : BN * 64;   // e2m1: BKE/2 bytes of codes per column
-    constexpr int S_BYTES = IS_E2M1 ? BN * 4 : (IS_MX ? (BM + BN) * 4 : 0);   // scale dwords
+    // scales: e2m1 one fp16 per column (whole 256-byte loads), MX one dword per
+    // row of A and per column of B
+    constexpr int S_BYTES = IS_E2M1 ? (BN * 2 + 255) / 256 * 256 : (IS_MX ? (BM + BN) * 4 : 0);
     constexpr int STAGE = A_ALL + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
@@ -216,19 +219,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         Bbase = reinterpret_cast<const char *>(p.B) + (int64_t)n0 * ESZ;
         b_bytes = (uint32_t)((p.K - 1) * (int64_t)ldb_b + (nr - n0) * ESZ);
     }
-    // e2m1 scales: fp16 scale (n, g) sits at element n * ld_scale + g.  They are
-    // fetched as the aligned dword that holds them, from a descriptor based at
-    // the scale pointer rounded down to 4 bytes; `smis` is the byte distance
-    // of the pointer from that base (0 or 2).  The range is rounded up to whole
-    // dwords: the last dword never leaves the 4-byte word holding the array's end.
+    // e2m1 scales: group-major, fp16 scale (g, n) at element g * ld_scale + n
+    // (ld_scale even, the pointer 4-byte aligned), so a K step's scales for the
+    // tile's columns are contiguous and are fetched as whole dwords, two
+    // columns each.  The range is the whole array: columns past N read the next
+    // group's (discarded) or zeros.
     const char *Sbase = nullptr;
-    uint32_t s_bytes = 0, smis = 0;
+    uint32_t s_bytes = 0;
     if constexpr (IS_E2M1) {
-        const uintptr_t sp = reinterpret_cast<uintptr_t>(p.scale);
-        smis = (uint32_t)(sp & 3);
-        Sbase = reinterpret_cast<const char *>(sp - smis);
-        const int64_t last = (int64_t)(N - 1) * p.ld_scale + p.K / 32;   // one past the last element
-        s_bytes = (uint32_t)((smis + 2 * last + 3) & ~(int64_t)3);
+        Sbase = reinterpret_cast<const char *>(p.scale);
+        s_bytes = (uint32_t)((int64_t)(p.K / 32) * p.ld_scale * 2);
     }
     // MX scales: e8m0 bytes, row r of A at scale_a + r * ld_scale_a, column n of
     // B at scale + n * ld_scale (both pitches multiples of 4, both pointers
@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const int col = (i * NW + swave) * 64 + lane;   // byte of scale (n0 + col, 0) from Sbase
         if constexpr (IS_MX)   // entries [0, BM): rows of A; [BM, BM + BN): columns of B
             os[i] = col < BM ? (uint32_t)((m0 + col) * p.ld_scale_a) : (uint32_t)((n0 + col - BM) * p.ld_scale);
-        else
-            os[i] = smis + 2 * (uint32_t)((n0 + col) * p.ld_scale);
+        else   // e2m1: dword `col` of the stage holds columns 2 col and 2 col + 1
+            os[i] = 2 * (uint32_t)(n0 + 2 * col);
     }
 
     // Issue the loads of step j (k0 = kbeg + j * BKE) into LDS stage j % NBUF.
@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const int q = i - A_LD - B_LD;
             if (S_NL % NW == 0 || q * NW + swave < S_NL) {   // wave-uniform
                 const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sbase, real ? s_bytes : 0u);
-                buf_ld4_lds(rS, (os[q] + 2 * (uint32_t)(k0 >> 5)) & ~3u,
+                buf_ld4_lds(rS, os[q] + 2 * (uint32_t)(k0 >> 5) * (uint32_t)p.ld_scale,
                             sb + A_BYTES + B_TILE + (q * NW + swave) * 256);
             }
         }
@@ -380,11 +380,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             boff[ni] = 0;
         }
     }
-    // e2m1: parity of the scale's half within its dword, at group 0
-    uint32_t spar[FN];
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni)
-        spar[ni] = IS_E2M1 ? ((smis >> 1) + (uint32_t)((n0 + wn * WTN + ni * 32 + lr) * p.ld_scale)) & 1u : 0u;
 
     // One fragment read: A block mi, or B block ni, of substep s of stage buf.
     auto read_a = [&](int buf, auto s_tag, int mi, Frag &f) {
@@ -432,8 +427,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const int row = col0 + lr;
             if constexpr (s == 0) {
                 const u32x4 raw = *reinterpret_cast<const u32x4 *>(sB + row * 16);
-                const unsigned sd = *reinterpret_cast<const unsigned *>(sB + B_TILE + row * 4);
-                const unsigned sh = ((spar[ni] ^ (unsigned)g) & 1u) ? sd >> 16 : sd & 0xffffu;
+                const unsigned sh = *reinterpret_cast<const unsigned short *>(sB + B_TILE + row * 2);
                 f.b[ni] = u32x4{kg ? raw.y : raw.x, sh, 0u, 0u};
                 e2_next[ni] = kg ? raw.w : raw.z;
                 e2_sh[ni] = sh;

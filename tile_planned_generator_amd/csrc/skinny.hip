@@ -240,7 +240,8 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
 }
 
 // ----------------------------------------------------------------- e2m1 path
-// B codes stored N x K (K contiguous, even k in the low nibble), scales N x G.
+// B codes stored N x K (K contiguous, even k in the low nibble), scales G x N
+// (group-major, ld_scale per group).
 // Four columns per wave, 16 lanes each (16 columns per workgroup); lane q of a
 // column takes the 32-code groups q, q+16, ... of the slice: one 16-byte load of
 // codes, one fp16 scale, the group's dot product with A in fp32
@@ -270,7 +271,7 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
     const int M = p.M;
 
     const char *Bc = reinterpret_cast<const char *>(p.B) + (int64_t)nc * (p.ldb / 2);
-    const _Float16 *S = reinterpret_cast<const _Float16 *>(p.scale) + (int64_t)nc * p.ld_scale;
+    const _Float16 *S = reinterpret_cast<const _Float16 *>(p.scale) + nc;   // group g at S[g * ld_scale]
     const _Float16 *A = reinterpret_cast<const _Float16 *>(p.A);
 
     u32x4 c[GU];
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
             const bool in = gi < gend;
             gcs[u] = in ? gi : gbeg;   // a valid group; its terms are dropped below
             c[u] = ld16_nt(Bc + (int64_t)gcs[u] * 16);
-            sc[u] = in ? (float)S[gcs[u]] : 0.f;
+            sc[u] = in ? (float)S[(int64_t)gcs[u] * p.ld_scale] : 0.f;
         }
     };
     if (gbeg + q < gend) load_groups(gbeg + q);

@@ -221,9 +221,16 @@ def pack_e2m1(codes_kn):
     return (t[:, 0::2] & 0xF) | ((t[:, 1::2] & 0xF) << 4)
 
 
-def scales_nk(scale_gn):
-    """Logical group scales [K/32][N] -> device layout [N][K/32]."""
-    return scale_gn.t().contiguous()
+def scales_gn(scale_gn):
+    """Logical group scales [K/32][N] -> device layout: group-major rows of N
+    rounded up to even (the padding column is zero), contiguous."""
+    import torch
+    G, N = scale_gn.shape
+    if N % 2 == 0:
+        return scale_gn.contiguous()
+    out = torch.zeros(G, N + 1, dtype=scale_gn.dtype, device=scale_gn.device)
+    out[:, :N] = scale_gn
+    return out
 
 
 # ------------------------------------------------------------ torch wrapper
@@ -365,7 +372,8 @@ class Handle:
 
         A: [M, K] (row-major, rows may be padded: A.stride(0) is lda).
         B: [K, N] row-major, or, with b_layout=DG_COL_MAJOR, [N, K]; for e2m1 the
-           packed codes [N, K/2] (uint8) with ``b_scale`` [N, K/32] fp16.
+           packed codes [N, K/2] (uint8) with ``b_scale`` the group-major fp16
+           scales of scales_gn ([K/32][N rounded up to even]).
         Returns the plan info.  ``workspace``: a device tensor of at least the
         planned bytes (allocated here when None and the plan needs one).
         """
