@@ -151,17 +151,17 @@ class PreparedMx:
             self.R = -(-CACHE_BYTES // per) if rotate and per < CACHE_BYTES else 1
             self.Xs = [X0] + [X0.clone() for _ in range(self.R - 1)]
             self.Qs = [torch.empty(M, K, dtype=torch.uint8, device=dev) for _ in range(self.R)]
-            self.Ss = [torch.empty(M, G, dtype=torch.uint8, device=dev) for _ in range(self.R)]
+            self.Ss = [torch.empty(G, M, dtype=torch.uint8, device=dev) for _ in range(self.R)]   # group-major
             self.C = self.Qs[0]
             self.info = None
             self.fn = self.lib.dg_quant_mx
             self.args = [(h.h, M, K, self.Xs[i].data_ptr(), K, self.Qs[i].data_ptr(), K,
-                          self.Ss[i].data_ptr(), G, self.stream) for i in range(self.R)]
+                          self.Ss[i].data_ptr(), M, self.stream) for i in range(self.R)]
             return
         self.A = t["A"].contiguous()
-        self.SA = t["SA"].contiguous()
+        self.SA = t["SA"].t().contiguous()          # group-major [K/32][M]
         B0 = dg.pack_e2m1(t["codes"])
-        S0 = t["SB"].t().contiguous()
+        S0 = t["SB"].contiguous()                   # group-major [K/32][N]
         per = B0.numel() + S0.numel()
         self.R = -(-CACHE_BYTES // per) if rotate and per < CACHE_BYTES else 1
         self.Bs = [B0] + [B0.clone() for _ in range(self.R - 1)]
@@ -172,8 +172,8 @@ class PreparedMx:
                    if self.info.workspace_bytes else None)
         self.epi = dg.dg_epilogue(dg.EPI[w.epilogue], 0, None, 1.0)
         self.fn = self.lib.dg_gemm_mx
-        self.args = [(h.h, M, N, K, self.A.data_ptr(), K, self.SA.data_ptr(), G, self.Bs[i].data_ptr(),
-                      K, self.Ss[i].data_ptr(), G, self.C.data_ptr(), dg.DG_F16, N, C.c_float(w.alpha),
+        self.args = [(h.h, M, N, K, self.A.data_ptr(), K, self.SA.data_ptr(), M, self.Bs[i].data_ptr(),
+                      K, self.Ss[i].data_ptr(), N, self.C.data_ptr(), dg.DG_F16, N, C.c_float(w.alpha),
                       C.byref(self.epi), None, self.ws.data_ptr() if self.ws is not None else None,
                       self.ws.numel() if self.ws is not None else 0, self.stream)
                      for i in range(self.R)]

@@ -288,19 +288,22 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
  * (v_mfma_scale_f32_32x32x64_f8f6f4) without a decode step.  The element and
  * scale formats are those of the OCP Microscaling (MX) v1.0 specification:
  *   C[i][j] = act( alpha * sum_k a[i][k] * w[k][j] + bias[j] )
- *   a[i][k] = e4m3(A[i][k]) * 2^(a_scale[i][k/32] - 127)
- *   w[k][j] = e2m1(B[j][k]) * 2^(b_scale[j][k/32] - 127)
+ *   a[i][k] = e4m3(A[i][k]) * 2^(a_scale[k/32][i] - 127)
+ *   w[k][j] = e2m1(B[j][k]) * 2^(b_scale[k/32][j] - 127)
  * accumulated in fp32 (products and block sums inside the MFMA, then fp32
  * additions along K), rounded once to C's type.
  *   A          device, fp8 e4m3 codes, M x K row-major, lda bytes (0: K); 16-byte
  *              aligned, lda a multiple of 16
- *   a_scale    device, e8m0 codes [M][K/32], lda_scale bytes per row (0: K/32
- *              rounded up to a multiple of 4); 4-byte aligned, lda_scale a
- *              multiple of 4
+ *   a_scale    device, e8m0 codes, group-major [K/32][lda_scale] (the scale of
+ *              row i, block g at g * lda_scale + i: a K step's scales for
+ *              consecutive rows are contiguous), lda_scale >= M (0: M rounded up
+ *              to a multiple of 4); 4-byte aligned, lda_scale a multiple of 4
  *   B          device, e2m1 codes N x K (K contiguous), two per byte with even k
  *              in the low nibble, ldb in codes (0: K, a multiple of 32); 16-byte
  *              aligned
- *   b_scale    device, e8m0 codes [N][K/32], ldb_scale bytes (as lda_scale)
+ *   b_scale    device, e8m0 codes, group-major [K/32][ldb_scale] (column n,
+ *              block g at g * ldb_scale + n), ldb_scale >= N (0: N rounded up to
+ *              a multiple of 4); as a_scale
  *   C          device, M x N row-major, ldc elements (0: N), c_type F16 or F32
  *   alpha      the product's multiplier
  *   epi        NULL or DG_EPI_NONE / BIAS / GELU_ERF / BIAS_GELU_ERF (bias F16,
@@ -326,7 +329,8 @@ dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K,
  *   X        device binary16, M x K row-major, ldx elements (0: K); 16-byte
  *            aligned rows
  *   codes    device, M x K bytes, ldq bytes per row (0: K); 16-byte aligned rows
- *   scales   device, [M][K/32] bytes, ld_scale bytes per row (0: K/32)
+ *   scales   device, group-major [K/32][ld_scale] bytes (block g of row i at
+ *            g * ld_scale + i: the layout dg_gemm_mx takes), ld_scale >= M (0: M)
  * K must be a multiple of 32 (DG_ERR_ALIGNMENT).  Enqueues one kernel on
  * `stream`.  Errors: DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG,
  * DG_ERR_UNSUPPORTED, DG_ERR_ALIGNMENT, DG_ERR_HIP. */

@@ -38,19 +38,19 @@ def padded(t, ld, fill=0):
 
 
 def mx_operands(M, N, K, seed=601, pad=0, scale_fill=0xFF):
-    """Seeded MX inputs: (host A, SA, codes [K][N], SB [K/32][N]) and their
-    device layouts (A [M][K], SA [M][ld], B packed [N][K/2], SB [N][ld]).  Scale
-    rows are padded to a multiple of 4 bytes (plus `pad`), the padding holding
-    the NaN scale code, which no output may see."""
+    """Seeded MX inputs: (host A, SA [M][K/32], codes [K][N], SB [K/32][N]) and
+    their device layouts (A [M][K], SA group-major [K/32][lda], B packed [N][K/2],
+    SB group-major [K/32][ldb]).  Scale rows are padded to a multiple of 4 bytes
+    (plus `pad`), the padding holding the NaN scale code, which no output may
+    see."""
     w = synth.make("mx_4096x4096x4096", M=M, N=N, K=K, seed=seed)
     t = w.tensors
-    G = K // 32
-    lds = (G + 3) // 4 * 4 + pad
+    r4 = lambda n: (n + 3) // 4 * 4
     r16 = lambda n: (n + 15) // 16 * 16            # code rows start on 16-byte boundaries
     A = padded(t["A"], r16(K + pad))
-    SA = padded(t["SA"], lds, scale_fill)
+    SA = padded(t["SA"].t().contiguous(), r4(M) + r4(pad), scale_fill)
     B = padded(dg.pack_e2m1(t["codes"]), r16(K // 2 + pad))
-    SB = padded(t["SB"].t().contiguous(), lds, scale_fill)
+    SB = padded(t["SB"].contiguous(), r4(N) + r4(pad), scale_fill)
     host = (t["A"].numpy(), t["SA"].numpy(), t["codes"].numpy(), t["SB"].numpy())
     return host, (A, SA, B, SB)
 
@@ -80,15 +80,17 @@ def run_mx(h, M, N, K, *, seed=601, pad=0, opts=None, out=torch.float16, alpha=1
 
 # ------------------------------------------------------------------ quantiser
 def quant_gpu(h, X, pad=0):
+    """Codes [M][K] and scales as [M][K/32] (the device layout is group-major,
+    [K/32][ld >= M]; transposed back here to compare with the oracle)."""
     M, K = X.shape
     Xd = padded(X, K + (pad + 7) // 8 * 8) if pad else X.to(DEV).contiguous()
     codes = padded(torch.zeros(M, K, dtype=torch.uint8), K + (pad + 15) // 16 * 16, 0xAA) if pad else \
         torch.full((M, K), 0xAA, dtype=torch.uint8, device=DEV)
-    scales = padded(torch.zeros(M, K // 32, dtype=torch.uint8), K // 32 + pad, 0xAA) if pad else \
-        torch.full((M, K // 32), 0xAA, dtype=torch.uint8, device=DEV)
+    scales = padded(torch.zeros(K // 32, M, dtype=torch.uint8), M + pad, 0xAA) if pad else \
+        torch.full((K // 32, M), 0xAA, dtype=torch.uint8, device=DEV)
     h.quant_mx(Xd, codes, scales)
     torch.cuda.synchronize()
-    return codes.cpu().numpy(), scales.cpu().numpy()
+    return codes.cpu().numpy(), scales.t().contiguous().cpu().numpy()
 
 
 @pytest.mark.parametrize("M,K,pad", [(37, 96, 0), (64, 320, 5), (1, 32, 0)])
@@ -196,9 +198,9 @@ def test_gemm_mx_empty_k(h):
     bias = synth.to_storage(synth.uniform(3, N, -0.1, 0.1), torch.float16).to(DEV)
     Cd = torch.full((M, N), 7, dtype=torch.float16, device=DEV)
     h.gemm_mx(torch.zeros(M, 16, dtype=torch.uint8, device=DEV)[:, :0],
-              torch.zeros(M, 4, dtype=torch.uint8, device=DEV),
+              torch.zeros(0, M, dtype=torch.uint8, device=DEV),
               torch.zeros(N, 16, dtype=torch.uint8, device=DEV)[:, :0],
-              torch.zeros(N, 4, dtype=torch.uint8, device=DEV), Cd, epilogue="bias", bias=bias)
+              torch.zeros(0, N, dtype=torch.uint8, device=DEV), Cd, epilogue="bias", bias=bias)
     torch.cuda.synchronize()
     assert torch.equal(Cd.cpu(), bias.cpu().expand(M, N))
 
@@ -210,8 +212,11 @@ def test_gemm_mx_rejects_bad_arguments(h):
         h.gemm_mx(A[:, :96], SA, B[:, :48], SB, C)
     assert e.value.status == dg.DG_ERR_ALIGNMENT
     with pytest.raises(dg.DGError) as e:     # scale rows not a multiple of 4 bytes
-        h.gemm_mx(A, SA[:, :3].contiguous(), B, SB, C, K=96 + 32)
-    assert e.value.status in (dg.DG_ERR_ALIGNMENT, dg.DG_ERR_INVALID_ARG)
+        h.gemm_mx(A, torch.zeros(4, 65, dtype=torch.uint8, device=DEV), B, SB, C)
+    assert e.value.status == dg.DG_ERR_ALIGNMENT
+    with pytest.raises(dg.DGError) as e:     # scale rows shorter than M
+        h.gemm_mx(A, torch.zeros(4, 60, dtype=torch.uint8, device=DEV), B, SB, C)
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
     with pytest.raises(dg.DGError) as e:
         h.gemm_mx(A, SA, B, SB, torch.empty(64, 64, dtype=torch.int32, device=DEV))
     assert e.value.status == dg.DG_ERR_UNSUPPORTED
@@ -235,10 +240,10 @@ def test_quant_then_gemm_end_to_end(h):
     w = synth.make("mx_4096x4096x4096", M=M, N=N, K=K, seed=612).tensors
     G = K // 32
     codes = torch.empty(M, K, dtype=torch.uint8, device=DEV)
-    scales = torch.empty(M, (G + 3) // 4 * 4, dtype=torch.uint8, device=DEV)
-    h.quant_mx(X.to(DEV), codes, scales[:, :G])
+    scales = torch.empty(G, (M + 3) // 4 * 4, dtype=torch.uint8, device=DEV)   # group-major
+    h.quant_mx(X.to(DEV), codes, scales[:, :M])
     B = dg.pack_e2m1(w["codes"]).to(DEV)
-    SB = padded(w["SB"].t().contiguous(), (G + 3) // 4 * 4)
+    SB = padded(w["SB"].contiguous(), (N + 3) // 4 * 4)
     Cd = torch.empty(M, N, dtype=torch.float16, device=DEV)
     h.gemm_mx(codes, scales, B, SB, Cd)
     torch.cuda.synchronize()

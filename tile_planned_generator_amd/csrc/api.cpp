@@ -702,8 +702,8 @@ dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K, const void 
         const dg_dtypes dt{DG_F8E4M3, DG_E2M1, c_type, DG_F32};
         const int64_t G = K / 32;
         const int64_t la = lda ? lda : K, lb = ldb ? ldb : K;
-        const int64_t lsa = lda_scale ? lda_scale : (G + 3) / 4 * 4;
-        const int64_t lsb = ldb_scale ? ldb_scale : (G + 3) / 4 * 4;
+        const int64_t lsa = lda_scale ? lda_scale : (M + 3) / 4 * 4;   // group-major scale rows
+        const int64_t lsb = ldb_scale ? ldb_scale : (N + 3) / 4 * 4;
         if (lda < 0 || ldb < 0 || lda_scale < 0 || ldb_scale < 0 || ldc < 0)
             return fail(DG_ERR_INVALID_ARG, "negative leading dimension");
         const dg_layouts L{DG_ROW_MAJOR, DG_COL_MAJOR, la, lb, ldc ? ldc : N, N};
@@ -712,7 +712,8 @@ dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K, const void 
         Problem pr;
         dg_status s = describe(M, N, K, &dt, &L, 32, E.kind, 0, 0, pr);
         if (s) return s;
-        if (lsa < G || lsb < G) return fail(DG_ERR_INVALID_ARG, "a scale leading dimension is smaller than K/32");
+        if (K > 0 && (lsa < M || lsb < N))
+            return fail(DG_ERR_INVALID_ARG, "a scale leading dimension is smaller than M (a_scale) or N (b_scale)");
         int cur = -1;
         if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
             return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
@@ -737,8 +738,8 @@ dg_status dg_gemm_mx(dg_handle_t h, int64_t M, int64_t N, int64_t K, const void 
         s = plan_cached(h, pr, o, c);
         if (s) return s;
         if (c.family != F_TILED) return fail(DG_ERR_INTERNAL, "MX plan is not a tiled plan");
-        if (M * la >= (int64_t(1) << 32) || N * lb / 2 >= (int64_t(1) << 32) || M * lsa >= (int64_t(1) << 32) ||
-            N * lsb >= (int64_t(1) << 32))
+        if (M * la >= (int64_t(1) << 32) || N * lb / 2 >= (int64_t(1) << 32) || G * lsa >= (int64_t(1) << 32) ||
+            G * lsb >= (int64_t(1) << 32))
             return fail(DG_ERR_UNSUPPORTED, "an operand spans 4 GiB or more (32-bit offsets of the tiled path)");
         if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
             return fail(DG_ERR_WORKSPACE, "workspace missing or smaller than " + std::to_string(c.ws_bytes) + " bytes");
@@ -808,8 +809,8 @@ dg_status dg_quant_mx(dg_handle_t h, int64_t M, int64_t K, const void *X, int64_
             return fail(DG_ERR_INVALID_ARG, "negative size or leading dimension");
         if (M > INT32_MAX || K > INT32_MAX) return fail(DG_ERR_UNSUPPORTED, "sizes above 2^31-1 are not supported");
         if (K % 32) return fail(DG_ERR_ALIGNMENT, "K is not a multiple of the 32-value scale block");
-        const int64_t lx = ldx ? ldx : K, lq = ldq ? ldq : K, ls = ld_scale ? ld_scale : K / 32;
-        if (lx < K || lq < K || ls < K / 32) return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
+        const int64_t lx = ldx ? ldx : K, lq = ldq ? ldq : K, ls = ld_scale ? ld_scale : M;
+        if (lx < K || lq < K || ls < M) return fail(DG_ERR_INVALID_ARG, "a leading dimension is smaller than the matrix");
         int cur = -1;
         if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
             return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");

@@ -89,11 +89,11 @@ constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
 // K-contiguous B take 64 bytes per row (per column of B), a row-major B 64 bytes
 // per column (BN columns of a 32-k or 64-k step); e2m1 B takes 16 bytes of codes
 // per column plus the step's fp16 scales (whole 256-byte loads).  MX: two 64-byte rows of fp8 A per tile
-// row, 64 bytes of e2m1 codes per column, and one dword of four e8m0 scales per
-// row of A and per column of B.
+// row, 64 bytes of e2m1 codes per column, and 2 KB of e8m0 scales (a 256-byte
+// chunk per operand and group of the step).
 constexpr int tiled_stage_bytes(int path, int bm, int bn)
 {
-    return path == 4 ? bm * 128 + bn * 64 + (bm + bn) * 4
+    return path == 4 ? bm * 128 + bn * 64 + 2048
          : bm * 64 + (path == 3 ? bn * 16 + (bn * 2 + 255) / 256 * 256 : bn * 64);
 }
 // LDS stages: five for the eight-wave variants when they fit gfx950's 160 KB

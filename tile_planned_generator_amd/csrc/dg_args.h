@@ -39,10 +39,10 @@ struct EpiArgs {
 // Tiled MFMA GEMM.
 struct TiledArgs {
     const void *A, *B, *scale;
-    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1; e2m1 scales: elements per group
-                                  // row; MX: bytes per column)
-    const void *scale_a;          // MX: A's e8m0 scales [M][K/32]
-    int64_t ld_scale_a;           // MX: bytes between rows of scale_a (a multiple of 4)
+    int64_t lda, ldb, ld_scale;   // elements (codes for e2m1); ld_scale: per group row of the
+                                  // scales (e2m1: elements; MX: bytes)
+    const void *scale_a;          // MX: A's e8m0 scales, group-major [K/32][ld_scale_a]
+    int64_t ld_scale_a;           // MX: bytes between group rows of scale_a (a multiple of 4)
     int M, N, K;
     int split_k, k_slice;         // K slices; every slice but the last has k_slice
     int tiles_m, tiles_n, group_m;
@@ -74,7 +74,8 @@ struct TailArgs {
 };
 
 // MX quantiser: binary16 X (M x K, ldx elements) -> fp8 e4m3 codes (ldq bytes)
-// and one e8m0 scale per 32 values of a row (ld_scale bytes).
+// and one e8m0 scale per 32 values of a row, group-major (block g of row r at
+// g * ld_scale + r).
 struct QuantMxArgs {
     const void *X;
     void *codes, *scales;

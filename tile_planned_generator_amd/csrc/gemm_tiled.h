@@ -39,9 +39,10 @@
 //     go to the block-scaled MFMA as stored, without decoding.  A step is 128 k:
 //     two 64-byte fp8 rows per tile row (k 0-63 and 64-127 of the step, each
 //     laid out and swizzled like an int8 A row), 64 bytes of codes per column
-//     (laid out like a K-contiguous B), and one dword of four scales per row of
-//     A and per column of B.  The scale register of lane group kg covers k
-//     32kg .. +31 of one MFMA, so a lane's scale is one byte of that dword.
+//     (laid out like a K-contiguous B), and per operand and group a 256-byte
+//     chunk of scales (the scale arrays are group-major, so each chunk is one
+//     contiguous load).  The scale register of lane group kg covers k 32kg .. +31
+//     of one MFMA.
 //   - Accumulators stay in registers for the whole K range (32x32 blocks:
 //     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8,
 //     v_mfma_scale_f32_32x32x64_f8f6f4).
@@ -144,9 +145,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int A_BYTES = BM * 64;                    // one A region
     constexpr int A_ALL = A_REG * A_BYTES;
     constexpr int B_TILE = IS_E2M1 ? BN * 16 : BN * 64;   // e2m1: BKE/2 bytes of codes per column
-    // scales: e2m1 one fp16 per column (whole 256-byte loads), MX one dword per
-    // row of A and per column of B
-    constexpr int S_BYTES = IS_E2M1 ? (BN * 2 + 255) / 256 * 256 : (IS_MX ? (BM + BN) * 4 : 0);
+    // scales: e2m1 one fp16 per column (whole 256-byte loads); MX, per operand
+    // and group of the step, one byte per row of A (column of B) in a 256-byte
+    // chunk: [A g0..g3][B g0..g3]
+    constexpr int S_BYTES = IS_E2M1 ? (BN * 2 + 255) / 256 * 256 : (IS_MX ? 2048 : 0);
+    static_assert(!IS_MX || (BM <= 256 && BN <= 256), "MX scale chunks hold 256 rows");
     constexpr int STAGE = A_ALL + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
@@ -230,18 +233,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         Sbase = reinterpret_cast<const char *>(p.scale);
         s_bytes = (uint32_t)((int64_t)(p.K / 32) * p.ld_scale * 2);
     }
-    // MX scales: e8m0 bytes, row r of A at scale_a + r * ld_scale_a, column n of
-    // B at scale + n * ld_scale (both pitches multiples of 4, both pointers
-    // 4-byte aligned, K/32 bytes used per row).  Each stage fetches the dword of
-    // its four blocks; the range ends at the last row's last dword, so rows past
-    // M or N (offsets at or past the range) read zeros.
+    // MX scales: e8m0 bytes, group-major: row r of A, group g at scale_a +
+    // g * ld_scale_a + r, column n of B, group g at scale + g * ld_scale + n (both
+    // pitches multiples of 4, both pointers 4-byte aligned).  A stage fetches,
+    // per operand and group, the 256 contiguous bytes from the tile's first row
+    // (column): rows past the tile or M read other rows' scales or, past the
+    // array, zeros, and are discarded.
     const char *SAbase = nullptr;
     uint32_t sa_bytes = 0;
     if constexpr (IS_MX) {
         SAbase = reinterpret_cast<const char *>(p.scale_a);
         Sbase = reinterpret_cast<const char *>(p.scale);
-        sa_bytes = (uint32_t)((M - 1) * p.ld_scale_a + ((p.K / 32 + 3) & ~3));
-        s_bytes = (uint32_t)((N - 1) * p.ld_scale + ((p.K / 32 + 3) & ~3));
+        sa_bytes = (uint32_t)((int64_t)(p.K / 32) * p.ld_scale_a);
+        s_bytes = (uint32_t)((int64_t)(p.K / 32) * p.ld_scale);
     }
 
     // ---- per-lane source offsets of this wave's direct-to-LDS loads.  Load q of
@@ -277,9 +281,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
     for (int i = 0; i < S_LD; ++i) {
         const int col = (i * NW + swave) * 64 + lane;   // byte of scale (n0 + col, 0) from Sbase
-        if constexpr (IS_MX)   // entries [0, BM): rows of A; [BM, BM + BN): columns of B
-            os[i] = col < BM ? (uint32_t)((m0 + col) * p.ld_scale_a) : (uint32_t)((n0 + col - BM) * p.ld_scale);
-        else   // e2m1: dword `col` of the stage holds columns 2 col and 2 col + 1
+        if constexpr (IS_MX) {   // load L = i NW + swave: operand L >> 2 (A, B), group L & 3
+            const int L = i * NW + swave;
+            os[i] = (uint32_t)(L & 3) * (uint32_t)((L >> 2) ? p.ld_scale : p.ld_scale_a) +
+                    (uint32_t)((L >> 2) ? n0 : m0) + 4 * (uint32_t)lane;
+        } else   // e2m1: dword `col` of the stage holds columns 2 col and 2 col + 1
             os[i] = 2 * (uint32_t)(n0 + 2 * col);
     }
 
@@ -311,10 +317,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         } else if constexpr (IS_MX) {
             const int q = i - A_LD - B_LD;
             if (S_NL % NW == 0 || q * NW + swave < S_NL) {   // wave-uniform
-                const bool rows = (q * NW + swave) * 64 < BM;   // wave-uniform: A's or B's scales
+                const bool rows = q * NW + swave < 4;   // wave-uniform: A's or B's scales
                 const __amdgpu_buffer_rsrc_t rS =
                     make_rsrc(rows ? SAbase : Sbase, real ? (rows ? sa_bytes : s_bytes) : 0u);
-                buf_ld4_lds(rS, os[q] + (uint32_t)(k0 >> 5), sb + A_ALL + B_TILE + (q * NW + swave) * 256);
+                buf_ld4_lds(rS, os[q] + (uint32_t)(k0 >> 5) * (uint32_t)(rows ? p.ld_scale_a : p.ld_scale),
+                            sb + A_ALL + B_TILE + (q * NW + swave) * 256);
             }
         } else if constexpr (IS_E2M1) {
             const int q = i - A_LD - B_LD;
@@ -394,18 +401,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // (the 4-bit operand holds k 32kg .. +31), and the scale of lane
             // group kg applies to k 32kg .. +31 of both operands (probed on the
             // GPU with one-hot operands).  So the lane reads chunks kg and kg+2.
-            // The stage's scale dword is read with substep 0 (shifted to this
-            // lane's block kg); substep 1 takes the same dword's next block pair
-            // from substep 0's fragment, which holds the same stage.
+            // The lane's scale is byte `row` of the chunk of group 2s + kg.
             const char *rA = sA + s * A_BYTES + row * 64;
             const int sw = (row >> 2) & 3;
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(rA + ((kg ^ sw) << 4));
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            if constexpr (s == 0)
-                f.sa[mi] = *reinterpret_cast<const unsigned *>(sA + A_ALL + B_TILE + row * 4) >> (8 * kg);
-            else
-                f.sa[mi] = f0.sa[mi] >> 16;
+            f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
         } else {
             f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
         }
@@ -438,12 +440,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
             f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
-            if constexpr (IS_MX) {
-                if constexpr (s == 0)
-                    f.sb[ni] = *reinterpret_cast<const unsigned *>(sB + B_TILE + BM * 4 + row * 4) >> (8 * kg);
-                else
-                    f.sb[ni] = f0.sb[ni] >> 16;
-            }
+            if constexpr (IS_MX)
+                f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
         } else {
             const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
             u32x2 lo, hi;

@@ -144,7 +144,8 @@ __global__ void __launch_bounds__(QWG) quant_mx_kernel(QuantMxArgs p, int64_t pe
             }
             __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(
                 reinterpret_cast<uint8_t *>(p.codes) + row * p.ldq + col * 8));
-            if ((col & 3) == 0) reinterpret_cast<uint8_t *>(p.scales)[row * p.ld_scale + col / 4] = (uint8_t)sc;
+            // scales are group-major: block g of row `row` at g * ld_scale + row
+            if ((col & 3) == 0) reinterpret_cast<uint8_t *>(p.scales)[(col / 4) * p.ld_scale + row] = (uint8_t)sc;
         }
 #pragma unroll
         for (int j = 0; j < QU; ++j) cur[j] = nxt[j];

@@ -283,7 +283,8 @@ class Handle:
 
     def quant_mx(self, X, codes, scales, stream=None):
         """MX quantiser through dg_quant_mx: X [M, K] fp16 -> codes [M, K] uint8
-        (fp8 e4m3) and scales [M, K/32] uint8 (e8m0); rows may be padded."""
+        (fp8 e4m3) and scales [K/32, M] uint8 (e8m0, group-major, the layout
+        gemm_mx takes); rows may be padded."""
         import torch
         M, K = X.shape
         for t, nm in ((X, "X"), (codes, "codes"), (scales, "scales")):
@@ -298,9 +299,10 @@ class Handle:
                 opts=None, workspace=None, stream=None):
         """C_out = act(alpha * (A.B) + bias) through dg_gemm_mx.
 
-        A: [M, K] uint8 fp8 e4m3 codes; SA: [M, >= K/32] uint8 e8m0 scales;
-        B: [N, K/2] uint8 packed e2m1 codes (pack_e2m1); SB: [N, >= K/32] uint8
-        e8m0 scales.  Rows may be padded (strides are the leading dimensions).
+        A: [M, K] uint8 fp8 e4m3 codes; SA: [K/32, >= M] uint8 e8m0 scales,
+        group-major; B: [N, K/2] uint8 packed e2m1 codes (pack_e2m1); SB:
+        [K/32, >= N] uint8 e8m0 scales, group-major.  Rows may be padded (strides
+        are the leading dimensions; scale strides multiples of 4).
         Returns the plan info.
         """
         import torch
