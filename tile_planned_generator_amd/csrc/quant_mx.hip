@@ -12,12 +12,12 @@
 // block holding an infinity or a NaN gets the NaN scale code 255 and NaN codes
 // 0x7f.
 //
-// Four lanes share a block: each lane loads 16 contiguous bytes (8 values), so
-// one load instruction of a wave reads 1 KB of consecutive memory, the block
-// maximum is combined over the four lanes with quad permutes, and each lane
-// stores its 8 codes (8 contiguous bytes).  Each workgroup streams a contiguous
-// share of the rows with the next round's loads in flight.
-// HBM-bound: 2 bytes read and 1 + 1/32 bytes written per value.
+// Four lanes share a block (a quad): each lane loads 16 contiguous bytes (8
+// values), so a wave's load reads 1 KB of one row; the block maximum is combined
+// over the quad with quad permutes; each lane stores its 8 codes.  A workgroup
+// takes 16 rows x 16 groups and writes that tile's scales through LDS, 16
+// contiguous bytes per group of the group-major scale array.  HBM-bound: 2 bytes
+// read and 1 + 1/32 bytes written per value.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,130 +41,98 @@ DG_DEV unsigned e4m3x4(float a, float b, float c, float d)
     return (unsigned)w;
 }
 
-constexpr int QU = 4;          // chunks of 8 values per thread and round
-constexpr int QWG = 256;       // threads per workgroup
-constexpr int QGRID = 2048;    // workgroups at most (eight per CU; measured on 4096x4096: 256, 512,
-                               // 1024, 2048 workgroups take 20.0, 14.1, 12.5, 11.7 us: parallelism
-                               // pays more than longer streams)
+constexpr int QWG = 256;   // threads per workgroup (four waves)
+constexpr int QR = 16;     // rows per workgroup (four per wave)
+constexpr int QG = 16;     // 32-value groups per workgroup (one 1 KB row segment)
 
-// Row and column (in chunks) of chunk c; 32-bit division whenever the chunk
-// count fits (`narrow` is the same for the whole grid).
-DG_DEV void chunk_rc(int64_t c, int64_t cpr, bool narrow, int64_t &row, int64_t &col)
+// A workgroup quantises QR rows x QG groups.  Wave w takes rows 4w .. 4w+3 of
+// the tile; for each, its 64 lanes read the row's 1 KB segment (lane l: group
+// l / 4, chunk l % 4, so the four lanes of a block form one quad), and write the
+// 512 bytes of codes.  The scales go through LDS: the tile's QG x QR scale bytes
+// are written group-major, 16 contiguous bytes per group.
+__global__ void __launch_bounds__(QWG) quant_mx_kernel(QuantMxArgs p)
 {
-    if (narrow) {
-        const uint32_t q = (uint32_t)c / (uint32_t)cpr;
-        row = q;
-        col = c - (int64_t)q * cpr;
-    } else {
-        row = c / cpr;
-        col = c - row * cpr;
+    __shared__ uint8_t s_sc[QG][QR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = p.K / 32;
+    const int gtiles = (G + QG - 1) / QG;
+    const int64_t rt = blockIdx.x / gtiles;
+    const int g0 = (int)(blockIdx.x - rt * gtiles) * QG;
+    const int64_t r0 = rt * QR;
+    const int g = g0 + (lane >> 2), part = lane & 3;
+    const bool g_ok = g < G;   // uniform over a quad
+    u32x4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = r0 + wave * 4 + i;
+        raw[i] = u32x4{0u, 0u, 0u, 0u};
+        if (row < p.M && g_ok)
+            raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                reinterpret_cast<const _Float16 *>(p.X) + row * p.ldx + g * 32 + part * 8));
     }
-}
-
-// Each workgroup streams a contiguous share of the chunks (`per` chunks, a
-// multiple of QWG * QU) in rounds of QWG * QU; the loads of round r + 1 are
-// issued before round r is converted.  Chunk of thread t, round r, item j:
-// base + r * QWG * QU + j * QWG + t, so the four lanes 4q .. 4q+3 of a wave hold
-// the four chunks of one block, and a block is in range for all four or for
-// none (the chunk count is a multiple of 4): the swaps only mix lanes of one
-// block.
-__global__ void __launch_bounds__(QWG) quant_mx_kernel(QuantMxArgs p, int64_t per)
-{
-    const int64_t cpr = p.K / 8;                          // chunks per row (a multiple of 4)
-    const int64_t nch = (int64_t)p.M * cpr;
-    const bool narrow = nch + (int64_t)QWG * QU <= 0xffffffffLL;
-    const int64_t base = (int64_t)blockIdx.x * per + threadIdx.x;
-    const int64_t end = min(nch, (int64_t)(blockIdx.x + 1) * per);
-    const int rounds = (int)(per / (QWG * QU));
-    auto load = [&](int r, u32x4 (&raw)[QU]) {
 #pragma unroll
-        for (int j = 0; j < QU; ++j) {
-            const int64_t c = base + (int64_t)r * QWG * QU + j * QWG;
-            if (c < end) {
-                int64_t row, col;
-                chunk_rc(c, cpr, narrow, row, col);
-                raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    reinterpret_cast<const _Float16 *>(p.X) + row * p.ldx + col * 8));
-            } else {
-                raw[j] = u32x4{0u, 0u, 0u, 0u};
-            }
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = r0 + wave * 4 + i;
+        // The block maximum on the magnitude bits: for binary16, the order of |x|
+        // is the integer order of its low 15 bits, infinities and NaN above every
+        // finite value (0x7c00 and up), so one packed integer maximum per dword
+        // finds both the maximum and any non-finite value.
+        unsigned mx = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const unsigned w = raw[i][d] & 0x7fff7fffu;
+            mx = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx),
+                                                                        __builtin_bit_cast(u16x2, w)));
         }
-    };
-    u32x4 cur[QU], nxt[QU];
-    load(0, cur);
-    for (int r = 0; r < rounds; ++r) {
-        if (base + (int64_t)r * QWG * QU >= end) break;   // uniform over a block's lanes
-        if (r + 1 < rounds) load(r + 1, nxt);
-#pragma unroll
-        for (int j = 0; j < QU; ++j) {
-            const int64_t c = base + (int64_t)r * QWG * QU + j * QWG;
-            const bool live = c < end;   // uniform over the four lanes of a block
-            // The block maximum on the magnitude bits: for binary16, the order of
-            // |x| is the integer order of its low 15 bits, infinities and NaN
-            // above every finite value (0x7c00 and up), so one packed integer
-            // maximum per dword finds both the maximum and any non-finite value.
-            unsigned mx = 0;
+        mx = max(mx & 0xffffu, mx >> 16);
+        // lanes 4q .. 4q+3: swap neighbours, then pairs (quad permutes [1,0,3,2]
+        // and [2,3,0,1], no LDS round trip)
+        mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, true));
+        mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, true));
+        if (row >= p.M || !g_ok) continue;
+        const bool bad = mx >= 0x7c00u;
+        const float amax = (float)__builtin_bit_cast(_Float16, (unsigned short)mx);
+        unsigned sc;
+        u32x2 out;
+        if (bad) {
+            sc = 255u;
+            out = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};
+        } else {
+            // amax is a binary32 normal (binary16 subnormals are), so its exponent
+            // field gives floor(log2 amax); e stays within -32 .. 7.
+            const int e = amax == 0.0f ? -127 : (int)(__builtin_bit_cast(unsigned, amax) >> 23) - 127 - 8;
+            sc = (unsigned)(e + 127);
+            // 2^-e as a binary32 (e >= -32: a normal power of two); amax = 0
+            // leaves every value zero, so any factor keeps the signs
+            const float inv = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
+            float f[8];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const unsigned w = cur[j][d] & 0x7fff7fffu;
-                mx = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx),
-                                                                            __builtin_bit_cast(u16x2, w)));
+                const unsigned w = raw[i][d];
+                f[2 * d] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu)) * inv;
+                f[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)) * inv;
             }
-            mx = max(mx & 0xffffu, mx >> 16);
-            // lanes 4q .. 4q+3: swap neighbours, then pairs (quad permutes
-            // [1,0,3,2] and [2,3,0,1], no LDS round trip)
-            mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, true));
-            mx = max(mx, (unsigned)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, true));
-            if (!live) continue;
-            const bool bad = mx >= 0x7c00u;
-            const float amax = (float)__builtin_bit_cast(_Float16, (unsigned short)mx);
-            int64_t row, col;
-            chunk_rc(c, cpr, narrow, row, col);
-            unsigned sc;
-            u32x2 out;
-            if (bad) {
-                sc = 255u;
-                out = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};
-            } else {
-                // amax is a binary32 normal (binary16 subnormals are), so its
-                // exponent field gives floor(log2 amax); e stays within -32 .. 7.
-                const int e = amax == 0.0f ? -127 : (int)(__builtin_bit_cast(unsigned, amax) >> 23) - 127 - 8;
-                sc = (unsigned)(e + 127);
-                // 2^-e as a binary32 (e >= -32: a normal power of two); amax = 0
-                // leaves every value zero, so any factor keeps the signs
-                const float inv = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
-                float f[8];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const unsigned w = cur[j][d];
-                    f[2 * d] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu)) * inv;
-                    f[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)) * inv;
-                }
-                out = u32x2{e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
-            }
-            __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(
-                reinterpret_cast<uint8_t *>(p.codes) + row * p.ldq + col * 8));
-            // scales are group-major: block g of row `row` at g * ld_scale + row
-            if ((col & 3) == 0) reinterpret_cast<uint8_t *>(p.scales)[(col / 4) * p.ld_scale + row] = (uint8_t)sc;
+            out = u32x2{e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
         }
-#pragma unroll
-        for (int j = 0; j < QU; ++j) cur[j] = nxt[j];
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(
+            reinterpret_cast<uint8_t *>(p.codes) + row * p.ldq + g * 32 + part * 8));
+        if (part == 0) s_sc[lane >> 2][wave * 4 + i] = (uint8_t)sc;
     }
+    __syncthreads();
+    // group-major scales: block g of row r at g * ld_scale + r
+    const int tg = threadIdx.x / QR, tr = threadIdx.x % QR;
+    if (g0 + tg < G && r0 + tr < p.M)
+        reinterpret_cast<uint8_t *>(p.scales)[(int64_t)(g0 + tg) * p.ld_scale + r0 + tr] = s_sc[tg][tr];
 }
 
 hipError_t launch_quant_mx(const QuantMxArgs &a, hipStream_t s)
 {
-    const int64_t chunks = (int64_t)a.M * (a.K / 8);
-    if (chunks == 0) return hipSuccess;
-    constexpr int64_t R = (int64_t)QWG * QU;              // chunks per workgroup round
-    int64_t grid = (chunks + R - 1) / R;
-    if (grid > QGRID) grid = QGRID;
-    const int64_t per = ((chunks + grid - 1) / grid + R - 1) / R * R;
-    grid = (chunks + per - 1) / per;
-    if (per / R > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t G = a.K / 32;
+    const int64_t grid = ((int64_t)a.M + QR - 1) / QR * ((G + QG - 1) / QG);
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
     QuantMxArgs arg = a;
-    int64_t per_arg = per;
-    void *args[] = {&arg, &per_arg};
+    void *args[] = {&arg};
     hipError_t e = hipLaunchKernel(reinterpret_cast<void *>(quant_mx_kernel), dim3((unsigned)grid, 1, 1),
                                    dim3(QWG, 1, 1), args, 0, s);
     if (e != hipSuccess) return e;
