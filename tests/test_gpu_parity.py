@@ -255,6 +255,15 @@ def test_e2m1_tiled_small(h, M, N, K):
     run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_TILED))
 
 
+@pytest.mark.parametrize("M,N,K,path", [(100, 257, 256, dg.DG_PATH_TILED), (300, 33, 1024, dg.DG_PATH_TILED),
+                                        (1, 33, 512, dg.DG_PATH_SKINNY), (3, 129, 2048, dg.DG_PATH_SKINNY)])
+def test_e2m1_odd_n(h, M, N, K, path):
+    # odd N: the group-major scale rows are padded to N + 1 (scales_gn), and the
+    # tiled kernel's paired scale loads cover a column past N
+    w = synth.make("e2m1_4096x4096x4096", M=M, N=N, K=K)
+    run(h, w, opts=dg.dg_plan_opts(force_path=path))
+
+
 def test_every_tiled_variant_on_a_ragged_problem(h):
     # each compiled tile shape, forced in turn, on a problem with ragged M and N,
     # a K tail (K = 7 full steps + a half step; e2m1 K is whole 32-groups, so
