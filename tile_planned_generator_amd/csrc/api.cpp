@@ -453,7 +453,8 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
             bool ok = true;
             for (size_t i = 0; i < ks.size() && ok; ++i) {
                 Problem pr;
-                describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
+                s = describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
+                if (s) return s;   // (every sample passed above; kept for safety)
                 PlanResult r = plan_problem(pr, h->desc, v);
                 if (r.status != DG_OK) {
                     ok = false;
