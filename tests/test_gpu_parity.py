@@ -319,6 +319,23 @@ def test_skinny_e2m1(h, M):
         run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY, force_split_k=S))
 
 
+@pytest.mark.parametrize("name,M,N,K,split,path,pad", [
+    # few outputs over many slices (32 to 160): the split-K reduction sums runs of
+    # slices per group of four outputs, group counts 1024, 136, 65 (the last
+    # workgroup partly empty), 128 and 256
+    ("i8_4096x4096x4096", 64, 64, 8192, 64, "tiled", 0),
+    ("i8_4096x4096x4096", 8, 68, 8192, 128, "tiled", 8),
+    ("f16_256x256x256_alpha_beta_d", 1, 260, 12800, 160, "skinny", 8),
+    ("f16_256x256x256_alpha_beta_d", 8, 64, 8192, 32, "skinny", 0),
+    ("f16_256x256x256_alpha_beta_d", 16, 64, 8192, 64, "tiled", 0),
+])
+def test_reduce_many_runs(h, name, M, N, K, split, path, pad):
+    w = synth.make(name, M=M, N=N, K=K)
+    p = dg.DG_PATH_TILED if path == "tiled" else dg.DG_PATH_SKINNY
+    info, _ = run(h, w, pad=pad, opts=dg.dg_plan_opts(force_split_k=split, force_path=p))
+    assert info.split_k == split
+
+
 def test_config_bf16_1x256x12800_full(h):
     run(h, synth.make("bf16_1x256x12800"))
 
