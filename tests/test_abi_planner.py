@@ -522,3 +522,30 @@ def test_plan_range_errors(off):
     assert dg.dg_plan_range(*args(128, 512, dg.dg_plan_opts(force_m_tile=128))) == dg.DG_ERR_CONFLICT
     assert dg.dg_plan_range(None, 1, 1, 16, 32, C.byref(dt), C.byref(lay), 0, 0, None, C.byref(ro), None,
                             None) == dg.DG_ERR_INVALID_STATE
+
+
+def test_transcript_tile_is_a_candidate_with_a100_budgets():
+    """[generator] DeepGEMM generator article, section 3.2 (the worked planner
+    run on an A100 for fp16 2048 x 2048 x 8192): the run keeps a handful of
+    Pareto configurations and ranks a 64 x 64 tile with a 32-deep K step first.
+    Its estimates cannot be reproduced (they equal the A100's peak rate, not a
+    prediction), so this is a sanity check only: with the A100's budgets in the
+    device description (108 SMs, 164 KB shared memory per SM and 163 KB per
+    block, 1.41 GHz, 1555 GB/s, a 40 MB L2), the Pareto set still holds a
+    64 x 64 tile stepping K by 32, and every candidate fits the described LDS
+    and covers K."""
+    a = dg.default_device_desc()
+    a.arch = b"a100-budgets"
+    a.cu_count, a.xcd_count = 108, 1
+    a.lds_bytes_per_cu, a.lds_bytes_per_wg = 164 * 1024, 163 * 1024
+    a.clock_ghz, a.hbm_gbps, a.l2_bytes_per_xcd = 1.41, 1555.0, 40.0 * 1024 * 1024
+    h = dg.Handle(offline=a)
+    try:
+        M, N, K = 2048, 2048, 8192
+        cands = h.candidates(M, N, K, "f16", "f16", "f16")
+        assert any(p.m_tile == 64 and p.n_tile == 64 and p.k_main == 32 for p in cands)
+        for p in cands:
+            assert p.lds_bytes <= a.lds_bytes_per_wg
+            assert p.k_main * p.n_main + p.k_tail * p.n_tail == -(-K // p.split_k)
+    finally:
+        h.close()
