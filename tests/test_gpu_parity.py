@@ -319,6 +319,25 @@ def test_skinny_e2m1(h, M):
         run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY, force_split_k=S))
 
 
+@pytest.mark.parametrize("M", [15, 16, 17])
+def test_m_either_side_of_the_streaming_limit(h, M):
+    # the streaming kernels take M <= 16: at 15 and 16 the 16-bit problems plan to
+    # the skinny MFMA kernel, at 17 to the tiled one (int8 and e2m1 stay tiled);
+    # N is ragged against every tile and the leading dimensions padded
+    for name in ("bf16_16x4096x131072", "f16_256x256x256_alpha_beta_d"):
+        run(h, synth.make(name, M=M, N=264, K=2080), pad=8)
+    run(h, synth.make("i8_4096x4096x4096", M=M, N=208, K=640))
+    run(h, synth.make("e2m1_4096x4096x4096", M=M, N=200, K=1024))
+
+
+@pytest.mark.parametrize("name,K", [("f16_256x256x256_alpha_beta_d", 32), ("bf16_16x4096x131072", 32),
+                                    ("i8_4096x4096x4096", 64), ("e2m1_4096x4096x4096", 32)])
+def test_k_of_one_step(h, name, K):
+    # K equal to one K step of the tiled kernels: one main step, no tail, no split
+    info, _ = run(h, synth.make(name, M=130, N=96, K=K))
+    assert info.n_main == 1 and info.n_tail == 0 and info.split_k == 1
+
+
 @pytest.mark.parametrize("name,M,N,K,split,path,pad", [
     # few outputs over many slices (32 to 160): the split-K reduction sums runs of
     # slices per group of four outputs, group counts 1024, 136, 65 (the last
