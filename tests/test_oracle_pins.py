@@ -515,9 +515,12 @@ def test_mx_scale_block_index():
     SB = np.array([[120 - g - 4 * j for j in range(N)] for g in range(K // 32)], np.uint8)
     A[1, 70] = 0x40            # 2.0, in block 2
     Bc[70, 2] = 7              # 6.0
+    A[0, 40] = 0x38            # 1.0, in block 1 (an odd block, next to block 0)
+    Bc[40, 0] = 2              # 1.0
     R = oracle.gemm_mx(A, SA, Bc, SB)
     assert R[1, 2] == 12.0 * 2.0 ** ((127 + 2 + 3) - 127) * 2.0 ** ((120 - 2 - 8) - 127)
-    assert np.count_nonzero(R) == 1
+    assert R[0, 0] == 2.0 ** ((127 + 1) - 127) * 2.0 ** ((120 - 1) - 127)
+    assert np.count_nonzero(R) == 2
 
 
 def test_mx_unit_scales_reduce_to_the_e2m1_gemm():
