@@ -8,9 +8,9 @@
 //   e     = floor(log2 amax) - 8     (8: the exponent of e4m3's largest normal, 448)
 //   scale = 2^e, stored as the e8m0 code e + 127 (code 0 when amax is 0)
 //   code  = e4m3(x / scale), nearest even, magnitudes above 448 saturating to 448
-// x / scale is exact in binary32, so the conversion is the only rounding.  A
-// block holding an infinity or a NaN gets the NaN scale code 255 and NaN codes
-// 0x7f.
+// x / scale is exact (a power of two within range), so the rounding to e4m3 is
+// the only one.  A block holding an infinity or a NaN gets the NaN scale code
+// 255 and NaN codes 0x7f.
 //
 // Four lanes share a block (a quad): each lane loads 16 contiguous bytes (8
 // values), so a wave's load reads 1 KB of one row; the block maximum is combined
@@ -26,19 +26,27 @@
 
 namespace dg {
 
-// Four e4m3 codes (one dword, first value in the low byte) of binary32 values
-// already divided by the block scale.  Clamping to +-448 first and then rounding
-// to nearest even gives what rounding then saturating gives: every magnitude in
-// (448, 464) rounds to 448 anyway, and larger ones saturate to it.  The
-// conversion instruction rounds to nearest even and keeps e4m3's subnormals.
-DG_DEV unsigned e4m3x4(float a, float b, float c, float d)
+typedef short qs16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 qh16x2 __attribute__((ext_vector_type(2)));
+
+// Four e4m3 codes (one dword, first value in the low byte) of the four binary16
+// values in two dwords, each divided by the block scale.  gfx950's scaled
+// conversion takes two binary16 values and a binary32 scale and writes two e4m3
+// codes into one half of the destination; measured over every binary16 pattern
+// and every scale 2^-32 .. 2^7, it divides exactly by the scale, rounds to
+// nearest even and keeps e4m3's subnormals, but a quotient that rounds past 448
+// gives the NaN code (0x7f, or 0xff when negative) instead of saturating.  The
+// inputs here are finite, so every NaN code is such an overflow: it becomes
+// +-448 (0x7e / 0xfe) by clearing the code's lowest bit.
+DG_DEV unsigned e4m3x4(unsigned lo, unsigned hi, float scale)
 {
-    const float lo = -448.0f, hi = 448.0f;
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi), __builtin_amdgcn_fmed3f(b, lo, hi),
-                                            0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi), __builtin_amdgcn_fmed3f(d, lo, hi), w,
-                                        true);
-    return (unsigned)w;
+    qs16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(qs16x2{0, 0}, __builtin_bit_cast(qh16x2, lo), scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, __builtin_bit_cast(qh16x2, hi), scale, true);
+    const unsigned u = __builtin_bit_cast(unsigned, w);
+    // a byte's low seven bits are 0x7f exactly when adding 1 sets its bit 7
+    // (no carry leaves a byte: each is at most 0x7f)
+    const unsigned nan = ((u & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+    return u ^ (nan >> 7);
 }
 
 constexpr int QWG = 256;   // threads per workgroup (four waves)
@@ -102,17 +110,10 @@ __global__ void __launch_bounds__(QWG) quant_mx_kernel(QuantMxArgs p)
             // field gives floor(log2 amax); e stays within -32 .. 7.
             const int e = amax == 0.0f ? -127 : (int)(__builtin_bit_cast(unsigned, amax) >> 23) - 127 - 8;
             sc = (unsigned)(e + 127);
-            // 2^-e as a binary32 (e >= -32: a normal power of two); amax = 0
-            // leaves every value zero, so any factor keeps the signs
-            const float inv = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
-            float f[8];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const unsigned w = raw[i][d];
-                f[2 * d] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu)) * inv;
-                f[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)) * inv;
-            }
-            out = u32x2{e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
+            // 2^e as a binary32 (a normal power of two); amax = 0 leaves every
+            // value zero, so any scale keeps the signs
+            const float scale = amax == 0.0f ? 1.0f : __builtin_bit_cast(float, (unsigned)(e + 127) << 23);
+            out = u32x2{e4m3x4(raw[i][0], raw[i][1], scale), e4m3x4(raw[i][2], raw[i][3], scale)};
         }
         __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(
             reinterpret_cast<uint8_t *>(p.codes) + row * p.ldq + g * 32 + part * 8));
