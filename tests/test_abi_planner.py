@@ -549,3 +549,16 @@ def test_transcript_tile_is_a_candidate_with_a100_budgets():
             assert p.k_main * p.n_main + p.k_tail * p.n_tail == -(-K // p.split_k)
     finally:
         h.close()
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    # the benchmark measures one GPU; asked for more it exits with status 2 and a
+    # message, before it touches a device
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                       timeout=120, env=dict(os.environ, **env))
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
