@@ -230,8 +230,8 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K,
 
 /* Plan for every K in [K_min, K_max] at once: the pages' range constraint
  * (K_min / K_max in the declaration instead of one K, so that one compact
- * kernel serves every layer whose K falls in the range, [overview] section 6,
- * the second stage of the service case).  K is sampled at both ends and at the
+ * kernel serves every layer whose K falls in the range, [overview] section
+ * 5.3, the second stage of the service case).  K is sampled at both ends and at the
  * doublings between them; each compiled kernel variant of the problem's path
  * (tile and wave grid, or the streaming path) is planned at every sample, and
  * the variant whose largest ratio of estimated time to the best plan of that K
