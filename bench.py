@@ -11,9 +11,11 @@ synthetic data drawn on the GPU and resident in HBM before any timing starts.
 
 Timing: HIP events on the stream the kernels run on (torch's current stream),
 bracketing K back-to-back steps after W warm-up steps; ms_per_step is the
-average and `value` the whole-job rate.  The roofline's `achieved` uses the
-average launch duration instead: a second pass puts an event pair around each
-launch, so the gaps between launches are not counted.  Its `traffic` is the HBM
+average and `value` the whole-job rate.  A step is one launch of the kernel,
+so the roofline's `achieved` is the same rate (the kernel's average duration
+over the timed region); `repeats` times five more runs of K steps (median and
+minimum), and `telemetry` records the engine clock and the package power over
+a 3 s loop of the headline kernel.  The roofline's `traffic` is the HBM
 bytes per launch recorded from rocprofv3 counters in profiles/hbm_traffic.txt,
 reported only while the kernel sources still hash to the recorded value.  Small HBM-bound workloads rotate through copies of B (>= 576 MB in
 all, twice the L2 + MALL) so that every step reads HBM, and are also reported
@@ -234,21 +236,6 @@ def time_steps(p, steps, warmup, use_graph):
     return e0.elapsed_time(e1) / steps, steps
 
 
-def launch_durations(p, n):
-    """Mean milliseconds of one launch: an event pair around each of n launches
-    on the launch stream, so the gaps between launches are not counted."""
-    import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        p.launch(i)
-        b.record()
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / n
-
-
 # Kernel sources whose text fixes the tiled kernel's code; a recorded traffic
 # figure holds only for the sources it was measured on.
 TILED_SOURCES = ["gemm_tiled.h", "gemm_tiled_i8.hip", "kcommon.h", "catalogue.h", "dg_args.h"]
@@ -358,6 +345,120 @@ def stage_breakdown(h, p, launches=5):
     return s
 
 
+def telemetry(p, ms_step, seconds=3.0):
+    """Engine clock and package power while the headline kernel runs back to back
+    for about `seconds`: the GPU metrics table of the AMD SMI library, sampled
+    from a thread every 20 ms.  The firmware refreshes the table about once a
+    second, so only samples taken after the first second of the loop and with a
+    new firmware timestamp are kept.  `sclk_mhz` is the mean engine clock over the
+    XCDs and those samples, `power_w` the mean socket power, and
+    `power_limited_frac` the share of the loop the power limit (PPT) was
+    throttling the clock (from the firmware's residency counters)."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        return {"error": f"amdsmi not importable: {e}"}
+    try:
+        amdsmi.amdsmi_init()
+        props = torch.cuda.get_device_properties(0)
+        want = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}"
+        handle = None
+        for x in amdsmi.amdsmi_get_processor_handles():
+            if str(amdsmi.amdsmi_get_gpu_device_bdf(x)).lower().startswith(want):
+                handle = x
+        if handle is None:
+            return {"error": f"no SMI device at {want}"}
+        limit = amdsmi.amdsmi_get_power_info(handle).get("power_limit")
+        samples, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                    samples.append((time.perf_counter(), m))
+                except Exception:
+                    pass
+                time.sleep(0.02)
+
+        n = max(1, int(seconds / (ms_step * 1e-3)))
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        for i in range(n):
+            p.launch(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        kept, seen = [], set()
+        for t, m in samples:
+            stamp = m.get("firmware_timestamp")
+            if t0 + 1.0 <= t <= t1 and stamp not in seen:
+                seen.add(stamp)
+                kept.append(m)
+        out = {"loop_s": round(t1 - t0, 3), "launches": n, "samples": len(kept),
+               "power_limit_w": round(limit / 1e6, 1) if isinstance(limit, (int, float)) and limit > 1e4
+               else limit, "source": "amdsmi gpu metrics"}
+        if not kept:
+            out["error"] = "no refreshed sample inside the loop"
+            return out
+
+        def num(v):
+            return isinstance(v, (int, float)) and not isinstance(v, bool)
+        clks = [[c for c in m.get("current_gfxclks", []) if num(c) and c > 0] for m in kept]
+        clks = [c for c in clks if c]
+        if clks:
+            out["sclk_mhz"] = round(sum(sum(c) / len(c) for c in clks) / len(clks), 1)
+            out["sclk_mhz_per_xcd"] = [round(sum(c[i] for c in clks) / len(clks)) for i in range(len(clks[0]))]
+        pw = [m.get("current_socket_power") for m in kept if num(m.get("current_socket_power"))]
+        if pw:
+            out["power_w"] = round(sum(pw) / len(pw), 1)
+        first, last = kept[0], kept[-1]
+        if all(num(x.get(k)) for x in (first, last) for k in ("ppt_residency_acc", "accumulation_counter")):
+            da = last["accumulation_counter"] - first["accumulation_counter"]
+            if da > 0:
+                out["power_limited_frac"] = round((last["ppt_residency_acc"] - first["ppt_residency_acc"]) / da, 3)
+        return out
+    except Exception as e:  # pragma: no cover
+        return {"error": f"{type(e).__name__}: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def versions():
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rocm = fh.read().strip()
+    except OSError:
+        pass
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "rocm": rocm}
+
+
+def repeats(p, steps, n=5):
+    """n more timed runs of `steps` back-to-back steps: median and minimum."""
+    import torch
+    ms = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            p.launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / steps)
+    ms.sort()
+    return {"n": n, "steps": steps, "ms_median": round(ms[n // 2], 6), "ms_min": round(ms[0], 6)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +468,8 @@ def main():
     ap.add_argument("--workloads", default="",
                     help="comma-separated subset of the other workloads to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the clock and power record (a 3 s loop of the headline kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB once (a plain copy kernel of known size, the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -396,12 +499,15 @@ def main():
     head = report(p, ms)
     ops, _ = algorithmic(p.w)
     achieved_job = ops / (ms * 1e-3) / 1e12
-    ms_launch = launch_durations(p, steps)
-    achieved = ops / (ms_launch * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["i8"],
-                "unit": "TOP/s", "frac": round(achieved / PEAK["i8"], 4),
-                "traffic": recorded_traffic(HEADLINE), "launch_ms": round(ms_launch, 6)}
+    # the kernel's average duration over the timed region (one launch per step)
+    roofline = {"bound": "mfma", "achieved": round(achieved_job, 2), "peak": PEAK["i8"],
+                "unit": "TOP/s", "frac": round(achieved_job / PEAK["i8"], 4),
+                "traffic": recorded_traffic(HEADLINE), "kernel_ms": round(ms, 6)}
+    rep = repeats(p, steps)
+    rep["TOP/s_median"] = round(ops / (rep["ms_median"] * 1e-3) / 1e12, 2)
+    rep["TOP/s_best"] = round(ops / (rep["ms_min"] * 1e-3) / 1e12, 2)
     stages = stage_breakdown(h, p)
+    telem = None if args.no_telemetry else telemetry(p, ms)
     del p
     torch.cuda.empty_cache()
 
@@ -435,8 +541,11 @@ def main():
                    "kernel": head["kernel"], "tile": head["tile"], "split_k": head["split_k"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "repeats": rep,
+        "telemetry": telem,
         "stages": stages,
         "device": {"name": props.name, "cus": props.multi_processor_count},
+        "versions": versions(),
         "workloads": workloads,
     }
     print(json.dumps(line), flush=True)

@@ -4,9 +4,9 @@ Every case draws its inputs with the shared generator, runs ``dg_gemm`` through
 the C ABI (ctypes binding), and compares with the oracle: bit for bit for int8
 -> int32 and the requantise epilogues, within the rule of ``tests/parity.py``
 for floating point.  Small cases span several tiles with ragged edges and
-padded leading dimensions and are checked on every output; the full-size
-workloads run in the launch configuration the benchmark times and are checked
-on sampled rows and columns (the oracle computes those outputs one by one).
+padded leading dimensions; the full-size workloads run in the launch
+configuration the benchmark times.  Every case is checked on every output, and
+the output's row padding and a few rows past its end must keep a sentinel.
 """
 import numpy as np
 import pytest
@@ -45,10 +45,41 @@ def to_dev(t, pad=0):
     return t.contiguous()
 
 
+GUARD_ROWS = 3
+SENTINEL = 7
+
+
+def guarded_out(M, N, dtype, pad):
+    """Output [M, N] inside a buffer whose row padding (pad > 0) and GUARD_ROWS
+    extra rows hold SENTINEL: a store past column N or row M changes them.
+    Returns (the [M, N] view, the whole buffer)."""
+    ld = (N + pad + 15) // 16 * 16 if pad else N
+    buf = torch.full((M + GUARD_ROWS, ld), SENTINEL, dtype=dtype, device=DEV)
+    return buf[:M, :N], buf
+
+
+def check_guards(buf, M, N):
+    """Every element of `buf` outside [:M, :N] still holds SENTINEL."""
+    host = buf.cpu()
+    mask = torch.ones(host.shape, dtype=torch.bool)
+    mask[:M, :N] = False
+    bad = int((host[mask] != SENTINEL).sum())
+    assert bad == 0, f"{bad} elements outside the output were written"
+
+
+def _chunks(n, size):
+    """Position slices of n columns, `size` at a time (one slice when size is 0)."""
+    size = size or max(n, 1)
+    return [slice(i, min(n, i + size)) for i in range(0, max(n, 1), size)]
+
+
 def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, rows=None,
-        cols=None, requant_scale=1.0, rq_bias=None, alpha=None, beta=None):
+        cols=None, requant_scale=1.0, rq_bias=None, alpha=None, beta=None, col_chunk=0):
     """Run workload ``w`` through dg_gemm and check it against the oracle on
-    rows x cols (all by default).  Returns (plan info, error stats)."""
+    rows x cols (all by default; the oracle runs on column blocks of
+    ``col_chunk`` columns when it is given, which bounds its binary64 copy of B).
+    The output's row padding and a few rows past M are checked untouched.
+    Returns (plan info, error stats)."""
     t = w.tensors
     M, N, K = w.M, w.N, w.K
     out = out or w.out
@@ -69,7 +100,7 @@ def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, ro
     else:
         Bd = to_dev(t["B"], pad)
         layout = dg.DG_ROW_MAJOR
-    Cd = to_dev(torch.full((M, N), 7, dtype=TORCH_OUT[out]), pad)
+    Cd, Cbuf = guarded_out(M, N, TORCH_OUT[out], pad)
     D = to_dev(t["D"], pad) if "D" in t and beta != 0 else None
     bias = t.get("bias")
     if epilogue in ("requant_i8", "requant_f16"):
@@ -79,42 +110,55 @@ def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, ro
                   b_scale=scale, b_layout=layout, opts=opts, requant_scale=requant_scale)
     torch.cuda.synchronize()
     say(f"       plan {info.kernel_name.decode()} S={info.split_k} tile={info.m_tile}x{info.n_tile}")
+    check_guards(Cbuf, M, N)
+    del A, Bd, scale
 
     r_idx = torch.arange(M) if rows is None else torch.as_tensor(rows)
     c_idx = torch.arange(N) if cols is None else torch.as_tensor(cols)
     Csub = Cd.cpu()[r_idx][:, c_idx]
     Ah = t["A"][r_idx.to(t["A"].device)].cpu()
     if w.path == "i8":
-        Bh = t["B"][:, c_idx.to(t["B"].device)].cpu()
         Dh = t["D"][r_idx][:, c_idx].cpu() if D is not None else None
-        R, Cw, ov = oracle.gemm_int(Ah.numpy(), Bh.numpy(), alpha=int(alpha), beta=int(beta),
-                                    D=bits(Dh) if Dh is not None else None)
+        parts = []
+        for pos in _chunks(len(c_idx), col_chunk):
+            Bh = t["B"][:, c_idx[pos].to(t["B"].device)].cpu()
+            Dc = bits(Dh[:, pos]) if Dh is not None else None
+            parts.append(oracle.gemm_int(Ah.numpy(), Bh.numpy(), alpha=int(alpha), beta=int(beta), D=Dc))
+        Cw = np.concatenate([p[1] for p in parts], axis=1)
+        ov = sum(p[2] for p in parts)
+        assert Cw.shape == (len(r_idx), len(c_idx))
         if epilogue in ("requant_i8", "requant_f16"):
             want = oracle.requant(Cw, alpha=requant_scale,
                                   bias=rq_bias.numpy()[c_idx.numpy()] if rq_bias is not None else None,
                                   out="i8" if epilogue == "requant_i8" else "f16")
             got = bits(Csub)
             assert np.array_equal(got, want), int((got != want).sum())
-            return info, {"bitexact": True}
+            return info, {"bitexact": True, "n": int(got.size)}
         got = Csub.numpy()
         assert np.array_equal(got, Cw), int((got != Cw).sum())
-        return info, {"bitexact": True, "overflow": ov}
+        say(f"       ok bit-exact on {got.size} outputs")
+        return info, {"bitexact": True, "overflow": ov, "n": int(got.size)}
     a_kind = "f16" if w.path in ("f16", "e2m1") else "bf16"
-    kw = {}
-    if w.path == "e2m1":
-        Bh = bits(t["codes"][:, c_idx.to(t["codes"].device)])
-        kw = dict(scale=bits(t["scale"][:, c_idx.to(t["scale"].device)]), group_k=32)
-        b_kind = "e2m1"
-    else:
-        Bh = bits(t["B"][:, c_idx.to(t["B"].device)])
-        b_kind = a_kind
-    if D is not None:
-        kw.update(D=bits(t["D"][r_idx][:, c_idx]), d_kind=out)
-    if bias is not None:
-        kw.update(bias=bits(t["bias"][c_idx.to(t["bias"].device)]), bias_kind=a_kind)
-    act = 1 if "gelu" in epilogue else 0
-    R = oracle.gemm_real(bits(Ah), Bh, a_kind=a_kind, b_kind=b_kind, alpha=alpha, beta=beta,
-                         act=act, **kw)
+    parts = []
+    for pos in _chunks(len(c_idx), col_chunk):
+        kw = {}
+        cd = c_idx[pos].to(t["A"].device)
+        if w.path == "e2m1":
+            Bh = bits(t["codes"][:, cd])
+            kw = dict(scale=bits(t["scale"][:, cd]), group_k=32)
+            b_kind = "e2m1"
+        else:
+            Bh = bits(t["B"][:, cd])
+            b_kind = a_kind
+        if D is not None:
+            kw.update(D=bits(t["D"][r_idx.to(t["D"].device)][:, cd]), d_kind=out)
+        if bias is not None:
+            kw.update(bias=bits(t["bias"][cd]), bias_kind=a_kind)
+        act = 1 if "gelu" in epilogue else 0
+        parts.append(oracle.gemm_real(bits(Ah), Bh, a_kind=a_kind, b_kind=b_kind, alpha=alpha,
+                                      beta=beta, act=act, **kw))
+        del Bh
+    R = np.concatenate(parts, axis=1)
     st = check_fp(Csub, R, tol_for(w.path, out))
     say(f"       ok {st}")
     return info, st
@@ -200,6 +244,31 @@ def test_rank_one_closed_form_exact(h):
     h.gemm(A.to(DEV), B.to(DEV), Cd)
     torch.cuda.synchronize()
     assert int(Cd[0, 0]) == -66584576 and int(Cd[39, 47]) == 2 ** 26
+
+
+def test_int32_accumulation_wraps(h):
+    # Sums past the int32 range: A = -128 everywhere and B[k][j] = -128 for the
+    # first L_j rows of K (0 after), so C[i][j] = 16384 * L_j, from just below
+    # 2^31 to about 1.28 * 2^31 across the columns (L_j = 131072 gives exactly
+    # 2^31).  The 32-bit result wraps modulo 2^32 (the oracle's wrapped C), with
+    # the whole K in one slice and split into slices reduced in 32 bits.
+    M, N, K = 64, 96, 131072
+    L = [K - 256 + 384 * j for j in range(N)]
+    B = torch.zeros(K + 2048 * 32, N, dtype=torch.int8)
+    for j, l in enumerate(L):
+        B[:l, j] = -128
+    for KK in (K, K + 2048 * 32):
+        Ak = torch.full((M, KK), -128, dtype=torch.int8)
+        Bk = B[:KK].contiguous()
+        R, Cw, ov = oracle.gemm_int(Ak.numpy(), Bk.numpy())
+        assert ov > 0 and int(R.max()) > 2 ** 31 - 1
+        for split in (1, 4):
+            say(f"[case] int32 wrap M={M} N={N} K={KK} split={split}")
+            Cd = torch.empty(M, N, dtype=torch.int32, device=DEV)
+            h.gemm(Ak.to(DEV), Bk.to(DEV), Cd,
+                   opts=dg.dg_plan_opts(force_split_k=split, force_path=dg.DG_PATH_TILED))
+            torch.cuda.synchronize()
+            assert np.array_equal(Cd.cpu().numpy(), Cw)
 
 
 def test_fp16_subnormal_inputs_not_flushed(h):
@@ -454,18 +523,13 @@ def test_operand_of_4_gib_is_refused_by_the_tiled_path(h):
 
 
 # ------------------------------------------------------ full-size workloads
-def _sample(n, k, seed):
-    g = torch.Generator().manual_seed(seed)
-    idx = torch.randperm(n, generator=g)[:k].sort().values
-    # always include the first and last row/column (tile edges)
-    return torch.unique(torch.cat([idx, torch.tensor([0, n - 1])]))
-
-
-@pytest.mark.parametrize("name", ["i8_4096x4096x4096", "f16_4096x4096x4096",
-                                  "f16_2048x2048x8192_bias_gelu", "e2m1_4096x4096x4096",
-                                  "bf16_1x4096x131072", "bf16_16x4096x131072"])
-def test_full_size_sampled(h, name):
+@pytest.mark.parametrize("name,col_chunk", [("i8_4096x4096x4096", 0), ("f16_4096x4096x4096", 0),
+                                            ("f16_2048x2048x8192_bias_gelu", 0),
+                                            ("e2m1_4096x4096x4096", 0),
+                                            ("bf16_1x4096x131072", 512), ("bf16_16x4096x131072", 512)])
+def test_full_size_every_output(h, name, col_chunk):
+    # the workload at its full size, in the launch configuration the benchmark
+    # times (planner's choice), compared with the oracle on every output
     w = synth.make(name, device=DEV)
-    rows = _sample(w.M, 48, 5) if w.M > 16 else None
-    cols = _sample(w.N, 96, 6)
-    run(h, w, rows=rows, cols=cols)
+    info, st = run(h, w, col_chunk=col_chunk)
+    assert st["n"] == w.M * w.N

@@ -45,6 +45,10 @@ MUTATIONS = {
     "quantiser block maximum over 16": (
         "            for (int t = 0; t < 32; ++t) {\n                double v = orc_f16_value(xb[t]);",
         "            for (int t = 0; t < 16; ++t) {\n                double v = orc_f16_value(xb[t]);"),
+    # requantise
+    "requant bias before the scale": ("volatile float v = a * alpha;\n            if (bias) v = v + bias[n];",
+                                      "volatile float v = (bias ? a + bias[n] : a) * alpha;"),
+    "requant rounds half away from zero": ("float r = rintf(v);", "float r = roundf(v);"),
 }
 
 

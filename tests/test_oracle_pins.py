@@ -362,25 +362,85 @@ def test_alpha_beta_linearity_and_bias_gelu_order():
     assert np.array_equal(Rb, oracle.gelu_erf(pre))
 
 
-def test_requant_against_numpy_binary32():
-    rng = np.random.default_rng(5)
-    acc = rng.integers(-2 ** 31, 2 ** 31 - 1, size=(37, 29), dtype=np.int64).astype(np.int32)
-    acc[0, :6] = [5, 7, -5, 2049, 2051, 1000]
-    bias = rng.uniform(-3, 3, 29).astype(np.float32)
-    for alpha in (0.5, 1.0, 3.0517578125e-05, 1.7e-6):
-        a32 = np.float32(alpha)
-        v = (acc.astype(np.float32) * a32).astype(np.float32) + bias[None, :]
-        v = v.astype(np.float32)
-        want_i8 = np.clip(np.rint(v), -128, 127).astype(np.int8)
-        assert np.array_equal(oracle.requant(acc, alpha=alpha, bias=bias, out="i8"), want_i8)
-        v0 = (acc.astype(np.float32) * a32).astype(np.float32)
-        want_f16 = v0.astype(np.float16).view(np.uint16)
-        assert np.array_equal(oracle.requant(acc, alpha=alpha, out="f16"), want_f16)
+def _rne_fraction(x: Fraction, p: int, emin: int, maxv: Fraction):
+    """Exact round-to-nearest-even of a rational to a binary format with p
+    significand bits and minimum normal exponent emin (Python's round() on a
+    Fraction rounds halves to even); None past the overflow threshold."""
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - (p - 1))
+    q = round(a / ulp) * ulp
+    if q > maxv:
+        return None
+    return q if x > 0 else -q
+
+
+F32_MAX = (2 - Fraction(1, 2 ** 23)) * Fraction(2) ** 127
+
+
+def _f32(x: Fraction) -> Fraction:
+    return _rne_fraction(x, 24, -126, F32_MAX)
+
+
+def _requant_exact(acc: int, alpha: Fraction, bias, out: str):
+    """The requantise rule written out in exact rationals: v = f32(f32(f32(acc) *
+    alpha) + bias), then int8: round half to even and saturate, or fp16: round
+    half to even (as a rational, or +-inf)."""
+    v = _f32(_f32(_f32(Fraction(acc)) * alpha) + (bias if bias is not None else 0))
+    if out == "i8":
+        return max(-128, min(127, round(v)))
+    q = _rne_fraction(v, 11, -14, Fraction(65504))
+    return q if q is not None else (math.inf if v > 0 else -math.inf)
+
+
+def test_requant_against_exact_rational_steps():
+    # Each binary32 step rounded exactly with Fractions (no floating-point
+    # arithmetic of the host in the expected values): accumulators across the
+    # whole int32 range, so f32(acc) and the product round; scales that are and
+    # are not powers of two; a bias that does and does not change the rounding.
+    acc = [int(v) for v in synth.int_range(91, 160, -2 ** 31, 2 ** 31 - 1).numpy()]
+    acc[:8] = [5, 7, -5, 2049, 2051, 1000, 2 ** 24 + 1, -(2 ** 31)]
+    bias_vals = [Fraction(float(b)) for b in np.float32(synth.uniform(92, 160, -3, 3).numpy())]
+    for alpha in (0.5, 1.0, 3.0517578125e-05, 1.7e-6, 0.3):
+        a32 = _f32(Fraction(alpha))
+        A = np.array(acc, np.int32).reshape(16, 10)
+        Bv = np.array([float(b) for b in bias_vals[:10]], np.float32)
+        got_i8 = oracle.requant(A, alpha=alpha, bias=Bv, out="i8")
+        got_f16 = oracle.f16_values(oracle.requant(A, alpha=alpha, out="f16"))
+        for i in range(16):
+            for j in range(10):
+                want = _requant_exact(int(A[i, j]), a32, Fraction(float(Bv[j])), "i8")
+                assert int(got_i8[i, j]) == want, (alpha, int(A[i, j]), float(Bv[j]))
+                wf = _requant_exact(int(A[i, j]), a32, None, "f16")
+                assert got_f16[i, j] == float(wf), (alpha, int(A[i, j]))
+
+
+def test_requant_exact_cases_round_the_real_value_once():
+    # With a power-of-two scale, |acc| < 2^24 and a bias on a coarse grid, every
+    # binary32 step is exact: the result is the rounding of the real value
+    # alpha * acc + bias itself - ties to even, saturation at -128 and 127, and
+    # fp16 ties and overflow.
+    acc = np.array([[5, 7, -5, -7, 1, 3, 1000, -1000, 255, -257, 2 ** 23, -(2 ** 23)]], np.int32)
+    for k in (1, 2, 4):
+        alpha = 2.0 ** -k
+        for bias in (0.0, 0.25, -0.75, 1.5):
+            q = oracle.requant(acc, alpha=alpha, bias=np.full(acc.shape[1], bias, np.float32), out="i8")
+            for j, a in enumerate(acc[0].tolist()):
+                exact = Fraction(a, 2 ** k) + Fraction(bias)
+                assert int(q[0, j]) == max(-128, min(127, round(exact))), (a, k, bias)
     # ties to even and saturation, by hand
     q = oracle.requant(np.array([[5, 7, -5, 1000, -1000]], np.int32), alpha=0.5, out="i8")
     assert q.tolist() == [[2, 4, -2, 127, -128]]
-    h = oracle.requant(np.array([[2049, 2051]], np.int32), alpha=1.0, out="f16")
-    assert oracle.f16_values(h).tolist() == [[2048.0, 2052.0]]
+    # fp16: 2049 and 2051 lie halfway between fp16 neighbours (spacing 2 above
+    # 2048); 65519 rounds down to 65504 and 65520 up to infinity
+    h = oracle.requant(np.array([[2049, 2051, 65519, 65520, -65520]], np.int32), alpha=1.0, out="f16")
+    assert oracle.f16_values(h).tolist() == [[2048.0, 2052.0, 65504.0, math.inf, -math.inf]]
 
 
 def test_thread_count_determinism():
