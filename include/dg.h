@@ -281,6 +281,27 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K,
                   const dg_epilogue *epi, const dg_plan_opts *opts,
                   void *workspace, size_t workspace_bytes, dg_stream_t stream);
 
+/* dg_gemm for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace.  The split-K partial sums go to the
+ * library's static device scratch instead, DG_SCRATCH_BYTES per GPU (a
+ * file-scope device array: each GPU the library runs on holds it from the
+ * library's load until the process ends; its address on a device is taken by
+ * dg_create).  The planner only considers plans whose partial sums fit it;
+ * a forced K split (or a pad_k plan) needing more is DG_ERR_WORKSPACE, before
+ * anything is enqueued.  Nothing is allocated, copied or synchronised.
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * partial sums (every K slice overwrites its whole partial, so nothing needs
+ * clearing): calls that overlap on one GPU (concurrent streams, several
+ * threads) race, and must be ordered by the caller.
+ * Errors: as dg_gemm; DG_ERR_WORKSPACE when no plan fits the scratch. */
+#define DG_SCRATCH_BYTES (32u << 20)
+dg_status dg_gemm_noalloc(dg_handle_t h, int64_t M, int64_t N, int64_t K,
+                          const dg_dtypes *dt, const dg_layouts *lay,
+                          const void *A, const void *B, const void *b_scale, int32_t group_k,
+                          const void *D, void *C, const void *alpha, const void *beta,
+                          const dg_epilogue *epi, const dg_plan_opts *opts, dg_stream_t stream);
+
 /* MX block-scaled GEMM: the 4-bit weight scheme of the pages (e2m1 weights with
  * a scale per group of 32 along K, [overview] section 2.2, second layer; the
  * in-register weight unpack of section 4.3) with the activations quantised to

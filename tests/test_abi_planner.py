@@ -238,6 +238,9 @@ def test_offline_and_destroyed_handles_are_invalid_state():
     s = dg.dg_gemm(h.h, 16, 16, 16, C.byref(dt), C.byref(lay), 16, 16, None, 0, None, 16,
                    C.byref(one), C.byref(zero), None, None, None, 0, None)
     assert s == dg.DG_ERR_INVALID_STATE and "offline" in dg.dg_last_error()
+    s = dg.dg_gemm_noalloc(h.h, 16, 16, 16, C.byref(dt), C.byref(lay), 16, 16, None, 0, None, 16,
+                           C.byref(one), C.byref(zero), None, None, None)
+    assert s == dg.DG_ERR_INVALID_STATE and "offline" in dg.dg_last_error()
     # the stage clock needs a device handle, and a consistent buffer size
     assert dg.dg_set_stage_clock(h.h, None, 0) == dg.DG_ERR_INVALID_STATE
     raw = C.c_void_p(h.h.value)

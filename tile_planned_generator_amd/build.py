@@ -18,7 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdg.so")
 
 KERNEL_SOURCES = ["gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip",
-                  "gemm_tiled_e2m1.hip", "gemm_tiled_mx.hip", "quant_mx.hip", "skinny.hip", "probe.hip"]
+                  "gemm_tiled_e2m1.hip", "gemm_tiled_mx.hip", "quant_mx.hip", "skinny.hip", "probe.hip",
+                  "scratch.hip"]
 HOST_SOURCES = ["gemm_tiled.hip", "api.cpp", "planner.cpp"]
 # kernel sources that issue transposing LDS reads (row-major B operands)
 TILED_TR_SOURCES = ["gemm_tiled_f16.hip", "gemm_tiled_bf16.hip", "gemm_tiled_i8.hip"]

@@ -160,8 +160,9 @@ dg_plan_opts opts_or_default(const dg_plan_opts *o)
 std::string cache_key(const Problem &p, const dg_plan_opts &o)
 {
     char k[256];
-    std::snprintf(k, sizeof k, "%lld,%lld,%lld+%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
-                  (long long)p.M, (long long)p.N, (long long)p.K, (long long)p.k_pad, p.path, p.b_kmajor,
+    std::snprintf(k, sizeof k, "%lld,%lld,%lld+%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
+                  (long long)p.M, (long long)p.N, (long long)p.K, (long long)p.k_pad, (long long)p.ws_limit,
+                  p.path, p.b_kmajor,
                   p.out_type, p.epi,
                   p.beta_nz, o.force_m_tile, o.force_n_tile, o.force_k_tile, o.force_split_k, o.force_path,
                   o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k, o.force_waves);
@@ -256,6 +257,10 @@ dg_status dg_create(dg_handle_t *out, int hip_device)
         if (e != hipSuccess) return fail(DG_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
         if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
             return fail(DG_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
+        // the static scratch of dg_gemm_noalloc: its address on this device
+        e = scratch_init(hip_device);
+        if (e != hipSuccess)
+            return fail(DG_ERR_HIP, std::string("static scratch address: ") + hipGetErrorString(e));
         dg_handle_s *h = new dg_handle_s();
         dg_default_device_desc(&h->desc);
         h->desc.cu_count = prop.multiProcessorCount;
@@ -512,12 +517,18 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K, con
     }
 }
 
-dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
-                  const void *A, const void *B, const void *b_scale, int32_t group_k, const void *D, void *C,
-                  const void *alpha, const void *beta, const dg_epilogue *epi, const dg_plan_opts *opts,
-                  void *workspace, size_t workspace_bytes, dg_stream_t stream)
+}  // extern "C"
+
+namespace {
+
+// dg_gemm and dg_gemm_noalloc.  ws_limit >= 0: the workspace is the static
+// scratch of that many bytes, and the planner only keeps plans that fit it.
+dg_status gemm_impl(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
+                    const void *A, const void *B, const void *b_scale, int32_t group_k, const void *D, void *C,
+                    const void *alpha, const void *beta, const dg_epilogue *epi, const dg_plan_opts *opts,
+                    void *workspace, size_t workspace_bytes, dg_stream_t stream, int64_t ws_limit)
 {
-    try {
+    {
         if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
         if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: planning only");
         if (!dt || !alpha || !beta) return fail(DG_ERR_INVALID_ARG, "dtypes, alpha and beta are required");
@@ -534,6 +545,7 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
         Problem pr;
         dg_status s = describe(M, N, K, dt, lay, group_k, E.kind, beta_nz, opts_or_default(opts).pad_k, pr);
         if (s) return s;
+        pr.ws_limit = ws_limit;
         const bool rq = E.kind == DG_EPI_REQUANT_I8 || E.kind == DG_EPI_REQUANT_F16;
         if (rq && ia != 1) return fail(DG_ERR_INVALID_ARG, "requantise epilogues need alpha == 1 (use epi->scale)");
         int cur = -1;
@@ -575,6 +587,9 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
                 (pr.path == P_E2M1 && (K / 32) * (N + (N & 1)) * 2 >= (int64_t(1) << 32)))
                 return fail(DG_ERR_UNSUPPORTED, "an operand spans 4 GiB or more (32-bit offsets of the tiled path)");
         }
+        if (ws_limit >= 0 && c.ws_bytes > ws_limit)
+            return fail(DG_ERR_WORKSPACE, "the plan's partial sums need " + std::to_string(c.ws_bytes) +
+                                              " bytes; the static scratch holds " + std::to_string(ws_limit));
         if (c.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)c.ws_bytes))
             return fail(DG_ERR_WORKSPACE, "workspace missing or smaller than " + std::to_string(c.ws_bytes) + " bytes");
         if (c.ws_bytes > 0 && !aligned(workspace, 16)) return fail(DG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
@@ -682,8 +697,42 @@ dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtype
             if (he != hipSuccess) return fail(DG_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
         }
         return ok();
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_gemm(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt, const dg_layouts *lay,
+                  const void *A, const void *B, const void *b_scale, int32_t group_k, const void *D, void *C,
+                  const void *alpha, const void *beta, const dg_epilogue *epi, const dg_plan_opts *opts,
+                  void *workspace, size_t workspace_bytes, dg_stream_t stream)
+{
+    try {
+        return gemm_impl(h, M, N, K, dt, lay, A, B, b_scale, group_k, D, C, alpha, beta, epi, opts, workspace,
+                         workspace_bytes, stream, -1);
     } catch (...) {
         return fail(DG_ERR_INTERNAL, "exception in dg_gemm");
+    }
+}
+
+dg_status dg_gemm_noalloc(dg_handle_t h, int64_t M, int64_t N, int64_t K, const dg_dtypes *dt,
+                          const dg_layouts *lay, const void *A, const void *B, const void *b_scale,
+                          int32_t group_k, const void *D, void *C, const void *alpha, const void *beta,
+                          const dg_epilogue *epi, const dg_plan_opts *opts, dg_stream_t stream)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (h->device < 0) return fail(DG_ERR_INVALID_STATE, "offline handle: planning only");
+        // the address dg_create looked up on the handle's device (never the
+        // array's host-side name)
+        void *ptr = scratch_ptr(h->device);
+        if (!ptr) return fail(DG_ERR_INVALID_STATE, "no static scratch address for the handle's device");
+        return gemm_impl(h, M, N, K, dt, lay, A, B, b_scale, group_k, D, C, alpha, beta, epi, opts, ptr,
+                         DG_SCRATCH_BYTES, stream, DG_SCRATCH_BYTES);
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_gemm_noalloc");
     }
 }
 

@@ -31,6 +31,12 @@ hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 // pad_k: the K tail past the aligned part, as one more partial slice.
 hipError_t launch_tail(const TailArgs &a, hipStream_t s);
 
+// Static device scratch of dg_gemm_noalloc (DG_SCRATCH_BYTES per GPU):
+// scratch_init looks up its address on `device` (once; the device is made
+// current for the lookup and restored), scratch_ptr returns it (NULL before).
+hipError_t scratch_init(int device);
+void *scratch_ptr(int device);
+
 // Hardware probe kernels (dg_probe): kind 0 stream read, 1 MFMA, 2 LDS banks.
 hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s);
 

@@ -186,6 +186,22 @@ double hbm_us(double bytes, const dg_device_desc &d) { return bytes / (d.hbm_gbp
 
 constexpr double LAUNCH_US = 2.0;
 
+// Workspace bytes of a plan with S slices: the partial sums, with one more
+// slice for the pad_k tail (which is then the only slice when the aligned
+// part of K is empty).
+int64_t plan_ws_bytes(const Problem &pr, int S)
+{
+    if (pr.k_pad) return ((pr.K == 0 ? 0 : S) + 1) * pr.M * pr.N * 4;
+    return S > 1 ? (int64_t)S * pr.M * pr.N * 4 : 0;
+}
+
+// The problem's workspace limit rules this plan out (a forced split is kept:
+// the caller reports it).
+bool over_ws_limit(const Problem &pr, int S, const dg_plan_opts &o)
+{
+    return pr.ws_limit >= 0 && !o.force_split_k && plan_ws_bytes(pr, S) > pr.ws_limit;
+}
+
 }  // namespace
 
 double roofline_us(const Problem &pr, const dg_device_desc &d)
@@ -201,7 +217,7 @@ double roofline_us(const Problem &pr, const dg_device_desc &d)
 
 // ------------------------------------------------------------------ families
 static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
-                       std::vector<Candidate> &out, int &enumerated, int &pruned)
+                       std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
     const int BKE = tiled_bk_elems(pr.path), KSUB = tiled_ksub(pr.path);
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
@@ -250,6 +266,10 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             else if (o.force_k_tile && o.force_k_tile != BKE) why = "forced K tile";
             else if (o.force_waves && o.force_waves != waves) why = "forced wave count";
             else if (S_eff != S && !o.force_split_k) why = "split collapses";
+            else if (over_ws_limit(pr, S_eff, o)) {
+                why = "workspace over the limit";
+                ++ws_pruned;
+            }
             if (why) {
                 ++pruned;
                 if (log_on())
@@ -314,7 +334,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
 // (S_eff) is kept as a plan with S_eff slices (the streaming kernels take any
 // slice count).
 static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
-                        std::vector<Candidate> &out, int &enumerated, int &pruned)
+                        std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
     if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves) return;  // tiled-only options
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
@@ -377,6 +397,10 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 else if (lds > lds_cap) why = "LDS over budget";
                 else if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
+                else if (over_ws_limit(pr, S_eff, o)) {
+                    why = "workspace over the limit";
+                    ++ws_pruned;
+                }
                 if (why) {
                     ++pruned;
                     continue;
@@ -422,6 +446,10 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 const char *why = nullptr;
                 if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
+                else if (over_ws_limit(pr, S_eff, o)) {
+                    why = "workspace over the limit";
+                    ++ws_pruned;
+                }
                 if (why) {
                     ++pruned;
                     continue;
@@ -468,6 +496,10 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
                 else if (lds_e > lds_cap) why = "LDS over budget";
                 else if (occ < occ_need) why = "occupancy below target";
                 else if (o.force_path == DG_PATH_TILED) why = "forced tiled path";
+                else if (over_ws_limit(pr, S_eff, o)) {
+                    why = "workspace over the limit";
+                    ++ws_pruned;
+                }
                 if (why) {
                     ++pruned;
                     continue;
@@ -531,8 +563,16 @@ PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_pla
         res.message = "forced tile sizes apply to the tiled path, the skinny path was forced";
         return res;
     }
-    if (want_tiled) enum_tiled(pr, d, o, all, res.enumerated, res.pruned);
-    if (want_skinny) enum_skinny(pr, d, o, all, res.enumerated, res.pruned);
+    if (want_tiled) enum_tiled(pr, d, o, all, res.enumerated, res.pruned, res.ws_pruned);
+    if (want_skinny) enum_skinny(pr, d, o, all, res.enumerated, res.pruned, res.ws_pruned);
+    if (all.empty() && res.ws_pruned > 0) {
+        res.status = DG_ERR_WORKSPACE;
+        char m[160];
+        std::snprintf(m, sizeof m, "no plan's partial sums fit the %lld-byte workspace limit "
+                      "(%d candidates pruned by it)", (long long)pr.ws_limit, res.ws_pruned);
+        res.message = m;
+        return res;
+    }
     if (all.empty()) {
         res.status = DG_ERR_NO_CANDIDATE;
         char m[160];

@@ -21,6 +21,8 @@ struct Problem {
     int epi;         // EpiKind
     int beta_nz;     // D is read
     int64_t k_pad = 0;   // pad_k: K elements past K (K is then the aligned part)
+    int64_t ws_limit = -1;   // >= 0: prune plans whose partial sums need more bytes
+                             // (a forced split is kept and checked by the caller)
 };
 
 struct Candidate {
@@ -44,6 +46,7 @@ struct PlanResult {
     std::string message;
     std::vector<Candidate> pareto;   // best first
     int enumerated = 0, pruned = 0;
+    int ws_pruned = 0;   // candidates pruned by ws_limit
 };
 
 // Enumerate, prune, score, Pareto-filter.  Deterministic.

@@ -85,7 +85,7 @@ class dg_plan_info(C.Structure):
 
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
-           "dg_plan_candidates", "dg_plan_range", "dg_gemm", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
+           "dg_plan_candidates", "dg_plan_range", "dg_gemm", "dg_gemm_noalloc", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
            "dg_probe", "dg_set_device_desc", "dg_last_error", "dg_status_str")
 
 _lib = None
@@ -117,6 +117,8 @@ def load():
         "dg_gemm": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), P, P, P, i32,
                      P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t,
                      P], S),
+        "dg_gemm_noalloc": ([H, i64, i64, i64, C.POINTER(dg_dtypes), C.POINTER(dg_layouts), P, P, P, i32,
+                             P, P, P, P, C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P], S),
         "dg_gemm_mx": ([H, i64, i64, i64, P, i64, P, i64, P, i64, P, i64, P, i32, i64, C.c_float,
                         C.POINTER(dg_epilogue), C.POINTER(dg_plan_opts), P, C.c_size_t, P], S),
         "dg_quant_mx": ([H, i64, i64, P, i64, P, i64, P, i64, P], S),
@@ -165,6 +167,10 @@ def dg_plan_range(*a):
 
 def dg_gemm(*a):
     return load().dg_gemm(*a)
+
+
+def dg_gemm_noalloc(*a):
+    return load().dg_gemm_noalloc(*a)
 
 
 def dg_gemm_mx(*a):
@@ -369,8 +375,9 @@ class Handle:
 
     def gemm(self, A, B, C_out, *, alpha=1.0, beta=0.0, D=None, bias=None, epilogue="none",
              b_scale=None, b_layout=None, K=None, requant_scale=1.0, opts=None, workspace=None,
-             stream=None):
-        """C_out = act(alpha * A.B + beta * D + bias) through dg_gemm.
+             stream=None, noalloc=False):
+        """C_out = act(alpha * A.B + beta * D + bias) through dg_gemm (through
+        dg_gemm_noalloc, with the library's static scratch, when ``noalloc``).
 
         A: [M, K] (row-major, rows may be padded: A.stride(0) is lda).
         B: [K, N] row-major, or, with b_layout=DG_COL_MAJOR, [N, K]; for e2m1 the
@@ -410,14 +417,21 @@ class Handle:
             al, be = C.c_float(float(alpha)), C.c_float(float(beta))
         epi = dg_epilogue(EPI[epilogue], DTYPE[_dtype_name(bias)] if bias is not None else 0,
                           bias.data_ptr() if bias is not None else None, float(requant_scale))
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device).cuda_stream
+        if noalloc:
+            check(dg_gemm_noalloc(self.h, M, N, K, C.byref(dt), C.byref(lay), A.data_ptr(), B.data_ptr(),
+                                  b_scale.data_ptr() if b_scale is not None else None, 32 if e2m1 else 0,
+                                  D.data_ptr() if D is not None else None, C_out.data_ptr(), C.byref(al),
+                                  C.byref(be), C.byref(epi), C.byref(opts) if opts is not None else None,
+                                  stream))
+            return None
         info = self.plan(M, N, K, a, b, c, b_layout, epilogue, opts=opts, lda=lda, ldb=ldb,
                          ldc=ldc, ldd=ldd)
         if workspace is None and info.workspace_bytes > 0:
             workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=A.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        if stream is None:
-            stream = torch.cuda.current_stream(A.device).cuda_stream
         check(dg_gemm(self.h, M, N, K, C.byref(dt), C.byref(lay), A.data_ptr(), B.data_ptr(),
                       b_scale.data_ptr() if b_scale is not None else None, 32 if e2m1 else 0,
                       D.data_ptr() if D is not None else None, C_out.data_ptr(), C.byref(al),
