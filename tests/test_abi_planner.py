@@ -156,13 +156,38 @@ def test_forced_tile_and_split(off):
 
 
 def test_variable_k_schedule_tail(off):
-    # K = 4096 + 48: 129 full steps of 32 and one tail step of 16 (one MFMA depth)
-    o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_split_k=1)
-    p = off.plan(512, 512, 4096 + 48, opts=o)
-    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (32, 129, 16, 1)
-    # int8, K = 4096 + 96: 65 full steps of 64 and one tail step of 32
-    p = off.plan(512, 512, 4096 + 96, "i8", "i8", "i32", opts=o)
-    assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == (64, 65, 32, 1)
+    # K = 4096 + 48 with the 32-k step: 129 full steps and one tail step of 16
+    # (one MFMA depth); with the 64-k step: 64 full steps and a tail of 48
+    for kt, want in ((32, (32, 129, 16, 1)), (64, (64, 64, 48, 1))):
+        o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_split_k=1, force_k_tile=kt)
+        p = off.plan(512, 512, 4096 + 48, opts=o)
+        assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == want
+    # int8, K = 4096 + 96: 65 steps of 64 and a tail of 32, or 32 steps of 128
+    # and a tail of 96
+    for kt, want in ((64, (64, 65, 32, 1)), (128, (128, 32, 96, 1))):
+        o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_split_k=1, force_k_tile=kt)
+        p = off.plan(512, 512, 4096 + 96, "i8", "i8", "i32", opts=o)
+        assert (p.k_main, p.n_main, p.k_tail, p.n_tail) == want
+
+
+def test_k_tile_is_a_planner_dimension(off):
+    # the compiled K steps of each path are enumerated: the candidate set of a
+    # large problem holds plans with different K steps, and a K step that no
+    # variant of the path compiles is pruned
+    for a, c, steps in (("f16", "f16", {32, 64}), ("bf16", "bf16", {32, 64}), ("i8", "i32", {64, 128})):
+        seen = set()
+        for kt in sorted(steps):
+            o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_k_tile=kt)
+            for p in off.candidates(4096, 4096, 4096, a, a, c, opts=o):
+                assert p.k_main == kt
+                seen.add(p.k_main)
+        assert seen == steps
+        with pytest.raises(dg.DGError) as e:
+            off.plan(4096, 4096, 4096, a, a, c, opts=dg.dg_plan_opts(force_k_tile=48))
+        assert e.value.status == dg.DG_ERR_NO_CANDIDATE
+    # e2m1 and MX compile one K step
+    assert {p.k_main for p in off.candidates(4096, 4096, 4096, "f16", "e2m1", "f16",
+                                             dg.DG_COL_MAJOR)} <= {32}
 
 
 def test_skinny_shapes_choose_streaming_path(off):
@@ -289,26 +314,29 @@ def test_planner_uses_the_compiled_resource_usage(off):
     # compiler reported for each variant (no spills allowed at build time)
     rows = _resources()
     assert rows and all(r[-1] == 0 for r in rows)
-    tiled = {tuple(r[1:7]): r for r in rows if r[0] == 0}
+    tiled = {tuple(r[1:8]): r for r in rows if r[0] == 0}
     names = {"f16": 0, "bf16": 1, "i8": 2, "e2m1": 3}
+    region_k = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32}
     for M, N, K, a, b, c, epi in PROBLEMS:
         for p in off.candidates(M, N, K, a, b, c, epilogue=epi):
             if p.path != dg.DG_PATH_TILED:
                 continue
             nm = p.kernel_name.decode().split("_")
-            wm, wn = map(int, nm[-1][1:].split("x"))
-            key = (names[nm[1]], 1 if nm[2] == "k" else 0, p.m_tile, p.n_tile, wm, wn)
+            wm, wn = map(int, nm[-2][1:].split("x"))
+            kr = int(nm[-1][1:]) // region_k[nm[1]]
+            assert p.k_main == int(nm[-1][1:])
+            key = (names[nm[1]], 1 if nm[2] == "k" else 0, p.m_tile, p.n_tile, wm, wn, kr)
             r = tiled[key]
-            assert (p.vgpr_est, p.agpr_est, p.lds_bytes) == (r[7], r[8], r[9])
-            assert p.waves_per_simd == r[10]
+            assert (p.vgpr_est, p.agpr_est, p.lds_bytes) == (r[8], r[9], r[10])
+            assert p.waves_per_simd == r[11]
     # occupancy 2/8 keeps only variants the compiler gave >= 2 waves per SIMD
     o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, target_occupancy=0.25)
     p = off.plan(2048, 2048, 2048, opts=o)
-    assert p.kernel_name.decode().endswith("w2x4") and p.waves_per_simd >= 2
-    for nw, suffix in ((4, "w2x2"), (8, "w2x4")):
+    assert "_w2x4_" in p.kernel_name.decode() and p.waves_per_simd >= 2
+    for nw, part in ((4, "_w2x2_"), (8, "_w2x4_")):
         o = dg.dg_plan_opts(force_m_tile=256, force_waves=nw)
         p = off.plan(2048, 2048, 2048, opts=o)
-        assert p.kernel_name.decode().endswith(suffix) and p.waves_per_wg == nw
+        assert part in p.kernel_name.decode() and p.waves_per_wg == nw
 
 
 def test_stage_cycles_summary():
@@ -467,9 +495,17 @@ def _range_samples(K_min, K_max, unit):
     return ks
 
 
-def _variants(off, path_b, bm_list=((128, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4))):
-    out = [dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=bm, force_n_tile=bn, force_waves=w)
-           for bm, bn, w in bm_list]
+# the compiled tiled variants of the 16-bit and int8 paths: (M tile, N tile,
+# waves, K regions per step)
+TILED_VARIANTS = ((128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
+                  (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2))
+
+
+def _variants(off, path_b, bm_list=TILED_VARIANTS):
+    region = 64 if path_b == "i8" else 32
+    out = [dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=bm, force_n_tile=bn, force_waves=w,
+                           force_k_tile=region * kr)
+           for bm, bn, w, kr in bm_list]
     out.append(dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY))
     return out
 
@@ -487,12 +523,12 @@ def test_plan_range_minimises_the_worst_ratio(off, M, N, K_min, K_max, a, c):
     worst = {}
     for v in _variants(off, a):
         try:
-            worst[(v.force_path, v.force_m_tile, v.force_n_tile, v.force_waves)] = max(
+            worst[(v.force_path, v.force_m_tile, v.force_n_tile, v.force_waves, v.force_k_tile)] = max(
                 off.plan(M, N, k, a, a, c, opts=v).est_us / b for k, b in zip(ks, best))
         except dg.DGError:
             pass
     ro, info, w = off.plan_range(M, N, K_min, K_max, a, a, c)
-    key = (ro.force_path, ro.force_m_tile, ro.force_n_tile, ro.force_waves)
+    key = (ro.force_path, ro.force_m_tile, ro.force_n_tile, ro.force_waves, ro.force_k_tile)
     assert key in worst and abs(worst[key] - w) < 1e-9
     assert w <= min(worst.values()) + 1e-9 and w >= 1.0 - 1e-12
     # the pinned variant plans every K of the range (on the MFMA depth)

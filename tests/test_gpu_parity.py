@@ -333,24 +333,39 @@ def test_e2m1_odd_n(h, M, N, K, path):
     run(h, w, opts=dg.dg_plan_opts(force_path=path))
 
 
+# compiled tiled variants: (M tile, N tile, waves, K regions per step); the
+# double K step exists for the 16-bit and int8 paths
+TILED_VARIANTS = ((128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
+                  (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2))
+
+
 def test_every_tiled_variant_on_a_ragged_problem(h):
-    # each compiled tile shape, forced in turn, on a problem with ragged M and N,
-    # a K tail (K = 7 full steps + a half step; e2m1 K is whole 32-groups, so
-    # 8 full steps) and a K split (slices of 4 and 3.5 steps: fewer steps than
-    # LDS stages)
+    # each compiled variant (tile shape, wave grid, K step), forced in turn, on a
+    # problem with ragged M and N, a K tail and a K split: one K region per step
+    # with K = 7 full steps + a half step (e2m1 K is whole 32-groups, so 8 full
+    # steps), two regions per step with K = 3 full steps + a tail of one, two or
+    # three substeps; split 2 gives slices with fewer steps than LDS stages
     for path, name, colm in (("f16", "f16_2048x2048x8192_bias_gelu", False),
                              ("f16", "f16_2048x2048x8192_bias_gelu", True),
                              ("bf16", "bf16_16x4096x131072", False),
                              ("i8", "i8_4096x4096x4096", False),
                              ("i8", "i8_4096x4096x4096", True),
                              ("e2m1", "e2m1_4096x4096x4096", True)):
-        ktail = {"i8": 7 * 64 + 32, "e2m1": 8 * 32}.get(path, 7 * 32 + 16)
-        w = synth.make(name, M=290, N=272, K=ktail)
-        for bm, bn, nw in ((128, 256, 4), (256, 256, 8), (256, 128, 4), (128, 128, 4), (64, 64, 4)):
-            for s in (1, 2):
-                o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
-                                    force_path=dg.DG_PATH_TILED, force_waves=nw)
-                run(h, w, b_colmajor=colm, opts=o)
+        region = 64 if path == "i8" else 32
+        for bm, bn, nw, kr in TILED_VARIANTS:
+            if kr > 1 and path == "e2m1":
+                continue
+            if kr == 1:
+                ks = [8 * 32] if path == "e2m1" else [7 * region + region // 2]
+            else:
+                ks = [3 * 2 * region + t * region // 2 for t in (1, 2, 3)]
+            for K in ks:
+                w = synth.make(name, M=290, N=272, K=K)
+                for s in (1, 2):
+                    o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
+                                        force_path=dg.DG_PATH_TILED, force_waves=nw, force_k_tile=region * kr)
+                    info, _ = run(h, w, b_colmajor=colm, opts=o)
+                    assert info.k_main == region * kr and info.waves_per_wg == nw
 
 
 def test_split_k_and_schedule_tail(h):
@@ -476,11 +491,12 @@ def test_k_zero_and_empty(h):
     run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=0))
     run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=40, N=64, K=0))
     # every loop shape with an empty K range (eight-wave and four-wave tiles)
-    for bm, bn, nw in ((256, 256, 8), (128, 256, 4), (128, 128, 4)):
-        o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_path=dg.DG_PATH_TILED,
-                            force_waves=nw)
-        run(h, synth.make("f16_256x256x256_alpha_beta_d", M=300, N=260, K=0), opts=o)
-        run(h, synth.make("i8_4096x4096x4096", M=300, N=260, K=0), opts=o)
+    # (the K step: regions of 32 k for 16-bit operands, 64 k for int8)
+    for bm, bn, nw, kr in ((256, 256, 8, 1), (128, 256, 4, 1), (128, 128, 4, 1), (256, 256, 4, 2)):
+        for name, region in (("f16_256x256x256_alpha_beta_d", 32), ("i8_4096x4096x4096", 64)):
+            o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_path=dg.DG_PATH_TILED,
+                                force_waves=nw, force_k_tile=region * kr)
+            run(h, synth.make(name, M=300, N=260, K=0), opts=o)
     # M = 0 or N = 0: nothing to do, nothing launched
     Ce = torch.empty(0, 64, dtype=torch.float16, device=DEV)
     h.gemm(torch.empty(0, 16, dtype=torch.float16, device=DEV),

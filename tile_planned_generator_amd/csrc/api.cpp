@@ -400,8 +400,8 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
         if (!range_opts) return fail(DG_ERR_INVALID_ARG, "range_opts is NULL");
         if (K_min < 0 || K_max < K_min) return fail(DG_ERR_INVALID_ARG, "K range must satisfy 0 <= K_min <= K_max");
         const dg_plan_opts o = opts_or_default(opts);
-        if (o.force_m_tile || o.force_n_tile || o.force_waves || o.force_path)
-            return fail(DG_ERR_CONFLICT, "a K range plan chooses the variant: leave tile, waves and path free");
+        if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves || o.force_path)
+            return fail(DG_ERR_CONFLICT, "a K range plan chooses the variant: leave tile, K step, waves and path free");
         // every K of the range must be a valid problem; both ends decide that
         // (alignment and leading dimensions only tighten as K grows or shrinks)
         Problem lo, hi;
@@ -433,7 +433,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
         };
         std::vector<Var> vars;
         const TiledShape shapes[] = {
-#define DG_TS(path, kmaj, bm, bn, wm, wn) {path, kmaj, bm, bn, wm, wn},
+#define DG_TS(path, kmaj, bm, bn, wm, wn, kr) {path, kmaj, bm, bn, wm, wn, kr},
             DG_TILED_CATALOGUE(DG_TS)
 #undef DG_TS
         };
@@ -445,6 +445,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
             v.force_m_tile = t.bm;
             v.force_n_tile = t.bn;
             v.force_waves = t.wm * t.wn;
+            v.force_k_tile = tiled_bk_elems(t.path) * t.kr;
             tries.push_back(v);
         }
         {

@@ -9,26 +9,42 @@
 
 namespace dg {
 
-// Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN)
+// Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN, KR)
 //   path      P_F16 / P_BF16 / P_I8 / P_E2M1 / P_MX
 //   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
 //   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
-#define DG_TILE_SHAPES(X, path, kmaj) \
-    X(path, kmaj, 128, 256, 2, 2)     \
-    X(path, kmaj, 256, 256, 2, 4)     \
-    X(path, kmaj, 256, 128, 2, 2)     \
-    X(path, kmaj, 128, 128, 2, 2)     \
-    X(path, kmaj, 64, 64, 2, 2)
+//   KR        64-byte K regions per K step: the K step (K_tile) is KR x 32 k
+//             for 16-bit operands and KR x 64 k for int8 (e2m1 and MX: KR = 1)
+#define DG_TILE_SHAPES(X, path, kmaj)  \
+    X(path, kmaj, 128, 256, 2, 2, 1)   \
+    X(path, kmaj, 256, 256, 2, 4, 1)   \
+    X(path, kmaj, 256, 128, 2, 2, 1)   \
+    X(path, kmaj, 128, 128, 2, 2, 1)   \
+    X(path, kmaj, 64, 64, 2, 2, 1)
+// The double K step (two regions per LDS stage, four MFMA substeps per
+// barrier), four-wave tiles only.
+#define DG_TILE_SHAPES_K2(X, path, kmaj) \
+    X(path, kmaj, 256, 256, 2, 2, 2)     \
+    X(path, kmaj, 128, 256, 2, 2, 2)     \
+    X(path, kmaj, 256, 128, 2, 2, 2)     \
+    X(path, kmaj, 128, 128, 2, 2, 2)     \
+    X(path, kmaj, 64, 64, 2, 2, 2)
 
-#define DG_TILED_CATALOGUE(X)       \
-    DG_TILE_SHAPES(X, P_F16, 0)     \
-    DG_TILE_SHAPES(X, P_F16, 1)     \
-    DG_TILE_SHAPES(X, P_BF16, 0)    \
-    DG_TILE_SHAPES(X, P_BF16, 1)    \
-    DG_TILE_SHAPES(X, P_I8, 0)      \
-    DG_TILE_SHAPES(X, P_I8, 1)      \
-    DG_TILE_SHAPES(X, P_E2M1, 1)    \
-    DG_TILE_SHAPES(X, P_MX, 1)
+#define DG_TILED_CATALOGUE(X)          \
+    DG_TILE_SHAPES(X, P_F16, 0)        \
+    DG_TILE_SHAPES(X, P_F16, 1)        \
+    DG_TILE_SHAPES(X, P_BF16, 0)       \
+    DG_TILE_SHAPES(X, P_BF16, 1)       \
+    DG_TILE_SHAPES(X, P_I8, 0)         \
+    DG_TILE_SHAPES(X, P_I8, 1)         \
+    DG_TILE_SHAPES(X, P_E2M1, 1)       \
+    DG_TILE_SHAPES(X, P_MX, 1)         \
+    DG_TILE_SHAPES_K2(X, P_F16, 0)     \
+    DG_TILE_SHAPES_K2(X, P_F16, 1)     \
+    DG_TILE_SHAPES_K2(X, P_BF16, 0)    \
+    DG_TILE_SHAPES_K2(X, P_BF16, 1)    \
+    DG_TILE_SHAPES_K2(X, P_I8, 0)      \
+    DG_TILE_SHAPES_K2(X, P_I8, 1)
 
 // Skinny VALU streaming GEMM over a row-major 16-bit B:
 // X(path, MR, LPR): up to MR rows of A; LPR lanes span one row of B (8 columns each).
@@ -49,7 +65,7 @@ namespace dg {
 
 // Resource facts of the variants, used by the planner's constraints.
 struct TiledShape {
-    int path, b_kmajor, bm, bn, wm, wn;
+    int path, b_kmajor, bm, bn, wm, wn, kr;
 };
 
 // Fewest direct-to-LDS loads any wave issues per stage when load i of an
@@ -66,9 +82,9 @@ constexpr int tiled_min_loads_per_wave(int a_nl, int b_nl, int s_nl, int nw)
     return m;
 }
 
-// k elements per K step (two MFMA substeps) and per MFMA.  MX: one
-// 32x32x64 block-scaled MFMA per substep, so a step is 128 k (two 64-byte rows
-// of fp8 A per row of the tile).
+// k elements per 64-byte K region (two MFMA substeps; a K step holds KR
+// regions) and per MFMA.  MX: one 32x32x64 block-scaled MFMA per substep, so
+// its one-region step is 128 k (two 64-byte rows of fp8 A per row of the tile).
 constexpr int tiled_bk_elems(int path) { return path == 4 /*P_MX*/ ? 128 : (path == 2 /*P_I8*/ ? 64 : 32); }
 constexpr int tiled_ksub(int path) { return path == 4 /*P_MX*/ ? 64 : (path == 2 /*P_I8*/ ? 32 : 16); }
 
@@ -77,8 +93,9 @@ constexpr int tiled_ksub(int path) { return path == 4 /*P_MX*/ ? 64 : (path == 2
 // 2048x2048x8192 workloads (fp16; int8 and e2m1 relative to it).  It folds in
 // what a peak-rate model leaves out: the engine clock under MFMA load (about
 // 1.9-2.0 GHz, not 2.4), the LDS-bound fragment reads and the barriers.
-constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
+constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves, int kr = 1)
 {
+    (void)kr;
     const double base = waves == 8 ? 0.48
                       : bm * bn >= 256 * 128 ? 0.40
                       : bm * bn >= 128 * 128 ? 0.30 : 0.15;
@@ -91,27 +108,31 @@ constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves)
 // per column plus the step's fp16 scales (whole 256-byte loads).  MX: two 64-byte rows of fp8 A per tile
 // row, 64 bytes of e2m1 codes per column, and 2 KB of e8m0 scales (a 256-byte
 // chunk per operand and group of the step).
-constexpr int tiled_stage_bytes(int path, int bm, int bn)
+constexpr int tiled_stage_bytes(int path, int bm, int bn, int kr = 1)
 {
     return path == 4 ? bm * 128 + bn * 64 + 2048
-         : bm * 64 + (path == 3 ? bn * 16 + (bn * 2 + 255) / 256 * 256 : bn * 64);
+         : (path == 3 ? bm * 64 + bn * 16 + (bn * 2 + 255) / 256 * 256 : kr * (bm * 64 + bn * 64));
 }
 // LDS stages: five for the eight-wave variants when they fit gfx950's 160 KB
 // (the loads of a stage are then issued a phase later, in the MFMA phase, with
-// the same lookahead), four otherwise; MX stages are larger, so as many as fit,
-// at most four (at least three).
-constexpr int tiled_nbuf(int path, int bm, int bn, int wm, int wn)
+// the same lookahead), four otherwise; MX stages and double K steps are
+// larger: as many as fit, at most four (at least two for a double K step,
+// three for MX).
+constexpr int tiled_nbuf(int path, int bm, int bn, int wm, int wn, int kr = 1)
 {
     return path == 4 ? (4 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 4 : 3)
-                     : (wm * wn == 8 && 5 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 5 : 4);
+         : kr > 1   ? (4 * tiled_stage_bytes(path, bm, bn, kr) <= 163840
+                           ? 4
+                           : (3 * tiled_stage_bytes(path, bm, bn, kr) <= 163840 ? 3 : 2))
+                    : (wm * wn == 8 && 5 * tiled_stage_bytes(path, bm, bn) <= 163840 ? 5 : 4);
 }
 // The epilogue reuses the LDS to stage 32 rows of every wave's accumulators
 // (4-byte values, rows padded by 4): the allocation is the larger of the two.
-constexpr int tiled_lds_bytes(int path, int bm, int bn, int wm, int wn)
+constexpr int tiled_lds_bytes(int path, int bm, int bn, int wm, int wn, int kr = 1)
 {
-    return tiled_nbuf(path, bm, bn, wm, wn) * tiled_stage_bytes(path, bm, bn) >
+    return tiled_nbuf(path, bm, bn, wm, wn, kr) * tiled_stage_bytes(path, bm, bn, kr) >
                    wm * wn * 32 * (bn / wn + 4) * 4
-               ? tiled_nbuf(path, bm, bn, wm, wn) * tiled_stage_bytes(path, bm, bn)
+               ? tiled_nbuf(path, bm, bn, wm, wn, kr) * tiled_stage_bytes(path, bm, bn, kr)
                : wm * wn * 32 * (bn / wn + 4) * 4;
 }
 

@@ -5,16 +5,19 @@
 //     directly (buffer_load_dwordx4 ... lds): no staging registers and no LDS
 //     store instructions.  The buffer range check returns zeros past the end of
 //     an operand, so ragged rows need no clamping.
-//   - Four LDS stages of one K step each (32 k for 16-bit and e2m1 operands, 64 k
-//     for int8: two MFMA k-substeps).  Step st runs its first substep, then one
-//     barrier, then its second substep; the barrier is placed where every wave
-//     holds both fragments of stage st in registers, so right after it the loads
-//     of stage st+4 are issued into stage st's buffer.  Loads therefore have
-//     three steps to land.  The barrier waits only for this wave's loads of the
-//     next stage (vmcnt with the later stages still in flight) and for its LDS
-//     reads; the workgroup fence of __syncthreads would wait for every load.
-//   - A (and a K-contiguous B) is kept as rows of 64 bytes (four 16-byte chunks,
-//     one K step) whose chunk index is XORed with (row >> 2) & 3, so the 16 rows a
+//   - LDS stages of one K step each (two to five, as many as fit).  A K step is
+//     one or two 64-byte K regions (KR, the K_tile the planner chooses: 32 or
+//     64 k for 16-bit operands, 64 or 128 k for int8; 32 k for e2m1, 128 k for
+//     MX), each region two MFMA k-substeps.  Step st runs its substeps with one
+//     barrier before the last; the barrier is placed where every wave holds all
+//     fragments of stage st in registers or in flight, so right after it the
+//     loads of stage st+NBUF are issued into stage st's buffer.  Loads therefore
+//     have NBUF-1 steps to land.  The barrier waits only for this wave's loads
+//     of the next stage (vmcnt with the later stages still in flight) and for
+//     its LDS reads; the workgroup fence of __syncthreads would wait for every
+//     load.
+//   - A (and a K-contiguous B) is kept as rows of 64 bytes per K region (four
+//     16-byte chunks) whose chunk index is XORed with (row >> 2) & 3, so the 16 rows a
 //     16-lane phase of a fragment read touches hit 16 distinct 16-byte bank
 //     groups of gfx950's 64-bank LDS.
 //   - A row-major B (N contiguous) is kept as it is in memory, K rows of BN
@@ -46,9 +49,9 @@
 //   - Accumulators stay in registers for the whole K range (32x32 blocks:
 //     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8,
 //     v_mfma_scale_f32_32x32x64_f8f6f4).
-//   - The K schedule is n_main full steps then at most one half step (one
-//     substep) for the tail (the pages' variable K step, [generator] DeepGEMM
-//     article, kwkr.cn, section 2.2, first layer).
+//   - The K schedule is n_main full steps then at most one shorter step of
+//     1 .. 2KR-1 substeps for the tail (the pages' variable K step, [generator]
+//     DeepGEMM article, kwkr.cn, section 2.2, first layer).
 //   - The epilogue (alpha, beta*D, bias, GELU, requantise, conversion) runs once
 //     per output element after the K loop, four columns per lane with vector
 //     loads and stores; with a K split the raw fp32 / int32 partials go to the
@@ -123,7 +126,19 @@ DG_DEV void wait_vm_barrier()
     asm volatile("s_barrier" : : : "memory");
 }
 
-template <int PATH, int BKMAJ, int BM, int BN, int WM, int WN>
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1 in order.
+template <typename F, int... I>
+DG_DEV void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+DG_DEV void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int PATH, int BKMAJ, int BM, int BN, int WM, int WN, int KR>
 __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 {
     constexpr int NW = WM * WN;
@@ -135,16 +150,22 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr bool FP4B = IS_E2M1 || IS_MX;            // B holds 4-bit codes, two per byte
     static_assert(!IS_MX || BKMAJ, "MX codes are stored N x K");
     constexpr bool B_TR = !BKMAJ && !FP4B;             // row-major B, transposing reads
-    constexpr int BKE = tiled_bk_elems(PATH);          // k elements per step
+    constexpr int BKE = tiled_bk_elems(PATH);          // k elements per K region
     constexpr int KSUB = tiled_ksub(PATH);             // k elements per MFMA
-    static_assert(BKE == 2 * KSUB, "two substeps per step");
-    constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN);
+    static_assert(BKE == 2 * KSUB, "two substeps per region");
+    static_assert(KR == 1 || PATH == P_F16 || PATH == P_BF16 || PATH == P_I8, "double K steps: 16-bit and int8");
+    static_assert(KR == 1 || KR == 2, "one or two K regions per step");
+    constexpr int BKS = KR * BKE;                      // k elements per K step
+    constexpr int NSUB = 2 * KR;                       // MFMA substeps per K step
+    constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN, KR);
+    static_assert(NBUF >= 2, "LDS stages");
     constexpr int ESZ = (IS_I8 || IS_MX) ? 1 : 2;      // bytes per element of A and of a 16-bit / int8 B
-    constexpr int A_REG = IS_MX ? 2 : 1;                // 64-byte A rows per tile row and step
-    static_assert(BKE * ESZ == 64 * A_REG, "64-byte rows");
+    static_assert(BKE * ESZ == 64 * (IS_MX ? 2 : 1), "64-byte rows");
+    constexpr int A_REG = (IS_MX ? 2 : 1) * KR;         // 64-byte A rows per tile row and step
     constexpr int A_BYTES = BM * 64;                    // one A region
     constexpr int A_ALL = A_REG * A_BYTES;
-    constexpr int B_TILE = IS_E2M1 ? BN * 16 : BN * 64;   // e2m1: BKE/2 bytes of codes per column
+    constexpr int B_REG = IS_E2M1 ? BN * 16 : BN * 64;  // one B region (e2m1: BKE/2 bytes of codes per column)
+    constexpr int B_TILE = KR * B_REG;
     // scales: e2m1 one fp16 per column (whole 256-byte loads); MX, per operand
     // and group of the step, one byte per row of A (column of B) in a 256-byte
     // chunk: [A g0..g3][B g0..g3]
@@ -154,8 +175,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    constexpr int LDS_BYTES = tiled_lds_bytes(PATH, BM, BN, WM, WN);
-    static_assert(STAGE == tiled_stage_bytes(PATH, BM, BN), "stage size");
+    constexpr int LDS_BYTES = tiled_lds_bytes(PATH, BM, BN, WM, WN, KR);
+    static_assert(STAGE == tiled_stage_bytes(PATH, BM, BN, KR), "stage size");
     static_assert(STAGE % 1024 == 0 || IS_E2M1 || (IS_MX && STAGE % 256 == 0), "stage alignment");
     // direct-to-LDS loads: a 16-byte load fills 1 KB (64 lanes), a dword load 256 B.
     // Load i of an operand is issued by wave i % NW (the scale loads from the
@@ -198,9 +219,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     const int split = blockIdx.y;
     const int kbeg = split * p.k_slice;
     const int kend = min(p.K, kbeg + p.k_slice);
-    const int nfull = (kend - kbeg) / BKE;
-    const int tail = (kend - kbeg) - nfull * BKE;   // 0 or KSUB (K is a multiple of KSUB)
+    const int nfull = (kend - kbeg) / BKS;
+    const int tail = (kend - kbeg) - nfull * BKS;   // a multiple of KSUB below BKS (K is a multiple of KSUB)
     const int nsteps = nfull + (tail ? 1 : 0);
+    const int nsub_last = tail ? tail / KSUB : NSUB;   // substeps the last step runs
 
     const int M = p.M, N = p.N;
     const uint32_t lda_b = (uint32_t)(p.lda * ESZ);
@@ -267,9 +289,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const int pc = (i * NW + wave) * 64 + lane;
         if constexpr (IS_E2M1) {            // [BN columns][16 B]
             ob[i] = pc * ldb_b;
-        } else if constexpr (BKMAJ) {       // as A, rows are columns of B
-            const int r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
-            ob[i] = r * ldb_b + c * 16;
+        } else if constexpr (BKMAJ) {       // as A, rows are columns of B (region reg: k + 64 bytes * reg)
+            const int reg = pc / (BN * 4), q = pc % (BN * 4);
+            const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+            ob[i] = reg * 64 + r * ldb_b + c * 16;
         } else {                            // K rows of BN columns
             const int k = pc / CPR, pcol = pc % CPR;
             const int sw = IS_I8 ? (2 * (k & 7)) % CPR : (4 * (k & 3)) % CPR;
@@ -296,7 +319,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // Load i of step j: the A loads first, then B, then the e2m1 scales.
     auto load_one = [&](int j, int i) {
         const bool real = j < nsteps;
-        const int k0 = real ? kbeg + j * BKE : 0;
+        const int k0 = real ? kbeg + j * BKS : 0;
         char *sb = smem + (j % NBUF) * STAGE;
         if (i < A_LD) {
             if (A_NL % NW == 0 || i * NW + wave < A_NL) {   // wave-uniform
@@ -389,10 +412,12 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     }
 
     // One fragment read: A block mi, or B block ni, of substep s of stage buf.
+    // Substep s reads K region s / 2 (16-bit and int8 operands; MX and e2m1
+    // steps are one region), chunk pair s % 2 of its 64-byte rows.
     auto read_a = [&](int buf, auto s_tag, int mi, Frag &f) {
         constexpr int s = decltype(s_tag)::value;
         const char *sA = smem + buf * STAGE;
-        const int c = 2 * s + kg;
+        const int c = 2 * (s & 1) + kg;
         const int row = wm * WTM + mi * 32 + lr;
         if constexpr (IS_MX) {
             // Region s.  The 8-bit operand of the 32x32x64 block-scaled MFMA is
@@ -409,13 +434,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
         } else {
-            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + (s >> 1) * A_BYTES + row * 64 +
+                                                        ((c ^ ((row >> 2) & 3)) << 4));
         }
     };
     auto read_b = [&](int buf, auto s_tag, int ni, Frag &f, int g) {
         constexpr int s = decltype(s_tag)::value;
         const char *sB = smem + buf * STAGE + A_ALL;
-        const int c = 2 * s + kg;
+        const int c = IS_MX ? 2 * s + kg : 2 * (s & 1) + kg;
         const int col0 = wn * WTN + ni * 32;
         if constexpr (IS_E2M1) {
             // raw: the code word and the scale's bits; decode_b turns them into
@@ -439,7 +465,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         } else if constexpr (BKMAJ) {
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
-            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + (IS_MX ? 0 : (s >> 1) * B_REG) + row * 64 +
+                                                        ((c ^ ((row >> 2) & 3)) << 4));
             if constexpr (IS_MX)
                 f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
         } else {
@@ -542,6 +569,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // and that no wave still reads stage st, whose buffer takes stage st+4.  The
     // body is branch-free.
     if constexpr (NW == 8) {
+        static_assert(KR == 1, "the eight-wave loop takes one K region per step");
         // Eight waves: two groups of four (waves 0-3 and 4-7, one of each per
         // SIMD) alternate a memory phase (read both fragments of stage st, wait
         // for this wave's loads of stage st+1) and a compute phase (the MFMAs of
@@ -613,10 +641,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     } else {
         // Four waves, one per SIMD: each wave hides its own LDS reads and buffer
         // loads behind its MFMAs, so the instruction order is fixed by hand
-        // (sched_barrier after every MFMA).  The fragment reads of the next
-        // substep go between the first two thirds of the MFMAs, so the last third
-        // covers their latency and the wait before the barrier finds them done;
-        // the loads of stage st+NBUF go between the rest.
+        // (sched_barrier after every MFMA).  A step runs NSUB substeps; the
+        // fragment reads of substep s+1 go between the first two thirds of
+        // substep s's MFMAs, so the last third covers their latency.  Every read
+        // of stage st is issued by the end of substep NSUB-2, so the one barrier
+        // of the step comes before the last substep: it finds those reads done,
+        // stage st+1 landed, and frees stage st's buffer, into which the last
+        // substep issues the loads of stage st+NBUF (between its last third of
+        // MFMAs) while it reads substep 0 of stage st+1.
         constexpr int NM = FM * FN, NRD = FM + FN, NLD = A_LD + B_LD + S_LD;
         constexpr int QR = NM >= 3 ? 2 * NM / 3 : NM;
         auto read_slot = [](int r) { return r * QR / NRD; };
@@ -629,38 +661,38 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             else read_b(buf, s_tag, r - FM, f, g);
         };
         // One step; the last one (LAST) issues no loads and no reads ahead, needs
-        // no barrier, and masks its second substep when it is a half step.
+        // no barrier, and masks the substeps past the K tail.
         auto step = [&](int st, auto last_tag) {
             constexpr bool LAST = decltype(last_tag)::value;
             const int buf = st % NBUF;
             const int nxt = (st + 1) % NBUF;
-            settle(f0);
-            decode_b(f0);
+            static_for<NSUB>([&](auto s_tag) {
+                constexpr int s = decltype(s_tag)::value;
+                Frag &F = (s & 1) ? f1 : f0;   // this substep's fragments
+                Frag &G = (s & 1) ? f0 : f1;   // the next substep's
+                if constexpr (!LAST && s == NSUB - 1) wait_vm_barrier<(NBUF - 2) * LPS>();
+                settle(F);
+                if constexpr (LAST && s > 0) keep_if(F, s < nsub_last);   // past the tail: 0 x 0
+                decode_b(F);
 #pragma unroll
-            for (int q = 0; q < NM; ++q) {
-                mfma1(f0, q / FN, q % FN);
+                for (int q = 0; q < NM; ++q) {
+                    mfma1(F, q / FN, q % FN);
+                    if constexpr (s < NSUB - 1) {
 #pragma unroll
-                for (int r = 0; r < NRD; ++r)
-                    if (read_slot(r) == q) read_item(buf, S1{}, r, f1, g0 + st);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if constexpr (!LAST) wait_vm_barrier<(NBUF - 2) * LPS>();
-            settle(f1);
-            if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
-            decode_b(f1);
+                        for (int r = 0; r < NRD; ++r)
+                            if (read_slot(r) == q)
+                                read_item(buf, std::integral_constant<int, s + 1>{}, r, G, g0 + st);
+                    } else if constexpr (!LAST) {
 #pragma unroll
-            for (int q = 0; q < NM; ++q) {
-                mfma1(f1, q / FN, q % FN);
-                if constexpr (!LAST) {
+                        for (int r = 0; r < NRD; ++r)
+                            if (read_slot(r) == q) read_item(nxt, S0{}, r, G, g0 + st + 1);
 #pragma unroll
-                    for (int r = 0; r < NRD; ++r)
-                        if (read_slot(r) == q) read_item(nxt, S0{}, r, f0, g0 + st + 1);
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i)
-                        if (load_slot(i) == q) load_one(st + NBUF, i);
+                        for (int i = 0; i < NLD; ++i)
+                            if (load_slot(i) == q) load_one(st + NBUF, i);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         };
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) load_stage(j);
@@ -673,8 +705,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
-        // (the last step reads nothing ahead, and settle(f1) waited for its reads:
-        // no transposing read is in flight when the epilogue reuses registers)
+        // (the last substep reads nothing ahead, and settling it waited for its
+        // reads: no transposing read is in flight when the epilogue reuses
+        // registers)
     }
 
     if (clk_on) {

@@ -44,7 +44,7 @@ constexpr int SKINNY_A_LDS = 32768;   // must match skinny.hip
 constexpr int E2M1_A_LDS = 32768;     // must match skinny.hip
 
 const TiledShape k_tiled_shapes[] = {
-#define DG_TS(path, kmaj, bm, bn, wm, wn) {path, kmaj, bm, bn, wm, wn},
+#define DG_TS(path, kmaj, bm, bn, wm, wn, kr) {path, kmaj, bm, bn, wm, wn, kr},
     DG_TILED_CATALOGUE(DG_TS)
 #undef DG_TS
 };
@@ -71,17 +71,18 @@ const int k_e2m1_mr[] = {
 // Registers, LDS and occupancy of the compiled variants, as the compiler
 // reported them when the library was built.
 struct ResRow {
-    int fam, a0, a1, a2, a3, a4, a5, vgpr, agpr, lds, occ, spill;
+    int fam, a0, a1, a2, a3, a4, a5, a6, vgpr, agpr, lds, occ, spill;
 };
 const ResRow k_res[] = {
 #include "resources.inc"
 };
 
-const ResRow *find_res(int fam, int a0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0)
+const ResRow *find_res(int fam, int a0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0,
+                       int a6 = 0)
 {
     for (const ResRow &r : k_res)
         if (r.fam == fam && r.a0 == a0 && r.a1 == a1 && r.a2 == a2 && r.a3 == a3 && r.a4 == a4 &&
-            r.a5 == a5)
+            r.a5 == a5 && r.a6 == a6)
             return &r;
     return nullptr;
 }
@@ -219,28 +220,29 @@ double roofline_us(const Problem &pr, const dg_device_desc &d)
 static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
                        std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
-    const int BKE = tiled_bk_elems(pr.path), KSUB = tiled_ksub(pr.path);
+    const int KSUB = tiled_ksub(pr.path);
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
     const int occ_need = std::max(1, (int)std::ceil(o.target_occupancy * d.max_waves_per_simd - 1e-9));
     const int nshapes = (int)(sizeof(k_tiled_shapes) / sizeof(k_tiled_shapes[0]));
     for (int id = 0; id < nshapes; ++id) {
         const TiledShape &s = k_tiled_shapes[id];
         if (s.path != pr.path || s.b_kmajor != pr.b_kmajor) continue;
+        const int BKE = tiled_bk_elems(pr.path) * s.kr;   // the variant's K step (K_tile)
         const int waves = s.wm * s.wn, NT = waves * 64;
         const int FM = s.bm / s.wm / 32, FN = s.bn / s.wn / 32;
         // registers (per lane): accumulators, staging, fragments, addressing
         const int acc = FM * FN * 16;
-        int stage = s.bm * 8 / NT * 4;
+        int stage = s.bm * 8 * s.kr / NT * 4;
         if (pr.path == P_MX) stage = s.bm * 16 / NT * 4 + s.bn * 8 / NT * 4 + (FM + FN) * 2;
         else if (pr.path == P_E2M1) stage += ceil_div(s.bn * 2, NT) * 5;
-        else if (s.b_kmajor) stage += s.bn * 8 / NT * 4;
-        else stage += (int)ceil_div(s.bn, NT) * 32;
+        else if (s.b_kmajor) stage += s.bn * 8 * s.kr / NT * 4;
+        else stage += (int)ceil_div(s.bn, NT) * 32 * s.kr;
         const int other = stage + (FM + FN) * 4 * 2 + 40;
         int vgpr, agpr;
         if (acc + other <= 256) { vgpr = acc + other; agpr = 0; }
         else { vgpr = other; agpr = acc; }
-        int lds = tiled_lds_bytes(s.path, s.bm, s.bn, s.wm, s.wn);
-        if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn)) {
+        int lds = tiled_lds_bytes(s.path, s.bm, s.bn, s.wm, s.wn, s.kr);
+        if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn, s.kr)) {
             vgpr = r->vgpr;
             agpr = r->agpr;
             lds = r->lds;
@@ -300,8 +302,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             // variant's measured sustained efficiency (catalogue.h); the LDS and
             // L2 terms only matter for variants that are not MFMA-bound.
             const double t_mfma = 2.0 * s.bm * s.bn * BKE / mfma_ops_per_clk_cu(pr.path) /
-                                  tiled_step_efficiency(s.path, s.bm, s.bn, waves);
-            const double stage = tiled_stage_bytes(s.path, s.bm, s.bn);
+                                  tiled_step_efficiency(s.path, s.bm, s.bn, waves, s.kr);
+            const double stage = tiled_stage_bytes(s.path, s.bm, s.bn, s.kr);
             const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + stage) / 128.0;
             const double t_l2 = stage / 64.0;
             // A K step waits for loads issued one step earlier.  When an operand is
@@ -322,8 +324,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             c.est_us = est;
             c.roof_us = roofline_us(pr, d);
             char nm[64];
-            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d", path_name(pr.path),
-                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn);
+            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d", path_name(pr.path),
+                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE);
             c.name = nm;
             out.push_back(c);
         }
