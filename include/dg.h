@@ -153,9 +153,12 @@ typedef struct {
 } dg_plan_opts;
 
 /* Description of the device the planner plans for.  dg_create fills it from
- * hipGetDeviceProperties; dg_default_device_desc gives the MI355X table
- * (the analogue of the pages' per-GPU hardware JSON, [generator] section 3.2,
- * step 1). */
+ * hipGetDeviceProperties and, when the hardware probe's JSON description is
+ * present, from that (dg_load_device_json); dg_default_device_desc gives the
+ * MI355X table (the analogue of the pages' per-GPU hardware JSON, [generator]
+ * section 3.2, step 1, whose rates come from micro-benchmarks run before
+ * candidate generation, [overview] section 4.1, stage 1).  The measured
+ * fields are 0 when unknown: the planner then uses the published figures. */
 typedef struct {
     char arch[32];            /* "gfx950" */
     int32_t cu_count;         /* compute units (256)                    */
@@ -167,8 +170,18 @@ typedef struct {
     int32_t vgpr_per_lane;    /* unified VGPR+AGPR file per SIMD lane (512) */
     int32_t max_waves_per_simd; /* 8                                    */
     double clock_ghz;         /* peak engine clock (2.4)                */
-    double hbm_gbps;          /* peak HBM bandwidth, GB/s (8000)        */
-    double l2_bytes_per_xcd;  /* 4 MiB                                  */
+    double hbm_gbps;          /* HBM read bandwidth, GB/s (8000 published; the probe's
+                                 streaming-read rate when measured)    */
+    double l2_bytes_per_xcd;  /* L2 per die (4 MiB; probed: where re-reads stop hitting it) */
+    double mall_bytes;        /* last-level (MALL) cache, all dies (256 MiB; probed)      */
+    double mfma_tflops_f16;   /* sustained fp16 MFMA rate of back-to-back MFMAs on every
+                                 SIMD, TFLOP/s (0: 4096 flop per clock per CU at clock_ghz);
+                                 int8 and the fp8 block-scaled MFMA run at twice it */
+    double launch_us;         /* an empty kernel launch, microseconds (0: 2.0)            */
+    int32_t lds_conflict_stride_words; /* smallest word stride at which a wave's dword LDS
+                                 reads are fully serialised: half the bank count (0: 32) */
+    int32_t calibrated;       /* number of tiled variants with a measured efficiency
+                                 (dg_load_device_json; output of dg_get_device_desc only) */
 } dg_device_desc;
 
 /* What the planner chose (the pages' "Solution": tile shape and the estimate
@@ -391,8 +404,10 @@ dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries);
  * (tile_planned_generator_amd/probe.py writes the results as a JSON device
  * description).
  *   DG_PROBE_STREAM  reads `bytes` (a multiple of 16) of device memory `buf`
- *                    with 16-byte non-temporal loads on `grid` workgroups of
- *                    256 threads; `out`: device uint32[grid] (a checksum)
+ *                    with 16-byte non-temporal loads (param bit 0 set: plain,
+ *                    cached loads) on `grid` workgroups of 256 threads, each a
+ *                    contiguous share, param >> 1 times (0: once; at most
+ *                    4096); `out`: device uint32[grid] (a checksum)
  *   DG_PROBE_MFMA    `grid` workgroups of 4 waves, each wave `param` rounds of
  *                    8 independent 32x32x16 fp16 MFMAs (2*32*32*16 flops each);
  *                    `out`: device float[grid]
@@ -407,10 +422,33 @@ dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, i
                    int32_t grid, dg_stream_t stream);
 
 /* Replace the description a handle plans with (for instance one measured by the
- * probe), and drop its cached plans.  Errors: DG_ERR_INVALID_STATE (handle NULL
- * or destroyed), DG_ERR_INVALID_ARG (desc NULL or a non-positive field, as for
+ * probe), and drop its cached plans; measured variant efficiencies loaded
+ * earlier stay.  Errors: DG_ERR_INVALID_STATE (handle NULL or destroyed),
+ * DG_ERR_INVALID_ARG (desc NULL or a non-positive field, as for
  * dg_create_offline). */
 dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc);
+
+/* Load a device description written by the hardware probe
+ * (tile_planned_generator_amd/probe.py): a JSON object whose "desc" object holds
+ * dg_device_desc fields by name, whose "measured" object holds the probed rates
+ * (hbm_gbps, mfma_tflops_f16, launch_us, lds_conflict_stride_words, l2_bytes_per_xcd,
+ * mall_bytes) and whose "tiled_efficiency" object maps tiled kernel names (as in
+ * dg_plan_info.kernel_name) to the fraction of the probed MFMA rate the variant
+ * sustains per K step, measured on the 4096^3 problem of its path.  The planner
+ * then scores with these numbers instead of its built-in fallbacks, and cached
+ * plans are dropped.  dg_create loads <library directory>/devices/<arch>.json by
+ * itself when it exists and describes the device (the environment variable
+ * DG_DEVICE_JSON names another file; set to an empty string it disables this).
+ * Errors: DG_ERR_INVALID_STATE (handle), DG_ERR_INVALID_ARG (path NULL,
+ * unreadable, not such a JSON object, or a field out of range),
+ * DG_ERR_UNSUPPORTED (a device handle and a description of another
+ * architecture or CU count). */
+dg_status dg_load_device_json(dg_handle_t h, const char *path);
+
+/* The description a handle plans with (after dg_create's own loading of the
+ * probe's JSON, dg_load_device_json or dg_set_device_desc).  Errors:
+ * DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG (out NULL). */
+dg_status dg_get_device_desc(dg_handle_t h, dg_device_desc *out);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char *dg_last_error(void);

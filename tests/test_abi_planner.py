@@ -384,10 +384,74 @@ def test_probe_description_round_trip():
     # the probe kernels need a device handle
     assert dg.dg_probe(h.h, dg.DG_PROBE_LDS, None, 0, 1, None, 1, None) == dg.DG_ERR_INVALID_STATE
     # the shipped MI355X description (written by the probe on the device) plans too
-    shipped = probe.load_desc(os.path.join(ROOT, "tile_planned_generator_amd", "devices", "mi355x.json"))
+    shipped = probe.load_desc(os.path.join(ROOT, "tile_planned_generator_amd", "devices", "gfx950.json"))
     assert shipped.cu_count == 256 and 5000 < shipped.hbm_gbps < 8000
     h.set_device_desc(shipped)
     assert h.plan(4096, 4096, 4096, "i8", "i8", "i32").split_k == 1
+    h.close()
+
+
+def _probe_json(tmp_path, **measured):
+    """A probe description (the shipped one's structure) with some measured
+    fields replaced; returns its path."""
+    import json
+    with open(os.path.join(ROOT, "tile_planned_generator_amd", "devices", "gfx950.json")) as f:
+        d = json.load(f)
+    d.setdefault("measured", {}).update(measured)
+    path = tmp_path / "dev.json"
+    path.write_text(json.dumps(d))
+    return str(path), d
+
+
+def test_device_json_feeds_the_planner(tmp_path):
+    # dg_load_device_json takes the probe's rates and variant efficiencies; the
+    # planner's estimates and choices follow them
+    path, d = _probe_json(tmp_path)
+    h = dg.Handle(offline=dg.default_device_desc())
+    h.load_device_json(path)
+    got = h.device_desc()
+    m = d["measured"]
+    assert got.hbm_gbps == m["hbm_gbps"] and got.mfma_tflops_f16 == m["mfma_tflops_f16"]
+    assert got.launch_us == m["launch_us"] and got.lds_conflict_stride_words == m["lds_conflict_stride_words"]
+    assert got.calibrated == len(d.get("tiled_efficiency", {}))
+    base = h.plan(4096, 4096, 4096, "i8", "i8", "i32")
+    # a ten times slower MFMA makes every tiled estimate slower
+    path2, _ = _probe_json(tmp_path, mfma_tflops_f16=m["mfma_tflops_f16"] / 10)
+    h.load_device_json(path2)
+    slow = h.plan(4096, 4096, 4096, "i8", "i8", "i32")
+    assert slow.est_us > 3 * base.est_us
+    # and the choices move with it: the tile and K split of a short, wide
+    # problem, and the K split of the GELU workload's shape (at a faster MFMA
+    # rate the partial sums' traffic of a split weighs more)
+    for M, N, K, f in ((32, 4096, 8192, 1 / 50), (2048, 2048, 8192, 5.0)):
+        got = []
+        for tf in (m["mfma_tflops_f16"], m["mfma_tflops_f16"] * f):
+            p, _ = _probe_json(tmp_path, mfma_tflops_f16=tf)
+            h.load_device_json(p)
+            q = h.plan(M, N, K, "bf16", "bf16", "bf16")
+            got.append((q.kernel_name.decode(), q.split_k))
+        assert got[0] != got[1], got
+    h.close()
+
+
+def test_device_json_errors(tmp_path):
+    import json
+    h = dg.Handle(offline=dg.default_device_desc())
+    assert dg.dg_load_device_json(h.h, None) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_load_device_json(h.h, str(tmp_path / "missing.json").encode()) == dg.DG_ERR_INVALID_ARG
+    bad = tmp_path / "bad.json"
+    for text in ("{", "[1, 2]", '{"desc": {}}', '{"arch": "gfx950", "desc": {"cu_count": -4}}',
+                 '{"arch": "gfx950", "tiled_efficiency": {"tiled_i8_n_256x256_w2x4_k64": 7}}',
+                 '{"arch": "gfx950", "desc": {"cu_count": 2.5}}'):
+        bad.write_text(text)
+        assert dg.dg_load_device_json(h.h, str(bad).encode()) == dg.DG_ERR_INVALID_ARG, text
+    # a failed load leaves the description as it was
+    assert h.device_desc().cu_count == 256 and h.device_desc().calibrated == 0
+    ok = tmp_path / "ok.json"
+    ok.write_text(json.dumps({"arch": "gfx950", "measured": {"launch_us": 5.5},
+                              "tiled_efficiency": {"tiled_i8_n_256x256_w2x4_k64": 0.5}}))
+    h.load_device_json(ok)
+    assert h.device_desc().launch_us == 5.5 and h.device_desc().calibrated == 1
     h.close()
 
 

@@ -1,19 +1,24 @@
 """GPU: the hardware probe (dg_probe, tile_planned_generator_amd.probe) gives
 rates in the range the device's published peaks allow, a consistent LDS
-bank-conflict curve, and a description a device handle plans and computes with
-correctly."""
+bank-conflict curve and cache capacities, per-variant efficiencies from the
+library's own kernels, and a description a device handle plans and computes
+with correctly; dg_create plans with the shipped description of the device."""
+import json
+import os
+
 import pytest
 
 from tests.test_gpu_parity import h, run  # noqa: F401  (fixture and runner)
 from tile_planned_generator_amd import dg, probe, synth
 
 pytestmark = pytest.mark.gpu
+SHIPPED = os.path.join(os.path.dirname(dg.LIB_PATH), "devices", "gfx950.json")
 
 
 def test_probe_measures_the_device(h):  # noqa: F811
-    r = probe.measure(0, stream_bytes=1 << 29, mfma_iters=1024)
+    r = probe.measure(0, stream_bytes=1 << 30, mfma_iters=1024, calibrate_tiles=False)
     m = r["measured"]
-    print(r)
+    print({k: v for k, v in m.items() if k != "lds_ticks_by_stride"})
     assert 1000 < m["hbm_gbps"] < 8000 * 1.05          # below the 8 TB/s peak
     assert 300 < m["mfma_tflops_f16"] < 2516.6 * 1.05  # below the fp16 dense peak
     assert 0.5 < m["mfma_clock_ghz"] < 2.5
@@ -24,6 +29,12 @@ def test_probe_measures_the_device(h):  # noqa: F811
     assert t[256] > 2 * t[1]
     assert m["lds_conflict_stride_words"] == min(s for s in strides if t[s] >= 0.9 * t[256])
     assert m["lds_conflict_stride_words"] >= 16
+    # caches: a per-die L2 of a few MiB and a last-level cache of some hundred
+    # MiB, read faster than HBM
+    assert 1 << 20 <= m["l2_bytes_per_xcd"] <= 16 << 20
+    assert 64 << 20 <= m["mall_bytes"] <= 1 << 30
+    rates = {int(k): v for k, v in m["cached_read_gbps_by_mib"].items()}
+    assert rates[4] > 1.5 * rates[1024]
     assert r["desc"]["cu_count"] == 256 and r["desc"]["hbm_gbps"] == m["hbm_gbps"]
     # a device handle planning with the measured description still computes right
     h.set_device_desc(probe.load_desc(r))
@@ -31,10 +42,42 @@ def test_probe_measures_the_device(h):  # noqa: F811
         run(h, synth.make("bf16_1x4096x131072", K=4096))
         run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=300, N=264, K=512))
     finally:
-        h.set_device_desc(dg.default_device_desc())
+        h.load_device_json(SHIPPED)
+
+
+def test_calibration_of_one_path(h):  # noqa: F811
+    # every int8 variant timed on the 4096^3 problem: efficiencies in (0, 1.5];
+    # of the 256 x 256 variants (one workgroup per CU, so the same rounds), the
+    # faster has the higher efficiency
+    d = json.load(open(SHIPPED))
+    desc = dict(d["desc"], mfma_tflops_f16=d["measured"]["mfma_tflops_f16"],
+                launch_us=d["measured"]["launch_us"])
+    eff, us = probe.calibrate(h, desc, "cuda:0", reps=10, rounds=1, paths=("i8",))
+    assert len(eff) == 20 and all(0 < e <= 1.5 for e in eff.values())
+    for lay in ("_n_", "_k_"):
+        names = [n for n in eff if lay in n and "_256x256_" in n]
+        fastest = min(names, key=lambda n: us[n])
+        assert eff[fastest] == max(eff[n] for n in names)
+
+
+def test_device_handle_plans_with_the_shipped_description(h, tmp_path):  # noqa: F811
+    d = json.load(open(SHIPPED))
+    got = h.device_desc()
+    assert got.calibrated == len(d["tiled_efficiency"]) > 0
+    assert got.mfma_tflops_f16 == d["measured"]["mfma_tflops_f16"]
+    assert got.mall_bytes == d["measured"]["mall_bytes"]
+    # another device's description is refused by a device handle, which keeps its own
+    for change in ({"arch": "gfx942"}, {"desc": dict(d["desc"], cu_count=128)}):
+        bad = dict(d, **change)
+        (tmp_path / "other.json").write_text(json.dumps(bad))
+        assert dg.dg_load_device_json(h.h, str(tmp_path / "other.json").encode()) == dg.DG_ERR_UNSUPPORTED
+    assert h.device_desc().cu_count == 256 and h.device_desc().calibrated == got.calibrated
 
 
 def test_probe_argument_errors(h):  # noqa: F811
     assert dg.dg_probe(h.h, dg.DG_PROBE_STREAM, None, 16, 0, None, 1, None) == dg.DG_ERR_INVALID_ARG
     assert dg.dg_probe(h.h, 7, None, 0, 0, dg.C.c_void_p(1), 1, None) == dg.DG_ERR_INVALID_ARG
     assert dg.dg_probe(h.h, dg.DG_PROBE_LDS, None, 0, 0, dg.C.c_void_p(1), 1, None) == dg.DG_ERR_INVALID_ARG
+    # a pass count past the limit is refused before launch
+    assert dg.dg_probe(h.h, dg.DG_PROBE_STREAM, dg.C.c_void_p(16), 16, 1 | (4097 << 1), dg.C.c_void_p(1), 1,
+                       None) == dg.DG_ERR_INVALID_ARG

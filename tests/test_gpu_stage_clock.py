@@ -42,8 +42,8 @@ def test_stage_clock_records(h, bm, bn, nw, split):  # noqa: F811
     assert (rt > 0).all()
     ghz = (rec[:, 2] - rec[:, 1]) / (rt * 10.0)
     assert (ghz > 0.3).all() and (ghz < 3.0).all(), ghz
-    # K steps: a step is 32 k; the slices are k_slice long but the last
-    steps = {-(-min(info.k_slice, w.K - s * info.k_slice) // 32) for s in range(info.split_k)}
+    # K steps: a step is k_main long; the slices are k_slice long but the last
+    steps = {-(-min(info.k_slice, w.K - s * info.k_slice) // info.k_main) for s in range(info.split_k)}
     assert set(rec[:, 6].tolist()) <= steps
     # grid coordinates: x + y * grid_x covers every workgroup once
     x, y = rec[:, 7] & 0xFFFFFFFF, rec[:, 7] >> 32

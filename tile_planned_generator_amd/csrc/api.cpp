@@ -1,12 +1,17 @@
 // api.cpp - the C ABI (include/dg.h): validation, plan cache, dispatch.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cctype>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <fstream>
+#include <map>
 #include <mutex>
+#include <sstream>
 #include <set>
 #include <string>
 #include <unordered_map>
@@ -23,6 +28,7 @@ using namespace dg;
 struct dg_handle_s {
     dg_device_desc desc;
     int device;   // -1: offline (planner only)
+    EffTable eff;  // measured tiled-variant efficiencies (dg_load_device_json)
     std::unordered_map<std::string, Candidate> cache;
     uint64_t *clk = nullptr;    // stage clock buffer (dg_set_stage_clock), or null
     int64_t clk_entries = 0;
@@ -201,12 +207,218 @@ dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, C
         out = it->second;
         return DG_OK;
     }
-    PlanResult r = plan_problem(pr, h->desc, o);
+    PlanResult r = plan_problem(pr, h->desc, o, h->eff.empty() ? nullptr : &h->eff);
     if (r.status != DG_OK) return fail(r.status, r.message);
     out = r.pareto.front();
     add_tail(pr, h->desc, out);
     h->cache.emplace(key, out);
     return DG_OK;
+}
+
+// ------------------------------------------------------- device description
+// A small JSON reader for the probe's description (objects, strings, numbers,
+// arrays, true/false/null).  Scalars come back flattened, the keys of nested
+// objects joined with '.'; array contents are skipped.
+struct JsonFlat {
+    std::map<std::string, double> num;
+    std::map<std::string, std::string> str;
+};
+
+class JsonReader {
+  public:
+    explicit JsonReader(const std::string &t) : t_(t) {}
+    bool parse(JsonFlat &f)
+    {
+        ws();
+        if (i_ >= t_.size() || t_[i_] != '{') return false;
+        if (!value("", f, 0)) return false;
+        ws();
+        return i_ == t_.size();
+    }
+
+  private:
+    const std::string &t_;
+    size_t i_ = 0;
+    void ws()
+    {
+        while (i_ < t_.size() && std::isspace((unsigned char)t_[i_])) ++i_;
+    }
+    bool lit(const char *w)
+    {
+        const size_t n = std::strlen(w);
+        if (t_.compare(i_, n, w) != 0) return false;
+        i_ += n;
+        return true;
+    }
+    bool str(std::string &out)
+    {
+        if (i_ >= t_.size() || t_[i_] != '"') return false;
+        ++i_;
+        out.clear();
+        while (i_ < t_.size() && t_[i_] != '"') {
+            char c = t_[i_++];
+            if (c == '\\') {
+                if (i_ >= t_.size()) return false;
+                const char e = t_[i_++];
+                if (e == 'u') {
+                    if (i_ + 4 > t_.size()) return false;
+                    i_ += 4;
+                    c = '?';
+                } else {
+                    c = e == 'n' ? '\n' : e == 't' ? '\t' : e == 'r' ? '\r' : e == 'b' ? '\b' : e == 'f' ? '\f' : e;
+                }
+            }
+            out.push_back(c);
+        }
+        if (i_ >= t_.size()) return false;
+        ++i_;
+        return true;
+    }
+    bool value(const std::string &key, JsonFlat &f, int depth)
+    {
+        if (depth > 32) return false;
+        ws();
+        if (i_ >= t_.size()) return false;
+        const char c = t_[i_];
+        if (c == '{' || c == '[') {
+            const bool obj = c == '{';
+            const char close = obj ? '}' : ']';
+            ++i_;
+            ws();
+            if (i_ < t_.size() && t_[i_] == close) {
+                ++i_;
+                return true;
+            }
+            JsonFlat skip;
+            for (;;) {
+                ws();
+                std::string k;
+                if (obj) {
+                    if (!str(k)) return false;
+                    ws();
+                    if (i_ >= t_.size() || t_[i_] != ':') return false;
+                    ++i_;
+                }
+                if (!value(obj ? (key.empty() ? k : key + "." + k) : "", obj ? f : skip, depth + 1)) return false;
+                ws();
+                if (i_ < t_.size() && t_[i_] == ',') {
+                    ++i_;
+                    continue;
+                }
+                if (i_ < t_.size() && t_[i_] == close) {
+                    ++i_;
+                    return true;
+                }
+                return false;
+            }
+        }
+        if (c == '"') {
+            std::string v;
+            if (!str(v)) return false;
+            f.str[key] = v;
+            return true;
+        }
+        if (c == 't') return lit("true");
+        if (c == 'f') return lit("false");
+        if (c == 'n') return lit("null");
+        const char *b = t_.c_str() + i_;
+        char *e = nullptr;
+        const double v = std::strtod(b, &e);
+        if (e == b) return false;
+        i_ += (size_t)(e - b);
+        f.num[key] = v;
+        return true;
+    }
+};
+
+bool desc_fields_valid(const dg_device_desc &d)
+{
+    return d.cu_count > 0 && d.simd_per_cu > 0 && d.lds_bytes_per_cu > 0 && d.lds_bytes_per_wg > 0 &&
+           d.vgpr_per_lane > 0 && d.max_waves_per_simd > 0 && d.clock_ghz > 0 && d.hbm_gbps > 0 &&
+           d.l2_bytes_per_xcd >= 0 && d.mall_bytes >= 0 && d.mfma_tflops_f16 >= 0 && d.launch_us >= 0 &&
+           d.lds_conflict_stride_words >= 0;
+}
+
+// Read the probe's JSON description into the handle (strict: every problem is
+// an error; the caller decides whether to report it).
+dg_status load_device_json(dg_handle_t h, const std::string &path)
+{
+    std::ifstream in(path);
+    if (!in) return fail(DG_ERR_INVALID_ARG, "cannot read " + path);
+    std::stringstream ss;
+    ss << in.rdbuf();
+    const std::string text = ss.str();
+    JsonFlat f;
+    if (!JsonReader(text).parse(f)) return fail(DG_ERR_INVALID_ARG, path + " is not a JSON object");
+    dg_device_desc d = h->desc;
+    const auto arch = f.str.find("arch");
+    if (arch == f.str.end()) return fail(DG_ERR_INVALID_ARG, path + " names no arch");
+    if (h->device >= 0 && arch->second != d.arch)
+        return fail(DG_ERR_UNSUPPORTED, path + " describes " + arch->second + ", the device is " + d.arch);
+    std::snprintf(d.arch, sizeof d.arch, "%s", arch->second.c_str());
+    auto num = [&](const std::string &k, double &v) {
+        const auto it = f.num.find(k);
+        if (it == f.num.end()) return false;
+        v = it->second;
+        return true;
+    };
+    struct IntField {
+        const char *name;
+        int32_t *p;
+    } ints[] = {{"cu_count", &d.cu_count}, {"xcd_count", &d.xcd_count}, {"simd_per_cu", &d.simd_per_cu},
+                {"wave_size", &d.wave_size}, {"lds_bytes_per_cu", &d.lds_bytes_per_cu},
+                {"lds_bytes_per_wg", &d.lds_bytes_per_wg}, {"vgpr_per_lane", &d.vgpr_per_lane},
+                {"max_waves_per_simd", &d.max_waves_per_simd},
+                {"lds_conflict_stride_words", &d.lds_conflict_stride_words}};
+    struct DblField {
+        const char *name;
+        double *p;
+    } dbls[] = {{"clock_ghz", &d.clock_ghz}, {"hbm_gbps", &d.hbm_gbps}, {"l2_bytes_per_xcd", &d.l2_bytes_per_xcd},
+                {"mall_bytes", &d.mall_bytes}, {"mfma_tflops_f16", &d.mfma_tflops_f16}, {"launch_us", &d.launch_us}};
+    // "desc" first, then "measured" (the probe's rates win)
+    for (const char *sec : {"desc.", "measured."}) {
+        for (auto &x : ints) {
+            double v;
+            if (num(std::string(sec) + x.name, v)) {
+                if (v != std::floor(v) || std::fabs(v) > 1e9)
+                    return fail(DG_ERR_INVALID_ARG, std::string(path) + ": " + sec + x.name + " is not an integer");
+                *x.p = (int32_t)v;
+            }
+        }
+        for (auto &x : dbls) {
+            double v;
+            if (num(std::string(sec) + x.name, v)) *x.p = v;
+        }
+    }
+    if (!desc_fields_valid(d)) return fail(DG_ERR_INVALID_ARG, path + ": a field is out of range");
+    if (h->device >= 0 && d.cu_count != h->desc.cu_count)
+        return fail(DG_ERR_UNSUPPORTED, path + " describes " + std::to_string(d.cu_count) + " CUs, the device has " +
+                                            std::to_string(h->desc.cu_count));
+    EffTable eff;
+    const std::string pre = "tiled_efficiency.";
+    for (const auto &kv : f.num) {
+        if (kv.first.compare(0, pre.size(), pre) != 0) continue;
+        if (!(kv.second > 0 && kv.second <= 1.5))
+            return fail(DG_ERR_INVALID_ARG, path + ": efficiency of " + kv.first.substr(pre.size()) + " out of (0, 1.5]");
+        eff[kv.first.substr(pre.size())] = kv.second;
+    }
+    d.calibrated = (int32_t)eff.size();
+    h->desc = d;
+    h->eff = std::move(eff);
+    h->cache.clear();
+    return DG_OK;
+}
+
+// <directory of this library>/devices/<arch>.json, or DG_DEVICE_JSON when set.
+std::string default_device_json(const char *arch)
+{
+    if (const char *e = std::getenv("DG_DEVICE_JSON")) return e;
+    Dl_info info;
+    if (!dladdr(reinterpret_cast<void *>(&default_device_json), &info) || !info.dli_fname) return "";
+    std::string dir = info.dli_fname;
+    const size_t slash = dir.rfind('/');
+    dir = slash == std::string::npos ? "." : dir.substr(0, slash);
+    return dir + "/devices/" + arch + ".json";
 }
 
 const char *status_names[] = {"DG_OK",
@@ -240,6 +452,9 @@ dg_status dg_default_device_desc(dg_device_desc *out)
     out->clock_ghz = 2.4;
     out->hbm_gbps = 8000.0;
     out->l2_bytes_per_xcd = 4.0 * 1024 * 1024;
+    out->mall_bytes = 256.0 * 1024 * 1024;
+    // measured fields: unknown until probed (mfma_tflops_f16, launch_us,
+    // lds_conflict_stride_words, calibrated = 0)
     return DG_OK;
 }
 
@@ -268,6 +483,12 @@ dg_status dg_create(dg_handle_t *out, int hip_device)
         if (prop.maxSharedMemoryPerMultiProcessor > 0)
             h->desc.lds_bytes_per_cu = (int32_t)prop.maxSharedMemoryPerMultiProcessor;
         h->device = hip_device;
+        // the hardware probe's description of this device, when present
+        const std::string json = default_device_json(h->desc.arch);
+        if (!json.empty() && std::ifstream(json).good()) {
+            const std::string saved = g_err;
+            if (load_device_json(h, json) != DG_OK) g_err = saved;   // another device's: planned without it
+        }
         {
             std::lock_guard<std::mutex> lk(g_live_mu);
             g_live.insert(h);
@@ -284,12 +505,11 @@ dg_status dg_create_offline(dg_handle_t *out, const dg_device_desc *desc)
     try {
         if (!out || !desc) return fail(DG_ERR_INVALID_ARG, "NULL argument");
         *out = nullptr;
-        if (desc->cu_count <= 0 || desc->simd_per_cu <= 0 || desc->lds_bytes_per_cu <= 0 ||
-            desc->lds_bytes_per_wg <= 0 || desc->vgpr_per_lane <= 0 || desc->max_waves_per_simd <= 0 ||
-            desc->clock_ghz <= 0 || desc->hbm_gbps <= 0)
-            return fail(DG_ERR_INVALID_ARG, "device description has a non-positive field");
+        if (!desc_fields_valid(*desc))
+            return fail(DG_ERR_INVALID_ARG, "device description has a non-positive (or negative measured) field");
         dg_handle_s *h = new dg_handle_s();
         h->desc = *desc;
+        h->desc.calibrated = 0;
         h->device = -1;
         {
             std::lock_guard<std::mutex> lk(g_live_mu);
@@ -314,11 +534,7 @@ dg_status dg_destroy(dg_handle_t h)
 }
 
 namespace {
-bool desc_valid(const dg_device_desc *d)
-{
-    return d && d->cu_count > 0 && d->simd_per_cu > 0 && d->lds_bytes_per_cu > 0 && d->lds_bytes_per_wg > 0 &&
-           d->vgpr_per_lane > 0 && d->max_waves_per_simd > 0 && d->clock_ghz > 0 && d->hbm_gbps > 0;
-}
+bool desc_valid(const dg_device_desc *d) { return d && desc_fields_valid(*d); }
 }  // namespace
 
 dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc)
@@ -327,11 +543,31 @@ dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc)
         if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
         if (!desc_valid(desc)) return fail(DG_ERR_INVALID_ARG, "device description is NULL or has a non-positive field");
         h->desc = *desc;
+        h->desc.calibrated = (int32_t)h->eff.size();
         h->cache.clear();
         return ok();
     } catch (...) {
         return fail(DG_ERR_INTERNAL, "exception in dg_set_device_desc");
     }
+}
+
+dg_status dg_load_device_json(dg_handle_t h, const char *path)
+{
+    try {
+        if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+        if (!path) return fail(DG_ERR_INVALID_ARG, "path is NULL");
+        return load_device_json(h, path);
+    } catch (...) {
+        return fail(DG_ERR_INTERNAL, "exception in dg_load_device_json");
+    }
+}
+
+dg_status dg_get_device_desc(dg_handle_t h, dg_device_desc *out)
+{
+    if (!is_live(h)) return fail(DG_ERR_INVALID_STATE, "handle is NULL or destroyed");
+    if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
+    *out = h->desc;
+    return DG_OK;
 }
 
 dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, int32_t param, void *out,
@@ -345,8 +581,9 @@ dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, i
             return fail(DG_ERR_INVALID_STATE, "the current HIP device is not the handle's device");
         if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
         if (kind == DG_PROBE_STREAM) {
-            if (!buf || bytes == 0 || bytes % 16 || grid <= 0)
-                return fail(DG_ERR_INVALID_ARG, "stream probe: buf, a multiple of 16 bytes and grid > 0");
+            if (!buf || bytes == 0 || bytes % 16 || grid <= 0 || param < 0 || (param >> 1) > 4096)
+                return fail(DG_ERR_INVALID_ARG,
+                            "stream probe: buf, a multiple of 16 bytes, grid > 0, 0 <= param, at most 4096 passes");
         } else if (kind == DG_PROBE_MFMA) {
             if (param < 0 || grid <= 0) return fail(DG_ERR_INVALID_ARG, "MFMA probe: param >= 0 and grid > 0");
         } else if (kind == DG_PROBE_LDS) {
@@ -420,7 +657,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
             Problem pr;
             s = describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
             if (s) return s;
-            PlanResult r = plan_problem(pr, h->desc, o);
+            PlanResult r = plan_problem(pr, h->desc, o, h->eff.empty() ? nullptr : &h->eff);
             if (r.status != DG_OK) return fail(r.status, r.message);
             best[i] = r.pareto.front().est_us;
         }
@@ -461,7 +698,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
                 Problem pr;
                 s = describe(M, N, ks[i], dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
                 if (s) return s;   // (every sample passed above; kept for safety)
-                PlanResult r = plan_problem(pr, h->desc, v);
+                PlanResult r = plan_problem(pr, h->desc, v, h->eff.empty() ? nullptr : &h->eff);
                 if (r.status != DG_OK) {
                     ok = false;
                     break;
@@ -505,7 +742,7 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K, con
         Problem pr;
         dg_status s = describe(M, N, K, dt, lay, group_k, epi_kind, 0, o.pad_k, pr);
         if (s) return s;
-        PlanResult r = plan_problem(pr, h->desc, o);
+        PlanResult r = plan_problem(pr, h->desc, o, h->eff.empty() ? nullptr : &h->eff);
         if (r.status != DG_OK) return fail(r.status, r.message);
         if (count) *count = (int32_t)r.pareto.size();
         for (int i = 0; i < cap && i < (int)r.pareto.size(); ++i) {

@@ -185,7 +185,31 @@ double clk_per_us(const dg_device_desc &d) { return d.clock_ghz * 1e3; }
 
 double hbm_us(double bytes, const dg_device_desc &d) { return bytes / (d.hbm_gbps * 1e3); }
 
-constexpr double LAUNCH_US = 2.0;
+// Launch cost: the probe's empty launch when measured.
+double launch_us(const dg_device_desc &d) { return d.launch_us > 0 ? d.launch_us : 2.0; }
+
+// MFMA operations per microsecond per CU: the published rate (mfma_ops_per_clk_cu
+// at the peak clock), or the probe's sustained fp16 rate (int8 and the fp8
+// block-scaled MFMA at twice it).
+double published_mfma_cu_us(int path, const dg_device_desc &d) { return mfma_ops_per_clk_cu(path) * clk_per_us(d); }
+double probed_mfma_cu_us(int path, const dg_device_desc &d)
+{
+    if (d.mfma_tflops_f16 <= 0) return published_mfma_cu_us(path, d);
+    const double f16 = d.mfma_tflops_f16 * 1e6 / d.cu_count;
+    return (path == P_I8 || path == P_MX) ? 2 * f16 : f16;
+}
+
+// LDS bytes a CU reads per clock: two bytes per bank, the bank count being twice
+// the probe's full-serialisation stride (64 banks on gfx950; fragment reads
+// reach about that rate).
+double lds_bytes_per_clk(const dg_device_desc &d)
+{
+    const int stride = d.lds_conflict_stride_words > 0 ? d.lds_conflict_stride_words : 32;
+    return 2.0 * 2 * stride;
+}
+
+// Last-level cache: operands larger than it are streamed from HBM.
+double mall_bytes(const dg_device_desc &d) { return d.mall_bytes > 0 ? d.mall_bytes : 256.0 * 1024 * 1024; }
 
 // Workspace bytes of a plan with S slices: the partial sums, with one more
 // slice for the pad_k tail (which is then the only slice when the aligned
@@ -217,7 +241,7 @@ double roofline_us(const Problem &pr, const dg_device_desc &d)
 }
 
 // ------------------------------------------------------------------ families
-static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
+static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o, const EffTable *eff,
                        std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
     const int KSUB = tiled_ksub(pr.path);
@@ -292,40 +316,49 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             c.grid_x = (int)tiles;
             c.grid_y = S_eff;
             c.ws_bytes = S_eff > 1 ? (int64_t)S_eff * pr.M * pr.N * 4 : 0;
-            // ---- cost model
+            // ---- cost model (microseconds)
             const double cpu = clk_per_us(d);
             const int wg_per_cu = std::max(1, occ * d.simd_per_cu / waves);
             const int64_t wgs = tiles * S_eff;
             const int64_t rounds = ceil_div(wgs, (int64_t)d.cu_count * wg_per_cu);
             const int W = (int)std::min<int64_t>(wg_per_cu, ceil_div(wgs, d.cu_count));
-            // MFMA time of one K step at the published rate, stretched by the
-            // variant's measured sustained efficiency (catalogue.h); the LDS and
-            // L2 terms only matter for variants that are not MFMA-bound.
-            const double t_mfma = 2.0 * s.bm * s.bn * BKE / mfma_ops_per_clk_cu(pr.path) /
-                                  tiled_step_efficiency(s.path, s.bm, s.bn, waves, s.kr);
+            // MFMA time of one K step: with a measured efficiency for this variant
+            // (the probe's calibration), the probed MFMA rate times it; without,
+            // the published rate times the built-in fraction (catalogue.h).  The
+            // LDS and L2 terms only matter for variants that are not MFMA-bound.
+            char nm[64];
+            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d", path_name(pr.path),
+                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE);
+            const double step_ops = 2.0 * s.bm * s.bn * BKE;
+            double t_mfma;
+            const auto hit = eff ? eff->find(nm) : EffTable::const_iterator();
+            if (eff && hit != eff->end() && hit->second > 0)
+                t_mfma = step_ops / (probed_mfma_cu_us(pr.path, d) * hit->second);
+            else
+                t_mfma = step_ops / (published_mfma_cu_us(pr.path, d) *
+                                     tiled_step_efficiency(s.path, s.bm, s.bn, waves, s.kr));
             const double stage = tiled_stage_bytes(s.path, s.bm, s.bn, s.kr);
-            const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + stage) / 128.0;
-            const double t_l2 = stage / 64.0;
+            const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + stage) / lds_bytes_per_clk(d) / cpu;
+            const double t_l2 = stage / 64.0 / cpu;
             // A K step waits for loads issued one step earlier.  When an operand is
             // streamed with almost no reuse across workgroups (one or two tile rows
-            // or columns), those loads come from HBM and the step is bound by DRAM
-            // latency (~1.7 us); otherwise mostly by L2 latency (~0.33 us).
+            // or columns), or the operands do not fit the last-level cache, those
+            // loads come from HBM and the step is bound by DRAM latency (~1.7 us);
+            // otherwise mostly by L2 latency (~0.33 us).
             const int64_t tm = ceil_div(pr.M, s.bm), tn = ceil_div(pr.N, s.bn);
-            const double lat = (tm <= 2 || tn <= 2) ? 4000.0 : 800.0;
+            const double op_bytes = pr.M * pr.K * a_elt_bytes(pr.path) + pr.K * pr.N * b_elt_bytes(pr.path);
+            const double lat = ((tm <= 2 || tn <= 2 || op_bytes > mall_bytes(d)) ? 4000.0 : 800.0) / cpu;
             const double per_step = std::max(W * std::max(t_mfma, std::max(t_lds, t_l2)), lat);
             const double steps = ceil_div(std::max(k_slice, 1), BKE);
-            const double t_comp = rounds * steps * per_step / cpu;
+            const double t_comp = rounds * steps * per_step;
             double floor_bytes = pr.M * pr.K * a_elt_bytes(pr.path) + pr.K * pr.N * b_elt_bytes(pr.path) +
                                  scale_bytes(pr);
             const double out_bytes = (double)pr.M * pr.N * elt_bytes(pr.out_type) * (pr.beta_nz ? 2 : 1);
             // the epilogue stores after the K loop, at about 70 % of HBM bandwidth
-            double est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + LAUNCH_US;
-            if (S_eff > 1) est += hbm_us((double)S_eff * pr.M * pr.N * 4 * 2 + out_bytes, d) + LAUNCH_US;
+            double est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + launch_us(d);
+            if (S_eff > 1) est += hbm_us((double)S_eff * pr.M * pr.N * 4 * 2 + out_bytes, d) + launch_us(d);
             c.est_us = est;
             c.roof_us = roofline_us(pr, d);
-            char nm[64];
-            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d", path_name(pr.path),
-                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE);
             c.name = nm;
             out.push_back(c);
         }
@@ -367,8 +400,8 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
         }
         const double t_mem = hbm_us(b_bytes, d) / (0.92 * std::max(eff, 1e-3));
         const double t_valu = valu_lane_ops / (d.cu_count * 64.0 * cpu);
-        double est = std::max(t_mem, t_valu) + hbm_us(out_bytes, d) + LAUNCH_US;
-        if (c.split_k > 1) est += hbm_us((double)c.split_k * pr.M * pr.N * 4 * 2, d) + LAUNCH_US;
+        double est = std::max(t_mem, t_valu) + hbm_us(out_bytes, d) + launch_us(d);
+        if (c.split_k > 1) est += hbm_us((double)c.split_k * pr.M * pr.N * 4 * 2, d) + launch_us(d);
         c.est_us = est;
         c.roof_us = roofline_us(pr, d);
     };
@@ -548,7 +581,7 @@ static bool better(const Candidate &a, const Candidate &b)
     return a.name < b.name;
 }
 
-PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o)
+PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o, const EffTable *eff)
 {
     PlanResult res;
     std::vector<Candidate> all;
@@ -565,7 +598,7 @@ PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_pla
         res.message = "forced tile sizes apply to the tiled path, the skinny path was forced";
         return res;
     }
-    if (want_tiled) enum_tiled(pr, d, o, all, res.enumerated, res.pruned, res.ws_pruned);
+    if (want_tiled) enum_tiled(pr, d, o, eff, all, res.enumerated, res.pruned, res.ws_pruned);
     if (want_skinny) enum_skinny(pr, d, o, all, res.enumerated, res.pruned, res.ws_pruned);
     if (all.empty() && res.ws_pruned > 0) {
         res.status = DG_ERR_WORKSPACE;

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/dg.h"
@@ -49,8 +50,14 @@ struct PlanResult {
     int ws_pruned = 0;   // candidates pruned by ws_limit
 };
 
-// Enumerate, prune, score, Pareto-filter.  Deterministic.
-PlanResult plan_problem(const Problem &pr, const dg_device_desc &desc, const dg_plan_opts &opts);
+// Measured sustained efficiency of tiled variants (kernel name -> fraction of
+// the probed MFMA rate), from the probe's JSON description.
+using EffTable = std::unordered_map<std::string, double>;
+
+// Enumerate, prune, score, Pareto-filter.  Deterministic.  `eff` may be null
+// (no calibration: the built-in fractions of the published peak are used).
+PlanResult plan_problem(const Problem &pr, const dg_device_desc &desc, const dg_plan_opts &opts,
+                        const EffTable *eff = nullptr);
 
 // Fill the public description of a candidate.
 void fill_info(const Candidate &c, dg_plan_info *out);

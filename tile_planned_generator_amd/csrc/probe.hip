@@ -11,27 +11,41 @@
 
 namespace dg {
 
-// Streams `n16` 16-byte chunks from `buf` with non-temporal loads: workgroup w
-// reads its own contiguous share, 256 consecutive chunks (4 KB) per load round
-// and eight rounds in flight, and folds them into one word per workgroup so
-// that no load is dead.
-__global__ void __launch_bounds__(256) probe_stream_kernel(const u32x4 *buf, int64_t n16, unsigned *sink)
+// Streams `n16` 16-byte chunks from `buf` `passes` times with non-temporal
+// loads (plain, cached loads when PLAIN: repeated over a buffer that fits a
+// cache level, they measure that level): workgroup w reads its own contiguous
+// share, 256 consecutive chunks (4 KB) per load round and eight rounds in
+// flight, and folds them into one word per workgroup so that no load is dead.
+template <bool PLAIN>
+DG_DEV u32x4 probe_load(const u32x4 *p)
+{
+    if constexpr (PLAIN) return *p;
+    else return __builtin_nontemporal_load(p);
+}
+
+template <bool PLAIN>
+__global__ void __launch_bounds__(256) probe_stream_kernel(const u32x4 *buf, int64_t n16, int passes,
+                                                           unsigned *sink)
 {
     unsigned acc = 0;
     const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
     const int64_t beg = (int64_t)blockIdx.x * per;
     const int64_t end = beg + per < n16 ? beg + per : n16;
-    int64_t i = beg + threadIdx.x;
-    for (; i + 7 * 256 < end; i += 8 * 256) {
-        u32x4 v[8];
+    for (int pass = 0; pass < passes; ++pass) {
+        asm volatile("" : : : "memory");   // every pass loads again
+        int64_t i = beg + threadIdx.x;
+        for (; i + 7 * 256 < end; i += 8 * 256) {
+            u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * 256);
+            for (int u = 0; u < 8; ++u) v[u] = probe_load<PLAIN>(buf + i + u * 256);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < end; i += 256) {
-        const u32x4 v = __builtin_nontemporal_load(buf + i);
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+            for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+        for (; i < end; i += 256) {
+            const u32x4 v = probe_load<PLAIN>(buf + i);
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+        acc = (acc << 1) | (acc >> 31);   // passes do not cancel
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, off, 64);
@@ -102,9 +116,16 @@ __global__ void __launch_bounds__(64) probe_lds_kernel(int stride, unsigned long
 hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s)
 {
     if (kind == 0) {
-        if (bytes % 16 || grid <= 0) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(probe_stream_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<const u32x4 *>(buf),
-                           (int64_t)(bytes / 16), reinterpret_cast<unsigned *>(out));
+        const int passes = (param >> 1) > 0 ? (param >> 1) : 1;
+        if (bytes % 16 || grid <= 0 || param < 0 || passes > 4096) return hipErrorInvalidValue;
+        if (param & 1)
+            hipLaunchKernelGGL(probe_stream_kernel<true>, dim3(grid), dim3(256), 0, s,
+                               reinterpret_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), passes,
+                               reinterpret_cast<unsigned *>(out));
+        else
+            hipLaunchKernelGGL(probe_stream_kernel<false>, dim3(grid), dim3(256), 0, s,
+                               reinterpret_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), passes,
+                               reinterpret_cast<unsigned *>(out));
     } else if (kind == 1) {
         if (param < 0 || grid <= 0) return hipErrorInvalidValue;
         hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(256), 0, s, param, reinterpret_cast<float *>(out));

@@ -64,7 +64,9 @@ class dg_device_desc(C.Structure):
                 ("lds_bytes_per_cu", C.c_int32), ("lds_bytes_per_wg", C.c_int32),
                 ("vgpr_per_lane", C.c_int32), ("max_waves_per_simd", C.c_int32),
                 ("clock_ghz", C.c_double), ("hbm_gbps", C.c_double),
-                ("l2_bytes_per_xcd", C.c_double)]
+                ("l2_bytes_per_xcd", C.c_double), ("mall_bytes", C.c_double),
+                ("mfma_tflops_f16", C.c_double), ("launch_us", C.c_double),
+                ("lds_conflict_stride_words", C.c_int32), ("calibrated", C.c_int32)]
 
 
 class dg_plan_info(C.Structure):
@@ -86,7 +88,8 @@ class dg_plan_info(C.Structure):
 
 EXPORTS = ("dg_create", "dg_create_offline", "dg_default_device_desc", "dg_destroy", "dg_plan",
            "dg_plan_candidates", "dg_plan_range", "dg_gemm", "dg_gemm_noalloc", "dg_gemm_mx", "dg_quant_mx", "dg_set_stage_clock",
-           "dg_probe", "dg_set_device_desc", "dg_last_error", "dg_status_str")
+           "dg_probe", "dg_set_device_desc", "dg_load_device_json", "dg_get_device_desc", "dg_last_error",
+           "dg_status_str")
 
 _lib = None
 
@@ -125,6 +128,8 @@ def load():
         "dg_set_stage_clock": ([H, P, i64], S),
         "dg_probe": ([H, i32, P, C.c_size_t, i32, P, i32, P], S),
         "dg_set_device_desc": ([H, C.POINTER(dg_device_desc)], S),
+        "dg_load_device_json": ([H, C.c_char_p], S),
+        "dg_get_device_desc": ([H, C.POINTER(dg_device_desc)], S),
         "dg_last_error": ([], C.c_char_p),
         "dg_status_str": ([C.c_int], C.c_char_p),
     }
@@ -167,6 +172,14 @@ def dg_plan_range(*a):
 
 def dg_gemm(*a):
     return load().dg_gemm(*a)
+
+
+def dg_load_device_json(*a):
+    return load().dg_load_device_json(*a)
+
+
+def dg_get_device_desc(*a):
+    return load().dg_get_device_desc(*a)
 
 
 def dg_gemm_noalloc(*a):
@@ -266,6 +279,16 @@ class Handle:
         """Plan with ``desc`` (a dg_device_desc, e.g. probe.load_desc(path)) from now on."""
         check(dg_set_device_desc(self.h, C.byref(desc)))
 
+    def load_device_json(self, path):
+        """Plan with the probe's JSON description at ``path`` (dg_load_device_json)."""
+        check(dg_load_device_json(self.h, str(path).encode()))
+
+    def device_desc(self):
+        """The description the handle plans with (dg_get_device_desc)."""
+        d = dg_device_desc()
+        check(dg_get_device_desc(self.h, C.byref(d)))
+        return d
+
     def set_stage_clock(self, buf):
         """Record per-workgroup stage clocks of tiled launches into ``buf`` (a
         device uint64/int64 tensor, 8 entries per workgroup), or stop (None)."""
@@ -302,8 +325,9 @@ class Handle:
                           scales.data_ptr(), scales.stride(0), stream))
 
     def gemm_mx(self, A, SA, B, SB, C_out, *, alpha=1.0, bias=None, epilogue="none", K=None,
-                opts=None, workspace=None, stream=None):
-        """C_out = act(alpha * (A.B) + bias) through dg_gemm_mx.
+                opts=None, workspace=None, stream=None, prepared=False):
+        """C_out = act(alpha * (A.B) + bias) through dg_gemm_mx (``prepared``: as
+        for gemm).
 
         A: [M, K] uint8 fp8 e4m3 codes; SA: [K/32, >= M] uint8 e8m0 scales,
         group-major; B: [N, K/2] uint8 packed e2m1 codes (pack_e2m1); SB:
@@ -330,10 +354,12 @@ class Handle:
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         if stream is None:
             stream = torch.cuda.current_stream(A.device).cuda_stream
-        check(dg_gemm_mx(self.h, M, N, K, A.data_ptr(), lda, SA.data_ptr(), SA.stride(0), B.data_ptr(),
-                         ldb, SB.data_ptr(), SB.stride(0), C_out.data_ptr(), DTYPE[c], ldc, float(alpha),
-                         C.byref(epi), C.byref(opts) if opts is not None else None, ws_ptr, ws_bytes,
-                         stream))
+        args = (self.h, M, N, K, A.data_ptr(), lda, SA.data_ptr(), SA.stride(0), B.data_ptr(),
+                ldb, SB.data_ptr(), SB.stride(0), C_out.data_ptr(), DTYPE[c], ldc, float(alpha),
+                C.byref(epi), C.byref(opts) if opts is not None else None, ws_ptr, ws_bytes, stream)
+        if prepared:
+            return info, _prepared(load().dg_gemm_mx, args, (A, SA, B, SB, C_out, bias, workspace))
+        check(dg_gemm_mx(*args))
         return info
 
     def plan(self, M, N, K, a="f16", b="f16", c="f16", b_layout=None, epilogue="none",
@@ -375,9 +401,11 @@ class Handle:
 
     def gemm(self, A, B, C_out, *, alpha=1.0, beta=0.0, D=None, bias=None, epilogue="none",
              b_scale=None, b_layout=None, K=None, requant_scale=1.0, opts=None, workspace=None,
-             stream=None, noalloc=False):
+             stream=None, noalloc=False, prepared=False):
         """C_out = act(alpha * A.B + beta * D + bias) through dg_gemm (through
         dg_gemm_noalloc, with the library's static scratch, when ``noalloc``).
+        With ``prepared`` nothing is launched: returns (plan info, a function
+        that enqueues the call with its arguments marshalled once).
 
         A: [M, K] (row-major, rows may be padded: A.stride(0) is lda).
         B: [K, N] row-major, or, with b_layout=DG_COL_MAJOR, [N, K]; for e2m1 the
@@ -432,12 +460,26 @@ class Handle:
             workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=A.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        check(dg_gemm(self.h, M, N, K, C.byref(dt), C.byref(lay), A.data_ptr(), B.data_ptr(),
-                      b_scale.data_ptr() if b_scale is not None else None, 32 if e2m1 else 0,
-                      D.data_ptr() if D is not None else None, C_out.data_ptr(), C.byref(al),
-                      C.byref(be), C.byref(epi), C.byref(opts) if opts is not None else None,
-                      ws_ptr, ws_bytes, stream))
+        args = (self.h, M, N, K, C.byref(dt), C.byref(lay), A.data_ptr(), B.data_ptr(),
+                b_scale.data_ptr() if b_scale is not None else None, 32 if e2m1 else 0,
+                D.data_ptr() if D is not None else None, C_out.data_ptr(), C.byref(al),
+                C.byref(be), C.byref(epi), C.byref(opts) if opts is not None else None,
+                ws_ptr, ws_bytes, stream)
+        if prepared:
+            return info, _prepared(load().dg_gemm, args, (A, B, C_out, D, bias, b_scale, workspace))
+        check(dg_gemm(*args))
         return info
+
+
+def _prepared(fn, args, keep):
+    """A function enqueueing fn(*args); `keep` holds the tensors the arguments
+    point into."""
+    def call():
+        s = fn(*args)
+        if s != 0:
+            check(s)
+    call.keep = keep
+    return call
 
 
 def stage_cycles(rec, wgs):

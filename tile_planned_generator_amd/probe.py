@@ -1,11 +1,15 @@
 """Hardware probe: measure the device and write the description the planner
 plans with, as JSON (the pages' per-GPU hardware description, [generator]
-section 3.2, step 1; the hardware-aware first stage of [overview] section 4.1).
+section 3.2, step 1; the micro-benchmarks whose results feed candidate
+generation, [overview] section 4.1, stage 1).
 
-    python -m tile_planned_generator_amd.probe --out mi355x.json
+    python -m tile_planned_generator_amd.probe --out tile_planned_generator_amd/devices/gfx950.json
 
-The structural fields come from the device properties; what the planner's cost
-model reads as rates is measured with the library's probe kernels (dg_probe):
+``dg_create`` reads ``<library directory>/devices/<arch>.json`` by itself, so
+the committed file is what every device handle plans with.  The structural
+fields come from the device properties; what the planner's cost model reads as
+rates is measured with the library's probe kernels (dg_probe) and its own
+GEMM kernels:
 
   hbm_gbps        streaming-read bandwidth of a buffer far larger than the
                   caches (16-byte non-temporal loads on every CU)
@@ -17,21 +21,44 @@ model reads as rates is measured with the library's probe kernels (dg_probe):
                   bank structure seen by dword accesses; 32 on MI355X), with the
                   ticks for every stride
   launch_us       an empty launch of the probe kernel on every CU
+  l2_bytes_per_xcd, mall_bytes
+                  cache capacities: repeated cached reads of buffers from 4 MiB
+                  to 1 GiB (every CU a contiguous share, so each die reads its
+                  own eighth); the read rate stays at the L2 rate while a die's
+                  eighth fits its L2, then at the last-level (MALL) rate while
+                  the whole buffer fits the MALL, then falls to HBM's
+  tiled_efficiency
+                  per compiled tiled kernel variant: the fraction of the probed
+                  MFMA rate (twice it for int8 and the fp8 MFMA) one K step
+                  sustains, measured end to end on the 4096^3 problem of the
+                  variant's path, with the epilogue's stores and the launch
+                  taken out as the planner's cost model counts them
 
 ``load_desc(path)`` turns the JSON back into a ``dg_device_desc`` (for
-``dg.Handle.set_device_desc`` or an offline handle).  The measured peak clock
-stays the device's published one: the planner's per-variant efficiencies
-already fold in the clock under load.
+``dg.Handle.set_device_desc`` or an offline handle); ``Handle.load_device_json``
+loads all of it, efficiencies included.
 """
 import argparse
 import ctypes as C
 import json
+import math
 
 from tile_planned_generator_amd import dg
 
 DESC_FIELDS = ("cu_count", "xcd_count", "simd_per_cu", "wave_size", "lds_bytes_per_cu",
                "lds_bytes_per_wg", "vgpr_per_lane", "max_waves_per_simd", "clock_ghz", "hbm_gbps",
-               "l2_bytes_per_xcd")
+               "l2_bytes_per_xcd", "mall_bytes")
+MEASURED_DESC = ("hbm_gbps", "mfma_tflops_f16", "launch_us", "lds_conflict_stride_words",
+                 "l2_bytes_per_xcd", "mall_bytes")
+
+# tiled variants of every path: (M tile, N tile, waves, K regions per step)
+VARIANTS = {
+    "f16": [(128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
+            (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2)],
+}
+VARIANTS["bf16"] = VARIANTS["i8"] = VARIANTS["f16"]
+VARIANTS["e2m1"] = VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1]
+REGION_K = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32, "mx": 128}
 
 
 def _timed(fn, reps):
@@ -47,7 +74,122 @@ def _timed(fn, reps):
     return e0.elapsed_time(e1) / reps * 1e-3   # seconds per call
 
 
-def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096):
+def cache_sizes(probe, buf, buf_bytes, cus, xcds):
+    """(l2_bytes_per_xcd, mall_bytes, {MiB: GB/s}) from cached reads of buffers
+    of growing size, each launch passing over its buffer repeatedly (about
+    512 MiB read per launch, so the launch cost does not count); 0 where a
+    level shows no step in the rate."""
+    import torch
+    mib = [m for m in (4, 8, 16, 24, 32, 48, 64, 96, 128, 160, 192, 224, 256, 320, 384, 512, 768, 1024)
+           if m << 20 <= buf_bytes]   # never past the buffer
+    grid = cus * 4
+    sink = torch.zeros(grid, dtype=torch.int32, device=buf.device)
+    rates = []
+    for m in mib:
+        nbytes = m << 20
+        passes = max(1, min(4096, 512 // m))
+        fn = lambda: probe(dg.DG_PROBE_STREAM, C.c_void_p(buf.data_ptr()), nbytes, 1 | (passes << 1), sink, grid)
+        fn()
+        t = min(_timed(fn, 5) for _ in range(3))
+        rates.append(passes * nbytes / t / 1e9)
+    by = {str(m): round(r, 1) for m, r in zip(mib, rates)}
+    # L2: the leading run of sizes within 3/4 of the best small-buffer rate.
+    # MALL: the run after it above the midpoint between its best rate and the
+    # largest buffer's (HBM) rate, when that best rate is a tenth above HBM's.
+    l2_rate, hbm_rate = max(rates[:3]), rates[-1]
+    i = 0
+    while i < len(mib) and rates[i] >= 0.75 * l2_rate:
+        i += 1
+    l2 = float((mib[i - 1] << 20) // xcds) if 0 < i < len(mib) else 0.0
+    mall = 0.0
+    if i < len(mib) and max(rates[i:]) >= 1.1 * hbm_rate:
+        mid = 0.5 * (max(rates[i:]) + hbm_rate)
+        j = i
+        while j < len(mib) and rates[j] >= mid:
+            j += 1
+        if i < j < len(mib):
+            mall = float(mib[j - 1] << 20)
+    return l2, mall, by
+
+
+def _operands(name, dev, **size):
+    """A workload's device operands; returns (workload, make, output element
+    size), make(h, opts, kmaj) giving a prepared call (B stored N x K when kmaj;
+    the e2m1 and MX operands are always so)."""
+    import torch
+    from tile_planned_generator_amd import synth
+    w = synth.make(name, device=dev, **size)
+    t = w.tensors
+    if w.path == "mx":
+        A, SA = t["A"].contiguous(), t["SA"].t().contiguous()
+        B, SB = dg.pack_e2m1(t["codes"]), t["SB"].contiguous()
+        Cout = torch.empty(w.M, w.N, dtype=torch.float16, device=dev)
+        return w, lambda h, o, kmaj=True: h.gemm_mx(A, SA, B, SB, Cout, opts=o, prepared=True), 2
+    out = {"f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}[w.out]
+    Cout = torch.empty(w.M, w.N, dtype=out, device=dev)
+    A = t["A"].contiguous()
+    if w.path == "e2m1":
+        B, S = dg.pack_e2m1(t["codes"]), dg.scales_gn(t["scale"])
+        return w, lambda h, o, kmaj=True: h.gemm(A, B, Cout, b_scale=S, opts=o, prepared=True), 2
+    Bn = t["B"].contiguous()
+    Bk = []
+
+    def make(h, o, kmaj=False):
+        if kmaj and not Bk:
+            Bk.append(Bn.t().contiguous())
+        return h.gemm(A, Bk[0] if kmaj else Bn, Cout, b_layout=dg.DG_COL_MAJOR if kmaj else dg.DG_ROW_MAJOR,
+                      opts=o, prepared=True)
+    return w, make, Cout.element_size()
+
+
+def calibrate(h, desc, dev, reps=40, rounds=3, paths=None):
+    """Per tiled variant: the fraction of the probed MFMA rate a K step sustains
+    on the 4096^3 problem of its path, with the epilogue's stores and the launch
+    taken out as the planner's cost model counts them.  Returns ({kernel name:
+    efficiency}, {kernel name: microseconds})."""
+    import torch
+    work = [("f16_4096x4096x4096", "f16", (False, True), {}), ("i8_4096x4096x4096", "i8", (False, True), {}),
+            ("bf16_16x4096x131072", "bf16", (False, True), dict(M=4096, N=4096, K=4096)),
+            ("e2m1_4096x4096x4096", "e2m1", (True,), {}), ("mx_4096x4096x4096", "mx", (True,), {})]
+    f16_cu_us = desc["mfma_tflops_f16"] * 1e6 / desc["cu_count"]
+    eff, times = {}, {}
+    for name, path, layouts, size in work:
+        if paths is not None and path not in paths:
+            continue
+        w, make, osz = _operands(name, dev, **size)
+        for kmaj in layouts:
+            calls = []
+            for bm, bn, nw, kr in VARIANTS[path]:
+                o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=nw, force_split_k=1,
+                                    force_k_tile=REGION_K[path] * kr, force_path=dg.DG_PATH_TILED)
+                try:
+                    calls.append(make(h, o, kmaj))
+                except dg.DGError:
+                    continue
+            meas = {i.kernel_name.decode(): [] for i, _ in calls}
+            for _ in range(rounds):            # interleaved, so that drift hits all alike
+                for info, call in calls:
+                    meas[info.kernel_name.decode()].append(_timed(call, reps) * 1e6)
+            for info, call in calls:
+                nm = info.kernel_name.decode()
+                t_us = sorted(meas[nm])[len(meas[nm]) // 2]
+                wg_cu = max(1, info.waves_per_simd * desc["simd_per_cu"] // info.waves_per_wg)
+                rnds = math.ceil(info.grid / (desc["cu_count"] * wg_cu))
+                W = min(wg_cu, math.ceil(info.grid / desc["cu_count"]))
+                steps = info.n_main + info.n_tail
+                store = w.M * w.N * osz / (0.7 * desc["hbm_gbps"] * 1e3)
+                per_step = (t_us - store - desc["launch_us"]) / (rnds * steps)
+                rate = f16_cu_us * (2 if path in ("i8", "mx") else 1)
+                step_ops = 2.0 * info.m_tile * info.n_tile * info.k_main
+                eff[nm] = round(min(1.5, W * step_ops / (rate * per_step)), 4)
+                times[nm] = round(t_us, 2)
+            del calls
+        del w, make
+        torch.cuda.empty_cache()
+    return eff, times
+
+
+def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=True):
     """Run the probes on HIP device ``device``; returns the JSON-ready dict."""
     import torch
     torch.cuda.set_device(device)
@@ -68,6 +210,8 @@ def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096):
         sink = torch.zeros(grid, dtype=torch.int32, device=device)
         t = _timed(lambda: probe(dg.DG_PROBE_STREAM, C.c_void_p(buf.data_ptr()), stream_bytes, 0, sink, grid), 20)
         hbm_gbps = stream_bytes / t / 1e9
+        # cache capacities (cached re-reads of growing buffers)
+        l2, mall, by_mib = cache_sizes(probe, buf, stream_bytes, cus, base.xcd_count)
         del buf
 
         # MFMA rate (two workgroups of four waves per CU: two waves per SIMD)
@@ -91,30 +235,36 @@ def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096):
             lds[s] = min(vals)
         worst = lds[256]
         conflict_stride = min(s for s in lds if lds[s] >= 0.9 * worst)
-    finally:
-        h.close()
 
-    desc = {f: getattr(base, f) for f in DESC_FIELDS}
-    desc.update(cu_count=cus, lds_bytes_per_cu=int(getattr(props, "shared_memory_per_multiprocessor", 0) or
-                                                     desc["lds_bytes_per_cu"]),
-                hbm_gbps=round(hbm_gbps, 1))
-    return {
-        "arch": props.gcnArchName.split(":")[0],
-        "name": props.name,
-        "desc": desc,
-        "measured": {
+        desc = {f: getattr(base, f) for f in DESC_FIELDS}
+        desc.update(cu_count=cus, lds_bytes_per_cu=int(getattr(props, "shared_memory_per_multiprocessor", 0) or
+                                                         desc["lds_bytes_per_cu"]),
+                    hbm_gbps=round(hbm_gbps, 1))
+        measured = {
             "hbm_gbps": round(hbm_gbps, 1),
             "mfma_tflops_f16": round(mfma_tflops, 1),
             "mfma_clock_ghz": round(mfma_clock, 3),
             "lds_conflict_stride_words": conflict_stride,
             "lds_ticks_by_stride": {str(k): v for k, v in lds.items()},
             "launch_us": round(t_0 * 1e6, 2),
-        },
-    }
+            "l2_bytes_per_xcd": l2,
+            "mall_bytes": mall,
+            "cached_read_gbps_by_mib": {str(k): v for k, v in by_mib.items()},
+        }
+        out = {"arch": props.gcnArchName.split(":")[0], "name": props.name, "desc": desc, "measured": measured}
+        if calibrate_tiles:
+            cal = dict(desc, **{k: measured[k] for k in ("mfma_tflops_f16", "launch_us")})
+            eff, times = calibrate(h, cal, device)
+            out["tiled_efficiency"] = eff
+            out["tiled_us_4096"] = times
+    finally:
+        h.close()
+    return out
 
 
 def load_desc(path_or_dict):
-    """A dg_device_desc from a probe JSON file (or its dict)."""
+    """A dg_device_desc from a probe JSON file (or its dict): the structural
+    fields, then the measured ones."""
     d = path_or_dict
     if not isinstance(d, dict):
         with open(d) as f:
@@ -125,6 +275,9 @@ def load_desc(path_or_dict):
     for f in DESC_FIELDS:
         if f in d["desc"]:
             setattr(out, f, type(getattr(out, f))(d["desc"][f]))
+    for f in MEASURED_DESC:
+        if f in d.get("measured", {}):
+            setattr(out, f, type(getattr(out, f))(d["measured"][f]))
     return out
 
 
@@ -132,13 +285,14 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--device", type=int, default=0)
     ap.add_argument("--out", default="")
+    ap.add_argument("--no-calibrate", action="store_true", help="skip the per-variant GEMM timing")
     a = ap.parse_args()
-    r = measure(a.device)
+    r = measure(a.device, calibrate_tiles=not a.no_calibrate)
     text = json.dumps(r, indent=1)
     if a.out:
         with open(a.out, "w") as f:
             f.write(text + "\n")
-    print(text)
+    print(text, flush=True)
 
 
 if __name__ == "__main__":
