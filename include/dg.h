@@ -432,11 +432,13 @@ dg_status dg_set_device_desc(dg_handle_t h, const dg_device_desc *desc);
  * (tile_planned_generator_amd/probe.py): a JSON object whose "desc" object holds
  * dg_device_desc fields by name, whose "measured" object holds the probed rates
  * (hbm_gbps, mfma_tflops_f16, launch_us, lds_conflict_stride_words, l2_bytes_per_xcd,
- * mall_bytes) and whose "tiled_efficiency" object maps tiled kernel names (as in
+ * mall_bytes), whose "tiled_efficiency" object maps tiled kernel names (as in
  * dg_plan_info.kernel_name) to the fraction of the probed MFMA rate the variant
- * sustains per K step, measured on the 4096^3 problem of its path.  The planner
- * then scores with these numbers instead of its built-in fallbacks, and cached
- * plans are dropped.  dg_create loads <library directory>/devices/<arch>.json by
+ * sustains per K step, and whose "tiled_round_us" object maps them to the fixed
+ * time of one round of its workgroups (entry, epilogue, launch share), both
+ * fitted from timings at two K lengths of each path's 4096 x 4096 problem on
+ * operands not in the caches.  The planner then scores with these numbers
+ * instead of its built-in fallbacks, and cached plans are dropped.  dg_create loads <library directory>/devices/<arch>.json by
  * itself when it exists and describes the device (the environment variable
  * DG_DEVICE_JSON names another file; set to an empty string it disables this).
  * Errors: DG_ERR_INVALID_STATE (handle), DG_ERR_INVALID_ARG (path NULL,

@@ -45,19 +45,31 @@ def test_probe_measures_the_device(h):  # noqa: F811
         h.load_device_json(SHIPPED)
 
 
-def test_calibration_of_one_path(h):  # noqa: F811
-    # every int8 variant timed on the 4096^3 problem: efficiencies in (0, 1.5];
-    # of the 256 x 256 variants (one workgroup per CU, so the same rounds), the
-    # faster has the higher efficiency
+def test_calibration_of_one_path(h, tmp_path):  # noqa: F811
+    # every int8 variant timed at two K lengths: efficiencies in (0, 1.5] and
+    # round times >= 0; with them loaded, the planner's estimate of each forced
+    # variant at K = 4096 is the measured time (the fit passes through it)
     d = json.load(open(SHIPPED))
     desc = dict(d["desc"], mfma_tflops_f16=d["measured"]["mfma_tflops_f16"],
                 launch_us=d["measured"]["launch_us"])
-    eff, us = probe.calibrate(h, desc, "cuda:0", reps=10, rounds=1, paths=("i8",))
+    eff, round_us, us = probe.calibrate(h, desc, "cuda:0", reps=10, rounds=1, paths=("i8",))
     assert len(eff) == 20 and all(0 < e <= 1.5 for e in eff.values())
-    for lay in ("_n_", "_k_"):
-        names = [n for n in eff if lay in n and "_256x256_" in n]
-        fastest = min(names, key=lambda n: us[n])
-        assert eff[fastest] == max(eff[n] for n in names)
+    assert set(round_us) == set(eff) and all(r >= 0 for r in round_us.values())
+    d2 = dict(d, tiled_efficiency=eff, tiled_round_us=round_us)
+    (tmp_path / "cal.json").write_text(json.dumps(d2))
+    off = dg.Handle(offline=dg.default_device_desc())
+    off.load_device_json(str(tmp_path / "cal.json"))
+    for nm in eff:
+        _, lay, mn, w, k = nm.split("_")[1:]
+        bm, bn = map(int, mn.split("x"))
+        o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=2 * int(w[-1]) if w == "w2x4" else 4,
+                            force_k_tile=int(k[1:]), force_split_k=1, force_path=dg.DG_PATH_TILED)
+        p = off.plan(4096, 4096, 4096, "i8", "i8", "i32", dg.DG_COL_MAJOR if lay == "k" else dg.DG_ROW_MAJOR,
+                     opts=o)
+        assert p.kernel_name.decode() == nm
+        # (within a few per cent: the latency floor of a K step can bind for small tiles)
+        assert abs(p.est_us - us[nm]["4096"]) <= 0.05 * us[nm]["4096"] + 1.0, (nm, p.est_us, us[nm])
+    off.close()
 
 
 def test_device_handle_plans_with_the_shipped_description(h, tmp_path):  # noqa: F811

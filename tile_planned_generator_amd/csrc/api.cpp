@@ -395,12 +395,19 @@ dg_status load_device_json(dg_handle_t h, const std::string &path)
         return fail(DG_ERR_UNSUPPORTED, path + " describes " + std::to_string(d.cu_count) + " CUs, the device has " +
                                             std::to_string(h->desc.cu_count));
     EffTable eff;
-    const std::string pre = "tiled_efficiency.";
+    const std::string pre = "tiled_efficiency.", pre_r = "tiled_round_us.";
     for (const auto &kv : f.num) {
-        if (kv.first.compare(0, pre.size(), pre) != 0) continue;
-        if (!(kv.second > 0 && kv.second <= 1.5))
-            return fail(DG_ERR_INVALID_ARG, path + ": efficiency of " + kv.first.substr(pre.size()) + " out of (0, 1.5]");
-        eff[kv.first.substr(pre.size())] = kv.second;
+        if (kv.first.compare(0, pre.size(), pre) == 0) {
+            if (!(kv.second > 0 && kv.second <= 1.5))
+                return fail(DG_ERR_INVALID_ARG,
+                            path + ": efficiency of " + kv.first.substr(pre.size()) + " out of (0, 1.5]");
+            eff.eff[kv.first.substr(pre.size())] = kv.second;
+        } else if (kv.first.compare(0, pre_r.size(), pre_r) == 0) {
+            if (!(kv.second >= 0 && kv.second < 1e6))
+                return fail(DG_ERR_INVALID_ARG,
+                            path + ": round time of " + kv.first.substr(pre_r.size()) + " out of [0, 1e6) us");
+            eff.round_us[kv.first.substr(pre_r.size())] = kv.second;
+        }
     }
     d.calibrated = (int32_t)eff.size();
     h->desc = d;

@@ -330,13 +330,16 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d", path_name(pr.path),
                           pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE);
             const double step_ops = 2.0 * s.bm * s.bn * BKE;
-            double t_mfma;
-            const auto hit = eff ? eff->find(nm) : EffTable::const_iterator();
-            if (eff && hit != eff->end() && hit->second > 0)
+            double t_mfma, round_us = -1;
+            const auto hit = eff ? eff->eff.find(nm) : std::unordered_map<std::string, double>::const_iterator();
+            if (eff && hit != eff->eff.end() && hit->second > 0) {
                 t_mfma = step_ops / (probed_mfma_cu_us(pr.path, d) * hit->second);
-            else
+                const auto r = eff->round_us.find(nm);
+                if (r != eff->round_us.end() && r->second >= 0) round_us = r->second;
+            } else {
                 t_mfma = step_ops / (published_mfma_cu_us(pr.path, d) *
                                      tiled_step_efficiency(s.path, s.bm, s.bn, waves, s.kr));
+            }
             const double stage = tiled_stage_bytes(s.path, s.bm, s.bn, s.kr);
             const double t_lds = (waves * (BKE / KSUB) * (FM + FN) * 1024.0 + stage) / lds_bytes_per_clk(d) / cpu;
             const double t_l2 = stage / 64.0 / cpu;
@@ -354,9 +357,20 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             double floor_bytes = pr.M * pr.K * a_elt_bytes(pr.path) + pr.K * pr.N * b_elt_bytes(pr.path) +
                                  scale_bytes(pr);
             const double out_bytes = (double)pr.M * pr.N * elt_bytes(pr.out_type) * (pr.beta_nz ? 2 : 1);
-            // the epilogue stores after the K loop, at about 70 % of HBM bandwidth
-            double est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + launch_us(d);
-            if (S_eff > 1) est += hbm_us((double)S_eff * pr.M * pr.N * 4 * 2 + out_bytes, d) + launch_us(d);
+            double est;
+            if (round_us >= 0) {
+                // measured: each round of workgroups costs its fixed time (entry,
+                // epilogue with its stores, launch share) plus its K steps
+                est = std::max(rounds * round_us + t_comp, hbm_us(floor_bytes + out_bytes, d));
+            } else {
+                // the epilogue stores after the K loop, at about 70 % of HBM bandwidth
+                est = std::max(t_comp, hbm_us(floor_bytes, d)) + hbm_us(out_bytes, d) / 0.7 + launch_us(d);
+            }
+            // a K split: the tiles' epilogues write fp32 partial sums in place of
+            // the output (measured to cost about what the output's stores do),
+            // and the reduction reads them and writes the output: one more
+            // launch
+            if (S_eff > 1) est += hbm_us((double)S_eff * pr.M * pr.N * 4 + out_bytes, d) + launch_us(d);
             c.est_us = est;
             c.roof_us = roofline_us(pr, d);
             c.name = nm;

@@ -50,9 +50,15 @@ struct PlanResult {
     int ws_pruned = 0;   // candidates pruned by ws_limit
 };
 
-// Measured sustained efficiency of tiled variants (kernel name -> fraction of
-// the probed MFMA rate), from the probe's JSON description.
-using EffTable = std::unordered_map<std::string, double>;
+// Measurements of the tiled variants, from the probe's JSON description, by
+// kernel name: the fraction of the probed MFMA rate a K step sustains, and the
+// fixed time of one round of workgroups (prologue, epilogue and launch share),
+// fitted from two K lengths of the same problem.
+struct EffTable {
+    std::unordered_map<std::string, double> eff, round_us;
+    bool empty() const { return eff.empty(); }
+    size_t size() const { return eff.size(); }
+};
 
 // Enumerate, prune, score, Pareto-filter.  Deterministic.  `eff` may be null
 // (no calibration: the built-in fractions of the published peak are used).

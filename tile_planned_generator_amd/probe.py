@@ -27,12 +27,12 @@ GEMM kernels:
                   own eighth); the read rate stays at the L2 rate while a die's
                   eighth fits its L2, then at the last-level (MALL) rate while
                   the whole buffer fits the MALL, then falls to HBM's
-  tiled_efficiency
-                  per compiled tiled kernel variant: the fraction of the probed
-                  MFMA rate (twice it for int8 and the fp8 MFMA) one K step
-                  sustains, measured end to end on the 4096^3 problem of the
-                  variant's path, with the epilogue's stores and the launch
-                  taken out as the planner's cost model counts them
+  tiled_efficiency, tiled_round_us
+                  per compiled tiled kernel variant, from timings of its path's
+                  M = N = 4096 problem at K = 4096 and 1024 on operands read
+                  from HBM: the fraction of the probed MFMA rate (twice it for
+                  int8 and the fp8 MFMA) one K step sustains, and the fixed
+                  time of one round of workgroups (entry, epilogue, launch)
 
 ``load_desc(path)`` turns the JSON back into a ``dg_device_desc`` (for
 ``dg.Handle.set_device_desc`` or an offline handle); ``Handle.load_device_json``
@@ -112,81 +112,115 @@ def cache_sizes(probe, buf, buf_bytes, cus, xcds):
     return l2, mall, by
 
 
-def _operands(name, dev, **size):
-    """A workload's device operands; returns (workload, make, output element
-    size), make(h, opts, kmaj) giving a prepared call (B stored N x K when kmaj;
-    the e2m1 and MX operands are always so)."""
+def _operands(name, dev, copies=1, **size):
+    """A workload's device operands, `copies` copies of each; returns (workload,
+    make, output element size), make(h, opts, kmaj) giving (plan info, a call
+    that enqueues the GEMM on the next copy in turn) - B stored N x K when kmaj
+    (the e2m1 and MX operands are always so)."""
     import torch
     from tile_planned_generator_amd import synth
     w = synth.make(name, device=dev, **size)
     t = w.tensors
+
+    def rep(x):
+        return [x] + [x.clone() for _ in range(copies - 1)]
+
+    def cycle(calls):
+        it = [0]
+
+        def call():
+            calls[it[0] % len(calls)][1]()
+            it[0] += 1
+        return calls[0][0], call
+
     if w.path == "mx":
-        A, SA = t["A"].contiguous(), t["SA"].t().contiguous()
-        B, SB = dg.pack_e2m1(t["codes"]), t["SB"].contiguous()
+        As, SAs = rep(t["A"].contiguous()), rep(t["SA"].t().contiguous())
+        Bs, SBs = rep(dg.pack_e2m1(t["codes"])), rep(t["SB"].contiguous())
         Cout = torch.empty(w.M, w.N, dtype=torch.float16, device=dev)
-        return w, lambda h, o, kmaj=True: h.gemm_mx(A, SA, B, SB, Cout, opts=o, prepared=True), 2
+        return w, lambda h, o, kmaj=True: cycle([h.gemm_mx(As[i], SAs[i], Bs[i], SBs[i], Cout, opts=o,
+                                                           prepared=True) for i in range(copies)]), 2
     out = {"f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}[w.out]
     Cout = torch.empty(w.M, w.N, dtype=out, device=dev)
-    A = t["A"].contiguous()
+    As = rep(t["A"].contiguous())
     if w.path == "e2m1":
-        B, S = dg.pack_e2m1(t["codes"]), dg.scales_gn(t["scale"])
-        return w, lambda h, o, kmaj=True: h.gemm(A, B, Cout, b_scale=S, opts=o, prepared=True), 2
-    Bn = t["B"].contiguous()
+        Bs, Ss = rep(dg.pack_e2m1(t["codes"])), rep(dg.scales_gn(t["scale"]))
+        return w, lambda h, o, kmaj=True: cycle([h.gemm(As[i], Bs[i], Cout, b_scale=Ss[i], opts=o, prepared=True)
+                                                 for i in range(copies)]), 2
+    Bn = rep(t["B"].contiguous())
     Bk = []
 
     def make(h, o, kmaj=False):
         if kmaj and not Bk:
-            Bk.append(Bn.t().contiguous())
-        return h.gemm(A, Bk[0] if kmaj else Bn, Cout, b_layout=dg.DG_COL_MAJOR if kmaj else dg.DG_ROW_MAJOR,
-                      opts=o, prepared=True)
+            Bk.extend(b.t().contiguous() for b in Bn)
+        Bs = Bk if kmaj else Bn
+        return cycle([h.gemm(As[i], Bs[i], Cout, b_layout=dg.DG_COL_MAJOR if kmaj else dg.DG_ROW_MAJOR,
+                             opts=o, prepared=True) for i in range(copies)])
     return w, make, Cout.element_size()
 
 
-def calibrate(h, desc, dev, reps=40, rounds=3, paths=None):
-    """Per tiled variant: the fraction of the probed MFMA rate a K step sustains
-    on the 4096^3 problem of its path, with the epilogue's stores and the launch
-    taken out as the planner's cost model counts them.  Returns ({kernel name:
-    efficiency}, {kernel name: microseconds})."""
+# operand bytes the calibration cycles through: twice the L2s and the MALL
+COLD_BYTES = 576 << 20
+
+
+def calibrate(h, desc, dev, reps=40, rounds=3, paths=None, ks=(4096, 1024)):
+    """Per tiled variant, from timings of the path's M = N = 4096 problem at two
+    K lengths (operands cycled through copies that exceed the caches, so every
+    launch reads them from HBM): the time of one K step and the fixed time of
+    one round of workgroups, fitted to t = rounds * (round + steps * step).
+    Returns ({kernel name: efficiency}, {kernel name: round us}, {kernel name:
+    microseconds at each K}); the efficiency is the step time as a fraction of
+    the probed MFMA rate (twice it for int8 and the fp8 MFMA), counting the
+    workgroups a CU runs at once."""
     import torch
-    work = [("f16_4096x4096x4096", "f16", (False, True), {}), ("i8_4096x4096x4096", "i8", (False, True), {}),
-            ("bf16_16x4096x131072", "bf16", (False, True), dict(M=4096, N=4096, K=4096)),
-            ("e2m1_4096x4096x4096", "e2m1", (True,), {}), ("mx_4096x4096x4096", "mx", (True,), {})]
+    work = [("f16_4096x4096x4096", "f16", (False, True)), ("i8_4096x4096x4096", "i8", (False, True)),
+            ("bf16_16x4096x131072", "bf16", (False, True)), ("e2m1_4096x4096x4096", "e2m1", (True,)),
+            ("mx_4096x4096x4096", "mx", (True,))]
     f16_cu_us = desc["mfma_tflops_f16"] * 1e6 / desc["cu_count"]
-    eff, times = {}, {}
-    for name, path, layouts, size in work:
+    eff, round_us, times = {}, {}, {}
+    for name, path, layouts in work:
         if paths is not None and path not in paths:
             continue
-        w, make, osz = _operands(name, dev, **size)
-        for kmaj in layouts:
-            calls = []
-            for bm, bn, nw, kr in VARIANTS[path]:
-                o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=nw, force_split_k=1,
-                                    force_k_tile=REGION_K[path] * kr, force_path=dg.DG_PATH_TILED)
-                try:
-                    calls.append(make(h, o, kmaj))
-                except dg.DGError:
-                    continue
-            meas = {i.kernel_name.decode(): [] for i, _ in calls}
-            for _ in range(rounds):            # interleaved, so that drift hits all alike
+        rate = f16_cu_us * (2 if path in ("i8", "mx") else 1)
+        fits = {}   # kernel name -> [(rounds, steps, W, step ops, us)] per K
+        for K in ks:
+            from tile_planned_generator_amd import synth
+            w0 = synth.make(name, M=8, N=8, K=K)
+            per = sum(x.numel() * x.element_size() for x in w0.tensors.values()) * 4096 // 8
+            copies = max(1, -(-COLD_BYTES // per))
+            w, make, osz = _operands(name, dev, copies=copies, M=4096, N=4096, K=K)
+            for kmaj in layouts:
+                calls = []
+                for bm, bn, nw, kr in VARIANTS[path]:
+                    o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=nw, force_split_k=1,
+                                        force_k_tile=REGION_K[path] * kr, force_path=dg.DG_PATH_TILED)
+                    try:
+                        calls.append(make(h, o, kmaj))
+                    except dg.DGError:
+                        continue
+                meas = {i.kernel_name.decode(): [] for i, _ in calls}
+                for _ in range(rounds):            # interleaved, so that drift hits all alike
+                    for info, call in calls:
+                        meas[info.kernel_name.decode()].append(_timed(call, reps) * 1e6)
                 for info, call in calls:
-                    meas[info.kernel_name.decode()].append(_timed(call, reps) * 1e6)
-            for info, call in calls:
-                nm = info.kernel_name.decode()
-                t_us = sorted(meas[nm])[len(meas[nm]) // 2]
-                wg_cu = max(1, info.waves_per_simd * desc["simd_per_cu"] // info.waves_per_wg)
-                rnds = math.ceil(info.grid / (desc["cu_count"] * wg_cu))
-                W = min(wg_cu, math.ceil(info.grid / desc["cu_count"]))
-                steps = info.n_main + info.n_tail
-                store = w.M * w.N * osz / (0.7 * desc["hbm_gbps"] * 1e3)
-                per_step = (t_us - store - desc["launch_us"]) / (rnds * steps)
-                rate = f16_cu_us * (2 if path in ("i8", "mx") else 1)
-                step_ops = 2.0 * info.m_tile * info.n_tile * info.k_main
-                eff[nm] = round(min(1.5, W * step_ops / (rate * per_step)), 4)
-                times[nm] = round(t_us, 2)
-            del calls
-        del w, make
-        torch.cuda.empty_cache()
-    return eff, times
+                    nm = info.kernel_name.decode()
+                    t_us = sorted(meas[nm])[len(meas[nm]) // 2]
+                    wg_cu = max(1, info.waves_per_simd * desc["simd_per_cu"] // info.waves_per_wg)
+                    rnds = math.ceil(info.grid / (desc["cu_count"] * wg_cu))
+                    W = min(wg_cu, math.ceil(info.grid / desc["cu_count"]))
+                    fits.setdefault(nm, []).append((rnds, info.n_main + info.n_tail, W,
+                                                    2.0 * info.m_tile * info.n_tile * info.k_main, t_us))
+                    times.setdefault(nm, {})[str(K)] = round(t_us, 2)
+                del calls
+            del w, make
+            torch.cuda.empty_cache()
+        for nm, pts in fits.items():
+            (r1, s1, W, ops, t1), (r2, s2, _, _, t2) = pts[0], pts[-1]
+            step = (t1 / r1 - t2 / r2) / (s1 - s2) if s1 != s2 else 0.0
+            if step <= 0:   # no usable second point: the whole time is steps
+                step = t1 / (r1 * s1)
+            eff[nm] = round(min(1.5, W * ops / (rate * step)), 4)
+            round_us[nm] = round(max(0.0, t1 / r1 - s1 * step), 3)
+    return eff, round_us, times
 
 
 def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=True):
@@ -254,9 +288,10 @@ def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=Tru
         out = {"arch": props.gcnArchName.split(":")[0], "name": props.name, "desc": desc, "measured": measured}
         if calibrate_tiles:
             cal = dict(desc, **{k: measured[k] for k in ("mfma_tflops_f16", "launch_us")})
-            eff, times = calibrate(h, cal, device)
+            eff, round_us, times = calibrate(h, cal, device)
             out["tiled_efficiency"] = eff
-            out["tiled_us_4096"] = times
+            out["tiled_round_us"] = round_us
+            out["tiled_us_by_k"] = times
     finally:
         h.close()
     return out
