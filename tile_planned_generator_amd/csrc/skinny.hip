@@ -244,23 +244,29 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
 // (group-major, ld_scale per group).
 // Four columns per wave, 16 lanes each (16 columns per workgroup); lane q of a
 // column takes the 32-code groups q, q+16, ... of the slice: one 16-byte load of
-// codes, one fp16 scale, the group's dot product with A in fp32
+// codes, its fp16 scale, the group's dot product with A in fp32
 // (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then v_dot2_f32_f16), and the
-// scale applied to the group sum.  A's slice is staged in LDS once per
-// workgroup, after the first codes are requested; groups are taken GU at a
-// time, all their loads issued before any arithmetic; the 16 lanes of a column
-// are summed in a fixed order at the end.
+// scale applied to the group sum.  A's slice and the slice's scales of the
+// workgroup's 16 columns (one 32-byte piece per group row of the group-major
+// scale array, fetched as dwords) are staged in LDS once per workgroup, after
+// the first codes are requested; groups are taken GU at a time, all their loads
+// issued before any arithmetic; the 16 lanes of a column are summed in a fixed
+// order at the end.
 constexpr int E2M1_COLS_PER_WG = 16;
 constexpr int E2M1_A_LDS = 32768;   // bytes of A staged per workgroup
+constexpr int E2M1_MAX_GROUPS = E2M1_A_LDS / 2 / 32;   // groups of the longest slice (MR = 1)
 
 template <int MR>
 __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
 {
     constexpr int GU = MR <= 2 ? 8 : 4;   // groups in flight per lane
     __shared__ __attribute__((aligned(16))) _Float16 sA[E2M1_A_LDS / 2];
+    __shared__ __attribute__((aligned(16))) _Float16 sS[E2M1_MAX_GROUPS * E2M1_COLS_PER_WG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane & 15;
-    const int n = blockIdx.x * E2M1_COLS_PER_WG + wave * 4 + (lane >> 4);
+    const int cw = wave * 4 + (lane >> 4);   // column within the workgroup
+    const int n0 = blockIdx.x * E2M1_COLS_PER_WG;
+    const int n = n0 + cw;
     const bool valid = n < p.N;
     const int nc = valid ? n : 0;   // columns past N read column 0 and store nothing
     const int split = blockIdx.y;
@@ -271,23 +277,34 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
     const int M = p.M;
 
     const char *Bc = reinterpret_cast<const char *>(p.B) + (int64_t)nc * (p.ldb / 2);
-    const _Float16 *S = reinterpret_cast<const _Float16 *>(p.scale) + nc;   // group g at S[g * ld_scale]
     const _Float16 *A = reinterpret_cast<const _Float16 *>(p.A);
 
     u32x4 c[GU];
-    float sc[GU];
     int gcs[GU];
     auto load_groups = [&](int g0) {
 #pragma unroll
         for (int u = 0; u < GU; ++u) {
             const int gi = g0 + 16 * u;
-            const bool in = gi < gend;
-            gcs[u] = in ? gi : gbeg;   // a valid group; its terms are dropped below
+            gcs[u] = gi < gend ? gi : gbeg;   // a valid group; its terms are dropped below
             c[u] = ld16_nt(Bc + (int64_t)gcs[u] * 16);
-            sc[u] = in ? (float)S[(int64_t)gcs[u] * p.ld_scale] : 0.f;
         }
     };
     if (gbeg + q < gend) load_groups(gbeg + q);
+
+    // stage the slice's scales of the workgroup's columns: group g, columns
+    // n0 .. n0+15 are 32 contiguous bytes (8 dwords) of the group-major array
+    // (rows of ld_scale fp16, ld_scale even); buffer loads return 0 past the
+    // array's end, and columns past N are never used
+    {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(p.scale), (short)0, (int)((int64_t)(p.K / 32) * p.ld_scale * 2), 0x00020000);
+        unsigned *sSw = reinterpret_cast<unsigned *>(sS);
+        for (int idx = tid; idx < (gend - gbeg) * 8; idx += 256) {
+            const int gr = idx >> 3, d = idx & 7;
+            const int off = (int)(((int64_t)(gbeg + gr) * p.ld_scale + n0) * 2 + 4 * d);
+            sSw[idx] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        }
+    }
 
     // stage A[0:M][kbeg:kend] (16-byte chunks; rows past M are zero)
     for (int idx = tid; idx < MR * L / 8; idx += 256) {
@@ -331,7 +348,7 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
                                                       dsum, false);
                     }
                 }
-                if (g0 + 16 * u < gend) acc[m] += sc[u] * dsum;
+                if (g0 + 16 * u < gend) acc[m] += (float)sS[(gcs[u] - gbeg) * E2M1_COLS_PER_WG + cw] * dsum;
             }
         }
     }
