@@ -414,10 +414,23 @@ dg_status dg_set_stage_clock(dg_handle_t h, uint64_t *buf, int64_t entries);
  *   DG_PROBE_LDS     one wave, 1024 dword LDS reads with lane l at word
  *                    l * param (1 <= param <= 16384); `out`: device uint64[2],
  *                    out[0] = s_memtime ticks of the reads
+ *   DG_PROBE_MFMA_DATA  the clock the MFMAs hold on given data: `grid`
+ *                    workgroups of 8 waves (two per SIMD), each wave param >> 3
+ *                    (>= 1) rounds of 8 independent int8 32x32x32 MFMAs on
+ *                    operands read once from `buf` (`bytes`, a multiple of 16,
+ *                    indexed modulo its size).  param & 7 is the mode: 0 one
+ *                    operand pair for every MFMA; 1 eight pairs, a different
+ *                    one for each MFMA of a round; 2 as 1 plus LDS reads of
+ *                    buf's data at 0.75 KB per MFMA (the tiled kernel's
+ *                    fragment traffic); 3 as 1 with A zero; 4 as 2 with the LDS
+ *                    holding zeros; 5 the LDS reads alone.  `out`: device
+ *                    uint64[3 * grid]: per workgroup the s_memtime ticks (the
+ *                    shader clock) and the 100 MHz s_memrealtime ticks of its
+ *                    first wave from entry to exit, and a checksum
  * Errors: DG_ERR_INVALID_STATE (handle NULL, destroyed or offline; wrong current
  * device), DG_ERR_INVALID_ARG (NULL out, NULL buf for the stream probe, bad
  * size, grid or param), DG_ERR_HIP (launch failure). */
-typedef enum { DG_PROBE_STREAM = 0, DG_PROBE_MFMA = 1, DG_PROBE_LDS = 2 } dg_probe_kind;
+typedef enum { DG_PROBE_STREAM = 0, DG_PROBE_MFMA = 1, DG_PROBE_LDS = 2, DG_PROBE_MFMA_DATA = 3 } dg_probe_kind;
 dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, int32_t param, void *out,
                    int32_t grid, dg_stream_t stream);
 

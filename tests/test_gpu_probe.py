@@ -86,10 +86,38 @@ def test_device_handle_plans_with_the_shipped_description(h, tmp_path):  # noqa:
     assert h.device_desc().cu_count == 256 and h.device_desc().calibrated == got.calibrated
 
 
+def test_mfma_data_probe(h):  # noqa: F811
+    # every mode runs, the clock and busy share are in range, and MFMAs whose A
+    # operands are all zero run at least as fast a clock as random ones
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = dg.C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(kind, buf, nbytes, param, out, grid):
+        dg.check(dg.dg_probe(h.h, kind, buf, nbytes, param, dg.C.c_void_p(out.data_ptr()), grid, stream))
+
+    res = probe.mfma_data_clock(launch, 0, cus, seconds=0.3, rounds=4000)
+    print(res)
+    assert set(res) == set(probe.DATA_MODES.values())
+    for name, row in res.items():
+        assert 0.3 < row["shader_ghz"] < 2.6, (name, row)
+        if name != "lds_reads_only":
+            assert 0 < row["int8_tops"] < 5033 * 1.05
+    for name in ("one_pair", "random", "zero_a"):
+        assert 0.8 < res[name]["mfma_busy"] < 1.05, (name, res[name])
+    assert res["zero_a"]["shader_ghz"] >= 0.95 * res["random"]["shader_ghz"]
+
+
 def test_probe_argument_errors(h):  # noqa: F811
     assert dg.dg_probe(h.h, dg.DG_PROBE_STREAM, None, 16, 0, None, 1, None) == dg.DG_ERR_INVALID_ARG
     assert dg.dg_probe(h.h, 7, None, 0, 0, dg.C.c_void_p(1), 1, None) == dg.DG_ERR_INVALID_ARG
     assert dg.dg_probe(h.h, dg.DG_PROBE_LDS, None, 0, 0, dg.C.c_void_p(1), 1, None) == dg.DG_ERR_INVALID_ARG
+    # the MFMA data probe: a source buffer, a known mode and at least one round
+    one = dg.C.c_void_p(16)
+    assert dg.dg_probe(h.h, dg.DG_PROBE_MFMA_DATA, None, 16, 1 | (8 << 3), one, 1, None) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_probe(h.h, dg.DG_PROBE_MFMA_DATA, one, 16, 6 | (8 << 3), one, 1, None) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_probe(h.h, dg.DG_PROBE_MFMA_DATA, one, 16, 1, one, 1, None) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_probe(h.h, dg.DG_PROBE_MFMA_DATA, one, 24, 1 | (8 << 3), one, 1, None) == dg.DG_ERR_INVALID_ARG
     # a pass count past the limit is refused before launch
     assert dg.dg_probe(h.h, dg.DG_PROBE_STREAM, dg.C.c_void_p(16), 16, 1 | (4097 << 1), dg.C.c_void_p(1), 1,
                        None) == dg.DG_ERR_INVALID_ARG

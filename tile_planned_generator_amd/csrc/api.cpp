@@ -595,6 +595,10 @@ dg_status dg_probe(dg_handle_t h, int32_t kind, const void *buf, size_t bytes, i
             if (param < 0 || grid <= 0) return fail(DG_ERR_INVALID_ARG, "MFMA probe: param >= 0 and grid > 0");
         } else if (kind == DG_PROBE_LDS) {
             if (param < 1 || param > 16384) return fail(DG_ERR_INVALID_ARG, "LDS probe: 1 <= param <= 16384");
+        } else if (kind == DG_PROBE_MFMA_DATA) {
+            if (!buf || bytes < 16 || bytes % 16 || grid <= 0 || (param & 7) > 5 || (param >> 3) < 1)
+                return fail(DG_ERR_INVALID_ARG,
+                            "MFMA data probe: buf, a multiple of 16 bytes, grid > 0, mode 0..5, rounds >= 1");
         } else {
             return fail(DG_ERR_INVALID_ARG, "unknown probe kind");
         }

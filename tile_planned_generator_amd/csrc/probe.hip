@@ -113,6 +113,86 @@ __global__ void __launch_bounds__(64) probe_lds_kernel(int stride, unsigned long
     if (acc == 0x12345678u) ticks[1] = acc;   // keeps the reads live
 }
 
+// The clock the MFMAs hold on given operand data.  Eight waves per workgroup
+// (two per SIMD, as in the 256x256 tiled kernel), each `rounds` rounds of 8
+// independent int8 32x32x32 MFMAs whose operands are read once from `src`
+// (n16 16-byte chunks, indexed modulo n16).  MODE:
+//   0  one operand pair for every MFMA (no change of inputs between MFMAs)
+//   1  eight operand pairs, a different one for each MFMA of a round
+//   2  as 1, plus six 16-byte LDS reads per lane per round (0.75 KB per MFMA,
+//      the fragment traffic of the tiled kernel's 128x64 wave tile), the LDS
+//      filled from src; the reads of a round are issued one round ahead
+//   3  as 1 with every A operand zero
+//   4  as 2 with the LDS holding zeros
+//   5  the LDS reads of 2 alone, no MFMAs
+// Wave 0 of each workgroup writes its s_memtime ticks (the shader clock) and
+// s_memrealtime ticks (100 MHz) from entry to exit, and the workgroup's
+// checksum, to out[3 * workgroup + 0, 1, 2].
+template <int MODE>
+__global__ void __launch_bounds__(512) probe_mfma_data_kernel(const intx4 *src, int64_t n16, int rounds,
+                                                              unsigned long long *out)
+{
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    __shared__ intx4 lds[4096];   // 64 KB
+    const int t = threadIdx.x;
+    for (int i = t; i < 4096; i += 512)
+        lds[i] = MODE == 4 ? intx4{0, 0, 0, 0} : src[((int64_t)blockIdx.x * 4096 + i) % n16];
+    __syncthreads();
+    intx4 a[8], b[8];
+    const int64_t base = ((int64_t)blockIdx.x * 512 + t) * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = MODE == 0 ? 0 : i;
+        a[i] = MODE == 3 ? intx4{0, 0, 0, 0} : src[(base + k) % n16];
+        b[i] = src[(base + 8 + k) % n16];
+    }
+    intx16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0;
+    constexpr bool READS = MODE == 2 || MODE == 4 || MODE == 5;
+    intx4 fold = {0, 0, 0, 0}, cur[6], nxt[6];
+    int off = t;
+    if (READS) {
+#pragma unroll
+        for (int j = 0; j < 6; ++j) cur[j] = lds[(off + j * 577) & 4095];
+    }
+    for (int it = 0; it < rounds; ++it) {
+        off = (off + 64) & 4095;
+        if (READS) {
+#pragma unroll
+            for (int j = 0; j < 6; ++j) nxt[j] = lds[(off + j * 577) & 4095];
+        }
+        if (MODE != 5) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[i], acc[i], 0, 0, 0);
+        }
+        if (READS) {
+#pragma unroll
+            for (int j = 0; j < 6; ++j) { fold ^= cur[j]; cur[j] = nxt[j]; }
+        }
+    }
+    int sum = fold[0] ^ fold[1] ^ fold[2] ^ fold[3];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum ^= acc[i][v];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum ^= __shfl_xor(sum, o, 64);
+    __shared__ int w[8];
+    if ((t & 63) == 0) w[t >> 6] = sum;
+    __syncthreads();
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (t == 0) {
+        int c = 0;
+        for (int i = 0; i < 8; ++i) c ^= w[i];
+        out[3 * blockIdx.x + 0] = t1 - t0;
+        out[3 * blockIdx.x + 1] = r1 - r0;
+        out[3 * blockIdx.x + 2] = (unsigned)c;
+    }
+}
+
 hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out, int grid, hipStream_t s)
 {
     if (kind == 0) {
@@ -133,6 +213,20 @@ hipError_t launch_probe(int kind, void *buf, size_t bytes, int param, void *out,
         if (param < 1 || param > 16384) return hipErrorInvalidValue;
         hipLaunchKernelGGL(probe_lds_kernel, dim3(1), dim3(64), 0, s, param,
                            reinterpret_cast<unsigned long long *>(out));
+    } else if (kind == 3) {
+        const int mode = param & 7, rounds = param >> 3;
+        if (!buf || bytes < 16 || bytes % 16 || grid <= 0 || mode > 5 || rounds < 1) return hipErrorInvalidValue;
+        const intx4 *src = reinterpret_cast<const intx4 *>(buf);
+        const int64_t n16 = (int64_t)(bytes / 16);
+        unsigned long long *o = reinterpret_cast<unsigned long long *>(out);
+        switch (mode) {
+        case 0: hipLaunchKernelGGL(probe_mfma_data_kernel<0>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        case 1: hipLaunchKernelGGL(probe_mfma_data_kernel<1>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        case 2: hipLaunchKernelGGL(probe_mfma_data_kernel<2>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        case 3: hipLaunchKernelGGL(probe_mfma_data_kernel<3>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        case 4: hipLaunchKernelGGL(probe_mfma_data_kernel<4>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        default: hipLaunchKernelGGL(probe_mfma_data_kernel<5>, dim3(grid), dim3(512), 0, s, src, n16, rounds, o); break;
+        }
     } else {
         return hipErrorInvalidValue;
     }

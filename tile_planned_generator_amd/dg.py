@@ -21,7 +21,7 @@ DG_EPI_NONE, DG_EPI_BIAS, DG_EPI_GELU_ERF, DG_EPI_BIAS_GELU_ERF, DG_EPI_REQUANT_
     DG_EPI_REQUANT_F16 = range(6)
 DG_UNIT_AUTO, DG_UNIT_MFMA, DG_UNIT_VALU = 0, 1, 2
 DG_PATH_AUTO, DG_PATH_TILED, DG_PATH_SKINNY = 0, 1, 2
-DG_PROBE_STREAM, DG_PROBE_MFMA, DG_PROBE_LDS = 0, 1, 2
+DG_PROBE_STREAM, DG_PROBE_MFMA, DG_PROBE_LDS, DG_PROBE_MFMA_DATA = 0, 1, 2, 3
 
 EPI = {"none": DG_EPI_NONE, "bias": DG_EPI_BIAS, "gelu_erf": DG_EPI_GELU_ERF,
        "bias_gelu_erf": DG_EPI_BIAS_GELU_ERF, "requant_i8": DG_EPI_REQUANT_I8,

@@ -27,6 +27,12 @@ GEMM kernels:
                   own eighth); the read rate stays at the L2 rate while a die's
                   eighth fits its L2, then at the last-level (MALL) rate while
                   the whole buffer fits the MALL, then falls to HBM's
+  int8_mfma_clock_by_data
+                  the shader clock and MFMA busy share of back-to-back int8
+                  MFMAs on random operands, on constant ones, with A zero, and
+                  with LDS reads at the tiled kernel's fragment rate (random or
+                  zero data): how much of the clock the data itself costs
+                  (recorded, not read by the planner)
   tiled_efficiency, tiled_round_us
                   per compiled tiled kernel variant, from timings of its path's
                   M = N = 4096 problem at K = 4096 and 1024 on operands read
@@ -223,7 +229,40 @@ def calibrate(h, desc, dev, reps=40, rounds=3, paths=None, ks=(4096, 1024)):
     return eff, round_us, times
 
 
-def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=True):
+# operand data of the MFMA data probe (DG_PROBE_MFMA_DATA's modes)
+DATA_MODES = {0: "one_pair", 1: "random", 2: "random_lds_reads", 3: "zero_a", 4: "random_lds_zeros",
+              5: "lds_reads_only"}
+
+
+def mfma_data_clock(probe, device, cus, seconds=1.0, rounds=20000, seed=1234):
+    """Per operand mode of DG_PROBE_MFMA_DATA (one workgroup of eight waves
+    per CU, random int8 operands from a seeded generator): the shader clock
+    the kernel ran at (s_memtime over s_memrealtime), the share of that clock
+    the MFMAs were busy, and the int8 rate.  Each mode first runs for about
+    `seconds` so that the clock settles."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 22,), dtype=torch.int32, generator=g).to(device)
+    out = torch.zeros(3 * cus, dtype=torch.int64, device=device)
+    res = {}
+    for mode, name in DATA_MODES.items():
+        def call(mode=mode):
+            probe(dg.DG_PROBE_MFMA_DATA, C.c_void_p(src.data_ptr()), src.numel() * 4, mode | (rounds << 3), out, cus)
+        t1 = _timed(call, 1)
+        _timed(call, max(1, int(seconds / t1)))          # settle
+        t = _timed(call, max(3, int(seconds / t1)))
+        o = out.view(cus, 3).cpu()
+        ghz = o[:, 0].sum().item() / o[:, 1].sum().item() * 0.1
+        row = {"shader_ghz": round(ghz, 3), "kernel_ms": round(t * 1e3, 3)}
+        if mode != 5:
+            cycles = 2 * rounds * 8 * 32                 # per SIMD: 2 waves x 8 MFMAs x 32 cycles a round
+            row["mfma_busy"] = round(cycles / (t * ghz * 1e9), 3)
+            row["int8_tops"] = round(cus * 8 * rounds * 8 * 2 * 32 * 32 * 32 / t / 1e12, 1)
+        res[name] = row
+    return res
+
+
+def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=True, data_clock=True):
     """Run the probes on HIP device ``device``; returns the JSON-ready dict."""
     import torch
     torch.cuda.set_device(device)
@@ -270,6 +309,9 @@ def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=Tru
         worst = lds[256]
         conflict_stride = min(s for s in lds if lds[s] >= 0.9 * worst)
 
+        # the clock the MFMAs hold on random operands, with and without LDS traffic
+        data = mfma_data_clock(probe, device, cus) if data_clock else None
+
         desc = {f: getattr(base, f) for f in DESC_FIELDS}
         desc.update(cu_count=cus, lds_bytes_per_cu=int(getattr(props, "shared_memory_per_multiprocessor", 0) or
                                                          desc["lds_bytes_per_cu"]),
@@ -285,6 +327,8 @@ def measure(device=0, stream_bytes=1 << 30, mfma_iters=4096, calibrate_tiles=Tru
             "mall_bytes": mall,
             "cached_read_gbps_by_mib": {str(k): v for k, v in by_mib.items()},
         }
+        if data is not None:
+            measured["int8_mfma_clock_by_data"] = data
         out = {"arch": props.gcnArchName.split(":")[0], "name": props.name, "desc": desc, "measured": measured}
         if calibrate_tiles:
             cal = dict(desc, **{k: measured[k] for k in ("mfma_tflops_f16", "launch_us")})
