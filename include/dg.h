@@ -133,7 +133,10 @@ typedef struct {
  * sm_mem_limit; section 5.3: use_hmma false for small GEMMs).  Zero-initialised
  * options mean "planner decides". */
 typedef struct {
-    int32_t force_m_tile, force_n_tile, force_k_tile; /* tiled path tile (0 = free)   */
+    int32_t force_m_tile, force_n_tile, force_k_tile; /* tiled path tile (0 = free);
+                                 * force_n_tile alone also picks the streaming
+                                 * kernels' columns per workgroup (VALU: 256, 512,
+                                 * 1024 or 2048; MFMA: 512; e2m1: 16) */
     int32_t force_split_k;    /* number of K slices (0 = free)                      */
     int32_t force_path;       /* dg_path (DG_PATH_AUTO = 0: planner decides)         */
     int32_t unit;             /* dg_unit: MFMA (matrix cores) or VALU (vector FMA)  */

@@ -241,6 +241,24 @@ def test_conflicting_compute_units(off):
     assert _status(off.plan, 1, 256, 256, opts=o)[0] == dg.DG_ERR_CONFLICT
 
 
+def test_forced_columns_pick_the_streaming_variant(off):
+    # force_n_tile alone selects the streaming kernels' columns per workgroup
+    for nt in (256, 512, 1024, 2048):
+        o = dg.dg_plan_opts(force_n_tile=nt, force_path=dg.DG_PATH_SKINNY, unit=dg.DG_UNIT_VALU)
+        p = off.plan(1, 4096, 131072, "bf16", "bf16", "bf16", opts=o)
+        assert p.n_tile == nt and p.kernel_name.decode() == f"skinny_valu_bf16_mr1_lpr{nt // 32}"
+    o = dg.dg_plan_opts(force_n_tile=512, force_path=dg.DG_PATH_SKINNY, unit=dg.DG_UNIT_MFMA)
+    assert off.plan(16, 4096, 131072, "bf16", "bf16", "bf16", opts=o).kernel_name.decode() == "skinny_mfma_bf16"
+    o = dg.dg_plan_opts(force_n_tile=16, force_path=dg.DG_PATH_SKINNY)
+    p = off.plan(1, 4096, 4096, "f16", "e2m1", "f16", dg.DG_COL_MAJOR, opts=o)
+    assert p.kernel_name.decode().startswith("skinny_e2m1") and p.n_tile == 16
+    # no streaming kernel has 128 columns per workgroup
+    o = dg.dg_plan_opts(force_n_tile=128, force_path=dg.DG_PATH_SKINNY)
+    assert _status(off.plan, 1, 4096, 131072, "bf16", "bf16", "bf16", opts=o)[0] == dg.DG_ERR_NO_CANDIDATE
+    # N = 256: only the 64-column waves keep all four waves of a workgroup busy
+    assert off.plan(1, 256, 12800, "bf16", "bf16", "bf16").kernel_name.decode() == "skinny_valu_bf16_mr1_lpr8"
+
+
 def test_unsupported_and_invalid(off):
     assert _status(off.plan, 64, 64, 64, "f16", "bf16", "f16")[0] == dg.DG_ERR_UNSUPPORTED
     assert _status(off.plan, 64, 64, 64, "f16", "f16", "bf16")[0] == dg.DG_ERR_UNSUPPORTED

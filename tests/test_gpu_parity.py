@@ -387,6 +387,21 @@ def test_skinny_valu(h, M, K):
     run(h, w, opts=dg.dg_plan_opts(unit=dg.DG_UNIT_VALU, force_split_k=3))
 
 
+@pytest.mark.parametrize("n_tile", [256, 512, 1024, 2048])
+def test_skinny_valu_every_width(h, n_tile):
+    # every column width of the VALU streaming kernel (64, 128, 256 or 512 columns
+    # per wave), with slices that end in a partial batch of rows, ragged N and
+    # padded leading dimensions
+    for name in ("bf16_1x4096x131072", "f16_256x256x256_alpha_beta_d"):
+        for M in (1, 3, 8):
+            for K, S in ((2000, 3), (4144, 0), (144, 1)):
+                w = synth.make(name, M=M, N=1000, K=K)
+                o = dg.dg_plan_opts(force_n_tile=n_tile, force_split_k=S, force_path=dg.DG_PATH_SKINNY,
+                                    unit=dg.DG_UNIT_VALU)
+                info, _ = run(h, w, opts=o, pad=8)
+                assert info.n_tile == n_tile and info.kernel_name.decode().endswith(f"lpr{n_tile // 32}")
+
+
 @pytest.mark.parametrize("M", [1, 9, 16])
 def test_skinny_mfma(h, M):
     w = synth.make("bf16_16x4096x131072", M=M, N=1000, K=4128)
@@ -417,9 +432,11 @@ def test_m_either_side_of_the_streaming_limit(h, M):
 @pytest.mark.parametrize("name,K", [("f16_256x256x256_alpha_beta_d", 32), ("bf16_16x4096x131072", 32),
                                     ("i8_4096x4096x4096", 64), ("e2m1_4096x4096x4096", 32)])
 def test_k_of_one_step(h, name, K):
-    # K equal to one K step of the tiled kernels: one main step, no tail, no split
-    info, _ = run(h, synth.make(name, M=130, N=96, K=K))
-    assert info.n_main == 1 and info.n_tail == 0 and info.split_k == 1
+    # K equal to one K step of the tiled kernels (the one-region step pinned, as
+    # the planner may otherwise take the two-region step as one short tail):
+    # one main step, no tail, no split
+    info, _ = run(h, synth.make(name, M=130, N=96, K=K), opts=dg.dg_plan_opts(force_k_tile=K))
+    assert info.n_main == 1 and info.n_tail == 0 and info.split_k == 1 and info.k_main == K
 
 
 @pytest.mark.parametrize("name,M,N,K,split,path,pad", [

@@ -53,9 +53,11 @@ namespace dg {
     DG_SKINNY_VALU_MR(X, P_F16, 64)        \
     DG_SKINNY_VALU_MR(X, P_F16, 32)        \
     DG_SKINNY_VALU_MR(X, P_F16, 16)        \
+    DG_SKINNY_VALU_MR(X, P_F16, 8)         \
     DG_SKINNY_VALU_MR(X, P_BF16, 64)       \
     DG_SKINNY_VALU_MR(X, P_BF16, 32)       \
-    DG_SKINNY_VALU_MR(X, P_BF16, 16)
+    DG_SKINNY_VALU_MR(X, P_BF16, 16)       \
+    DG_SKINNY_VALU_MR(X, P_BF16, 8)
 
 // Skinny MFMA streaming GEMM (M <= 16) over a row-major 16-bit B: X(path)
 #define DG_SKINNY_MFMA_CATALOGUE(X) X(P_F16) X(P_BF16)

@@ -162,7 +162,9 @@ std::vector<int> split_choices_grid(int64_t K, int unit, int min_slice, int forc
     if (force > 0 || grid_x <= 0) return s;
     for (double f : {0.75, 1.0, 2.0}) {
         const int v = (int)std::ceil(f * cus / (double)grid_x);
-        if (v > 1 && v <= 1024 && K / v >= min_slice && K / v >= unit &&
+        // (the slice as the kernel gets it: rounded up to the unit)
+        const int64_t slice = (K + v - 1) / v + unit - 1 - ((K + v - 1) / v + unit - 1) % unit;
+        if (v > 1 && v <= 1024 && slice >= min_slice && K / v >= unit &&
             std::find(s.begin(), s.end(), v) == s.end())
             s.push_back(v);
     }
@@ -385,7 +387,9 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
 static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
                         std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
-    if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves) return;  // tiled-only options
+    if (o.force_m_tile || o.force_k_tile || o.force_waves) return;  // tiled-only options
+    // force_n_tile picks the streaming kernels' columns per workgroup
+    auto n_ok = [&](int n_tile) { return o.force_n_tile == 0 || o.force_n_tile == n_tile; };
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
     const int occ_need = std::max(1, (int)std::ceil(o.target_occupancy * d.max_waves_per_simd - 1e-9));
     const double cpu = clk_per_us(d);
@@ -408,6 +412,10 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
             eff = wgs <= d.cu_count ? std::min(1.0, wgs / (0.75 * d.cu_count)) : wgs / (rounds * d.cu_count);
             // the share of the workgroups' columns that exist (four waves each)
             eff *= std::min(1.0, (double)pr.N / ((double)c.grid_x * 4 * cols_per_wave));
+            // waves of 64 columns (128-byte row pieces) stream about 5 % slower
+            // than wider ones (measured: bf16, M = 1, N = 4096, K = 131072,
+            // 173-179 us at 192-512 workgroups against 169 us with 128 columns)
+            if (cols_per_wave < 128) eff *= 0.95;
         } else {
             const double waves_active = c.grid_y * (double)pr.N / cols_per_wave;
             eff = std::min(1.0, waves_active / (d.cu_count * 8.0));
@@ -429,6 +437,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
             if (s.path != pr.path || s.mr < pr.M || (s.mr > 1 && s.mr / 2 >= pr.M)) continue;
             const int rpi = 64 / s.lpr;
             const int wcols = s.lpr * 8;
+            if (!n_ok(4 * wcols)) continue;
             for (int S : split_choices_grid(pr.K, 16, 64, o.force_split_k, ceil_div(pr.N, 4 * wcols), d.cu_count)) {
                 ++enumerated;
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 16) : 0;
@@ -480,7 +489,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
         o.unit != DG_UNIT_VALU) {
         const int nm_ = (int)(sizeof(k_mfma_paths) / sizeof(k_mfma_paths[0]));
         for (int id = 0; id < nm_; ++id) {
-            if (k_mfma_paths[id] != pr.path) continue;
+            if (k_mfma_paths[id] != pr.path || !n_ok(512)) continue;
             for (int S : split_choices_grid(pr.K, 32, 256, o.force_split_k, ceil_div(pr.N, 512), d.cu_count)) {
                 ++enumerated;
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 32) : 0;
@@ -529,7 +538,7 @@ static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_pla
         const int ne = (int)(sizeof(k_e2m1_mr) / sizeof(k_e2m1_mr[0]));
         for (int id = 0; id < ne; ++id) {
             const int mr = k_e2m1_mr[id];
-            if (mr < pr.M || (mr > 1 && mr / 2 >= pr.M)) continue;
+            if (mr < pr.M || (mr > 1 && mr / 2 >= pr.M) || !n_ok(16)) continue;
             for (int S : split_choices(pr.K, 32, 2048, o.force_split_k)) {
                 ++enumerated;
                 int k_slice = pr.K > 0 ? slice_len(pr.K, S, 32) : 0;
@@ -606,10 +615,9 @@ PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_pla
         res.message = "conflicting compute units: the tiled path runs on MFMA, VALU was requested";
         return res;
     }
-    if (o.force_path == DG_PATH_SKINNY &&
-        (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves)) {
+    if (o.force_path == DG_PATH_SKINNY && (o.force_m_tile || o.force_k_tile || o.force_waves)) {
         res.status = DG_ERR_CONFLICT;
-        res.message = "forced tile sizes apply to the tiled path, the skinny path was forced";
+        res.message = "forced M tile, K step and waves apply to the tiled path, the skinny path was forced";
         return res;
     }
     if (want_tiled) enum_tiled(pr, d, o, eff, all, res.enumerated, res.pruned, res.ws_pruned);

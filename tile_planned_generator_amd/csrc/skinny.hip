@@ -109,15 +109,26 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
         fma_batch(it + 1, b1);
     }
     if (it < nmain) fma_batch(it, b0);
-    for (int r = g + nmain * U * RPI; r < L; r += RPI) {
-        u32x4 b = ld16_nt(Bb + (int64_t)r * ldb_b);
-        float w[8];
-        unpack8(PATH, b, w);
+    // the rows after the last full batch (fewer than U per lane): all loaded at
+    // once, then added in ascending row order
+    {
+        const int r0 = g + nmain * U * RPI;
+        u32x4 bt[U];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            const float a = elt16(PATH, sA[m * L + r]);
+        for (int u = 0; u < U; ++u)
+            bt[u] = r0 + u * RPI < L ? ld16_nt(Bb + (int64_t)(r0 + u * RPI) * ldb_b) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[m][e] += a * w[e];
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * RPI;
+            if (r >= L) break;
+            float w[8];
+            unpack8(PATH, bt[u], w);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float a = elt16(PATH, sA[m * L + r]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[m][e] += a * w[e];
+            }
         }
     }
 
