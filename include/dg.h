@@ -153,6 +153,9 @@ typedef struct {
                                  e2m1 is not supported (DG_ERR_UNSUPPORTED).  0: such a
                                  K is DG_ERR_ALIGNMENT. */
     int32_t force_waves;      /* waves per workgroup of the tiled path (0 = free)    */
+    int32_t force_mfma;       /* MFMA output block of the tiled path: 32 (32x32) or 16
+                                 (16x16; 16-bit and int8 paths, eight-wave tiles)
+                                 (0 = free) */
 } dg_plan_opts;
 
 /* Description of the device the planner plans for.  dg_create fills it from
@@ -249,17 +252,21 @@ dg_status dg_plan_candidates(dg_handle_t h, int64_t M, int64_t N, int64_t K,
  * kernel serves every layer whose K falls in the range, [overview] section
  * 5.3, the second stage of the service case).  K is sampled at both ends and at the
  * doublings between them; each compiled kernel variant of the problem's path
- * (tile and wave grid, or the streaming path) is planned at every sample, and
+ * (tile, wave grid, K step and MFMA block, or the streaming path) is planned
+ * at every sample, and
  * the variant whose largest ratio of estimated time to the best plan of that K
- * is smallest wins (ties: fewer LDS bytes, then catalogue order).
- *   opts         as for dg_plan, with tile, waves and path left free
+ * is smallest wins (ties: fewer LDS bytes, then fewer registers, then
+ * catalogue order).
+ *   opts         as for dg_plan, with tile, K step, waves, MFMA block and
+ *                path left free
  *   range_opts   out: the options that pin the chosen variant; pass them to
  *                dg_gemm (or dg_plan) for any K of the range, where the planner
  *                still chooses the K split and schedule of that K
  *   out          nullable: the plan of the chosen variant at K_max
  *   worst_ratio  nullable: the chosen variant's largest estimated-time ratio
  * Errors: DG_ERR_INVALID_STATE, DG_ERR_INVALID_ARG (range_opts NULL, K_min < 0
- * or K_min > K_max), DG_ERR_CONFLICT (a forced tile, wave count or path), and
+ * or K_min > K_max), DG_ERR_CONFLICT (a forced tile, K step, wave count, MFMA
+ * block or path), and
  * what dg_plan returns at either end of the range (DG_ERR_ALIGNMENT for an
  * unaligned end without pad_k); DG_ERR_NO_CANDIDATE when no variant is valid
  * for every sample. */

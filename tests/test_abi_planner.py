@@ -332,7 +332,7 @@ def test_planner_uses_the_compiled_resource_usage(off):
     # compiler reported for each variant (no spills allowed at build time)
     rows = _resources()
     assert rows and all(r[-1] == 0 for r in rows)
-    tiled = {tuple(r[1:8]): r for r in rows if r[0] == 0}
+    tiled = {tuple(r[1:9]): r for r in rows if r[0] == 0}
     names = {"f16": 0, "bf16": 1, "i8": 2, "e2m1": 3}
     region_k = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32}
     for M, N, K, a, b, c, epi in PROBLEMS:
@@ -340,13 +340,17 @@ def test_planner_uses_the_compiled_resource_usage(off):
             if p.path != dg.DG_PATH_TILED:
                 continue
             nm = p.kernel_name.decode().split("_")
+            ms = 16 if nm[-1] == "m16" else 32
+            if ms == 16:
+                nm = nm[:-1]
             wm, wn = map(int, nm[-2][1:].split("x"))
             kr = int(nm[-1][1:]) // region_k[nm[1]]
             assert p.k_main == int(nm[-1][1:])
-            key = (names[nm[1]], 1 if nm[2] == "k" else 0, p.m_tile, p.n_tile, wm, wn, kr)
+            assert p.mfma_m == p.mfma_n == ms
+            key = (names[nm[1]], 1 if nm[2] == "k" else 0, p.m_tile, p.n_tile, wm, wn, kr, ms)
             r = tiled[key]
-            assert (p.vgpr_est, p.agpr_est, p.lds_bytes) == (r[8], r[9], r[10])
-            assert p.waves_per_simd == r[11]
+            assert (p.vgpr_est, p.agpr_est, p.lds_bytes) == (r[9], r[10], r[11])
+            assert p.waves_per_simd == r[12]
     # occupancy 2/8 keeps only variants the compiler gave >= 2 waves per SIMD
     o = dg.dg_plan_opts(force_m_tile=256, force_n_tile=256, target_occupancy=0.25)
     p = off.plan(2048, 2048, 2048, opts=o)
@@ -579,15 +583,17 @@ def _range_samples(K_min, K_max, unit):
 
 # the compiled tiled variants of the 16-bit and int8 paths: (M tile, N tile,
 # waves, K regions per step)
-TILED_VARIANTS = ((128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
-                  (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2))
+# (M tile, N tile, waves, K regions per step, MFMA block)
+TILED_VARIANTS = ((128, 256, 4, 1, 32), (256, 256, 8, 1, 32), (256, 128, 4, 1, 32), (128, 128, 4, 1, 32),
+                  (64, 64, 4, 1, 32), (256, 256, 4, 2, 32), (128, 256, 4, 2, 32), (256, 128, 4, 2, 32),
+                  (128, 128, 4, 2, 32), (64, 64, 4, 2, 32), (256, 256, 8, 1, 16))
 
 
 def _variants(off, path_b, bm_list=TILED_VARIANTS):
     region = 64 if path_b == "i8" else 32
     out = [dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=bm, force_n_tile=bn, force_waves=w,
-                           force_k_tile=region * kr)
-           for bm, bn, w, kr in bm_list]
+                           force_k_tile=region * kr, force_mfma=ms)
+           for bm, bn, w, kr, ms in bm_list]
     out.append(dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY))
     return out
 
@@ -605,12 +611,12 @@ def test_plan_range_minimises_the_worst_ratio(off, M, N, K_min, K_max, a, c):
     worst = {}
     for v in _variants(off, a):
         try:
-            worst[(v.force_path, v.force_m_tile, v.force_n_tile, v.force_waves, v.force_k_tile)] = max(
+            worst[(v.force_path, v.force_m_tile, v.force_n_tile, v.force_waves, v.force_k_tile, v.force_mfma)] = max(
                 off.plan(M, N, k, a, a, c, opts=v).est_us / b for k, b in zip(ks, best))
         except dg.DGError:
             pass
     ro, info, w = off.plan_range(M, N, K_min, K_max, a, a, c)
-    key = (ro.force_path, ro.force_m_tile, ro.force_n_tile, ro.force_waves, ro.force_k_tile)
+    key = (ro.force_path, ro.force_m_tile, ro.force_n_tile, ro.force_waves, ro.force_k_tile, ro.force_mfma)
     assert key in worst and abs(worst[key] - w) < 1e-9
     assert w <= min(worst.values()) + 1e-9 and w >= 1.0 - 1e-12
     # the pinned variant plans every K of the range (on the MFMA depth)

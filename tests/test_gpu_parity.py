@@ -333,14 +333,16 @@ def test_e2m1_odd_n(h, M, N, K, path):
     run(h, w, opts=dg.dg_plan_opts(force_path=path))
 
 
-# compiled tiled variants: (M tile, N tile, waves, K regions per step); the
-# double K step exists for the 16-bit and int8 paths
-TILED_VARIANTS = ((128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
-                  (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2))
+# compiled tiled variants: (M tile, N tile, waves, K regions per step, MFMA
+# block); the double K step and the 16x16 MFMAs exist for the 16-bit and int8
+# paths
+TILED_VARIANTS = ((128, 256, 4, 1, 32), (256, 256, 8, 1, 32), (256, 128, 4, 1, 32), (128, 128, 4, 1, 32),
+                  (64, 64, 4, 1, 32), (256, 256, 4, 2, 32), (128, 256, 4, 2, 32), (256, 128, 4, 2, 32),
+                  (128, 128, 4, 2, 32), (64, 64, 4, 2, 32), (256, 256, 8, 1, 16))
 
 
 def test_every_tiled_variant_on_a_ragged_problem(h):
-    # each compiled variant (tile shape, wave grid, K step), forced in turn, on a
+    # each compiled variant (tile shape, wave grid, K step, MFMA block), forced in turn, on a
     # problem with ragged M and N, a K tail and a K split: one K region per step
     # with K = 7 full steps + a half step (e2m1 K is whole 32-groups, so 8 full
     # steps), two regions per step with K = 3 full steps + a tail of one, two or
@@ -352,8 +354,8 @@ def test_every_tiled_variant_on_a_ragged_problem(h):
                              ("i8", "i8_4096x4096x4096", True),
                              ("e2m1", "e2m1_4096x4096x4096", True)):
         region = 64 if path == "i8" else 32
-        for bm, bn, nw, kr in TILED_VARIANTS:
-            if kr > 1 and path == "e2m1":
+        for bm, bn, nw, kr, ms in TILED_VARIANTS:
+            if (kr > 1 or ms == 16) and path == "e2m1":
                 continue
             if kr == 1:
                 ks = [8 * 32] if path == "e2m1" else [7 * region + region // 2]
@@ -363,9 +365,10 @@ def test_every_tiled_variant_on_a_ragged_problem(h):
                 w = synth.make(name, M=290, N=272, K=K)
                 for s in (1, 2):
                     o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_split_k=s,
-                                        force_path=dg.DG_PATH_TILED, force_waves=nw, force_k_tile=region * kr)
+                                        force_path=dg.DG_PATH_TILED, force_waves=nw, force_k_tile=region * kr,
+                                        force_mfma=ms)
                     info, _ = run(h, w, b_colmajor=colm, opts=o)
-                    assert info.k_main == region * kr and info.waves_per_wg == nw
+                    assert info.k_main == region * kr and info.waves_per_wg == nw and info.mfma_m == ms
 
 
 def test_split_k_and_schedule_tail(h):
@@ -566,3 +569,15 @@ def test_full_size_every_output(h, name, col_chunk):
     w = synth.make(name, device=DEV)
     info, st = run(h, w, col_chunk=col_chunk)
     assert st["n"] == w.M * w.N
+
+
+@pytest.mark.parametrize("name,ms", [("i8_4096x4096x4096", 16), ("i8_4096x4096x4096", 32),
+                                     ("f16_4096x4096x4096", 16), ("f16_4096x4096x4096", 32)])
+def test_full_size_each_mfma_block(h, name, ms):
+    # the 4096^3 workloads with the eight-wave 256x256 tile on each MFMA block
+    # (32x32 and 16x16), every output against the oracle
+    w = synth.make(name, device=DEV)
+    o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=256, force_n_tile=256, force_waves=8,
+                        force_mfma=ms)
+    info, st = run(h, w, opts=o)
+    assert st["n"] == w.M * w.N and info.mfma_m == ms

@@ -53,17 +53,19 @@ def test_calibration_of_one_path(h, tmp_path):  # noqa: F811
     desc = dict(d["desc"], mfma_tflops_f16=d["measured"]["mfma_tflops_f16"],
                 launch_us=d["measured"]["launch_us"])
     eff, round_us, us = probe.calibrate(h, desc, "cuda:0", reps=10, rounds=1, paths=("i8",))
-    assert len(eff) == 20 and all(0 < e <= 1.5 for e in eff.values())
+    assert len(eff) == 22 and all(0 < e <= 1.5 for e in eff.values())
     assert set(round_us) == set(eff) and all(r >= 0 for r in round_us.values())
     d2 = dict(d, tiled_efficiency=eff, tiled_round_us=round_us)
     (tmp_path / "cal.json").write_text(json.dumps(d2))
     off = dg.Handle(offline=dg.default_device_desc())
     off.load_device_json(str(tmp_path / "cal.json"))
     for nm in eff:
-        _, lay, mn, w, k = nm.split("_")[1:]
+        parts = nm.split("_")[1:]
+        ms = 16 if parts[-1] == "m16" else 32
+        _, lay, mn, w, k = parts[:5]
         bm, bn = map(int, mn.split("x"))
         o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=2 * int(w[-1]) if w == "w2x4" else 4,
-                            force_k_tile=int(k[1:]), force_split_k=1, force_path=dg.DG_PATH_TILED)
+                            force_k_tile=int(k[1:]), force_split_k=1, force_path=dg.DG_PATH_TILED, force_mfma=ms)
         p = off.plan(4096, 4096, 4096, "i8", "i8", "i32", dg.DG_COL_MAJOR if lay == "k" else dg.DG_ROW_MAJOR,
                      opts=o)
         assert p.kernel_name.decode() == nm

@@ -69,7 +69,7 @@ def _parse_resources(remarks):
                 cur = None
                 continue
             args = [int(x) for x in re.findall(r"Li(-?\d+)E", name)]
-            cur = (fam, tuple(args + [0] * (7 - len(args))))
+            cur = (fam, tuple(args + [0] * (8 - len(args))))
             rows[cur] = {}
             continue
         if cur is None:
@@ -128,7 +128,7 @@ def _check_transposing_reads(src):
 def _write_resources(rows):
     lines = ["// resources.inc - registers, LDS and occupancy of every compiled kernel variant,",
              "// extracted from the compiler's kernel-resource-usage remarks by build.py.",
-             "// {family, template args (7, zero-padded), VGPRs, AGPRs, LDS bytes, waves/SIMD, spills}"]
+             "// {family, template args (8, zero-padded), VGPRs, AGPRs, LDS bytes, waves/SIMD, spills}"]
     for (fam, args), r in sorted(rows.items()):
         lines.append("{%d, %s, %d, %d, %d, %d, %d}," % (
             fam, ", ".join(str(a) for a in args), r.get("vgpr", 0), r.get("agpr", 0),

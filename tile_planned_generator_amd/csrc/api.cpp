@@ -166,12 +166,12 @@ dg_plan_opts opts_or_default(const dg_plan_opts *o)
 std::string cache_key(const Problem &p, const dg_plan_opts &o)
 {
     char k[256];
-    std::snprintf(k, sizeof k, "%lld,%lld,%lld+%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d",
+    std::snprintf(k, sizeof k, "%lld,%lld,%lld+%lld,%lld,%d,%d,%d,%d,%d|%d,%d,%d,%d,%d,%d,%d,%.4f,%d,%d,%d",
                   (long long)p.M, (long long)p.N, (long long)p.K, (long long)p.k_pad, (long long)p.ws_limit,
                   p.path, p.b_kmajor,
                   p.out_type, p.epi,
                   p.beta_nz, o.force_m_tile, o.force_n_tile, o.force_k_tile, o.force_split_k, o.force_path,
-                  o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k, o.force_waves);
+                  o.unit, o.lds_limit_bytes, o.target_occupancy, o.pad_k, o.force_waves, o.force_mfma);
     return k;
 }
 
@@ -198,7 +198,7 @@ dg_status plan_cached(dg_handle_t h, const Problem &pr, const dg_plan_opts &o, C
     if (o.force_path < DG_PATH_AUTO || o.force_path > DG_PATH_SKINNY)
         return fail(DG_ERR_INVALID_ARG, "unknown path");
     if (o.force_split_k < 0 || o.force_m_tile < 0 || o.force_n_tile < 0 || o.force_k_tile < 0 ||
-        o.force_waves < 0 ||
+        o.force_waves < 0 || (o.force_mfma != 0 && o.force_mfma != 16 && o.force_mfma != 32) ||
         o.lds_limit_bytes < 0 || o.target_occupancy > 1.0f)
         return fail(DG_ERR_INVALID_ARG, "invalid planner option");
     const std::string key = cache_key(pr, o);
@@ -648,8 +648,8 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
         if (!range_opts) return fail(DG_ERR_INVALID_ARG, "range_opts is NULL");
         if (K_min < 0 || K_max < K_min) return fail(DG_ERR_INVALID_ARG, "K range must satisfy 0 <= K_min <= K_max");
         const dg_plan_opts o = opts_or_default(opts);
-        if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves || o.force_path)
-            return fail(DG_ERR_CONFLICT, "a K range plan chooses the variant: leave tile, K step, waves and path free");
+        if (o.force_m_tile || o.force_n_tile || o.force_k_tile || o.force_waves || o.force_mfma || o.force_path)
+            return fail(DG_ERR_CONFLICT, "a K range plan chooses the variant: leave tile, K step, waves, MFMA block and path free");
         // every K of the range must be a valid problem; both ends decide that
         // (alignment and leading dimensions only tighten as K grows or shrinks)
         Problem lo, hi;
@@ -677,11 +677,11 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
         struct Var {
             dg_plan_opts opt;
             double worst;
-            int lds;
+            int lds, regs;
         };
         std::vector<Var> vars;
         const TiledShape shapes[] = {
-#define DG_TS(path, kmaj, bm, bn, wm, wn, kr) {path, kmaj, bm, bn, wm, wn, kr},
+#define DG_TS(path, kmaj, bm, bn, wm, wn, kr, ms) {path, kmaj, bm, bn, wm, wn, kr, ms},
             DG_TILED_CATALOGUE(DG_TS)
 #undef DG_TS
         };
@@ -693,6 +693,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
             v.force_m_tile = t.bm;
             v.force_n_tile = t.bn;
             v.force_waves = t.wm * t.wn;
+            v.force_mfma = t.ms;
             v.force_k_tile = tiled_bk_elems(t.path) * t.kr;
             tries.push_back(v);
         }
@@ -703,7 +704,7 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
         }
         for (const dg_plan_opts &v : tries) {
             double worst = 0;
-            int lds = 0;
+            int lds = 0, regs = 0;
             bool ok = true;
             for (size_t i = 0; i < ks.size() && ok; ++i) {
                 Problem pr;
@@ -716,16 +717,19 @@ dg_status dg_plan_range(dg_handle_t h, int64_t M, int64_t N, int64_t K_min, int6
                 }
                 worst = std::max(worst, r.pareto.front().est_us / std::max(best[i], 1e-9));
                 lds = std::max(lds, r.pareto.front().lds);
+                regs = std::max(regs, r.pareto.front().vgpr + r.pareto.front().agpr);
             }
-            if (ok) vars.push_back(Var{v, worst, lds});
+            if (ok) vars.push_back(Var{v, worst, lds, regs});
         }
         if (vars.empty()) return fail(DG_ERR_NO_CANDIDATE, "No valid candidate found after pruning for every K of the range");
         // the smallest worst-case ratio to the best plan of each K; then fewer
-        // LDS bytes; then catalogue order (deterministic)
+        // LDS bytes; then fewer registers; then catalogue order (deterministic)
         size_t bi = 0;
         for (size_t i = 1; i < vars.size(); ++i) {
             const Var &a = vars[i], &b = vars[bi];
-            if (a.worst < b.worst - 1e-12 || (std::abs(a.worst - b.worst) <= 1e-12 && a.lds < b.lds)) bi = i;
+            const bool tie = std::abs(a.worst - b.worst) <= 1e-12;
+            if (a.worst < b.worst - 1e-12 || (tie && a.lds < b.lds) || (tie && a.lds == b.lds && a.regs < b.regs))
+                bi = i;
         }
         *range_opts = vars[bi].opt;
         if (worst_ratio) *worst_ratio = vars[bi].worst;

@@ -4,31 +4,36 @@
 // the kernel sources, which instantiate exactly these variants.  The pages'
 // planner searches tile shape x layout x granularity ([overview] DeepGEMM
 // article, section 4.1, stage 2); on gfx950 the tile shapes are multiples of
-// the 32x32 MFMA output block and the granularity is the wave grid.
+// the 32x32 MFMA output block, the granularity is the wave grid, and the MFMA
+// block (32x32 or 16x16) is one more dimension.
 #pragma once
 
 namespace dg {
 
-// Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN, KR)
+// Tiled MFMA GEMM: X(path, b_kmajor, BM, BN, WM, WN, KR, MS)
 //   path      P_F16 / P_BF16 / P_I8 / P_E2M1 / P_MX
 //   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
 //   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
 //   KR        64-byte K regions per K step: the K step (K_tile) is KR x 32 k
+//             (16-bit), KR x 64 k (int8)
+//   MS        MFMA output block: 32 (32x32) or 16 (16x16)
 //             for 16-bit operands and KR x 64 k for int8 (e2m1 and MX: KR = 1)
 #define DG_TILE_SHAPES(X, path, kmaj)  \
-    X(path, kmaj, 128, 256, 2, 2, 1)   \
-    X(path, kmaj, 256, 256, 2, 4, 1)   \
-    X(path, kmaj, 256, 128, 2, 2, 1)   \
-    X(path, kmaj, 128, 128, 2, 2, 1)   \
-    X(path, kmaj, 64, 64, 2, 2, 1)
+    X(path, kmaj, 128, 256, 2, 2, 1, 32)   \
+    X(path, kmaj, 256, 256, 2, 4, 1, 32)   \
+    X(path, kmaj, 256, 128, 2, 2, 1, 32)   \
+    X(path, kmaj, 128, 128, 2, 2, 1, 32)   \
+    X(path, kmaj, 64, 64, 2, 2, 1, 32)
 // The double K step (two regions per LDS stage, four MFMA substeps per
 // barrier), four-wave tiles only.
 #define DG_TILE_SHAPES_K2(X, path, kmaj) \
-    X(path, kmaj, 256, 256, 2, 2, 2)     \
-    X(path, kmaj, 128, 256, 2, 2, 2)     \
-    X(path, kmaj, 256, 128, 2, 2, 2)     \
-    X(path, kmaj, 128, 128, 2, 2, 2)     \
-    X(path, kmaj, 64, 64, 2, 2, 2)
+    X(path, kmaj, 256, 256, 2, 2, 2, 32)     \
+    X(path, kmaj, 128, 256, 2, 2, 2, 32)     \
+    X(path, kmaj, 256, 128, 2, 2, 2, 32)     \
+    X(path, kmaj, 128, 128, 2, 2, 2, 32)     \
+    X(path, kmaj, 64, 64, 2, 2, 2, 32)
+// 16x16 MFMAs (one per 64-byte K region and 16x16 block), the eight-wave tile.
+#define DG_TILE_SHAPES_M16(X, path, kmaj) X(path, kmaj, 256, 256, 2, 4, 1, 16)
 
 #define DG_TILED_CATALOGUE(X)          \
     DG_TILE_SHAPES(X, P_F16, 0)        \
@@ -44,7 +49,13 @@ namespace dg {
     DG_TILE_SHAPES_K2(X, P_BF16, 0)    \
     DG_TILE_SHAPES_K2(X, P_BF16, 1)    \
     DG_TILE_SHAPES_K2(X, P_I8, 0)      \
-    DG_TILE_SHAPES_K2(X, P_I8, 1)
+    DG_TILE_SHAPES_K2(X, P_I8, 1)      \
+    DG_TILE_SHAPES_M16(X, P_F16, 0)    \
+    DG_TILE_SHAPES_M16(X, P_F16, 1)    \
+    DG_TILE_SHAPES_M16(X, P_BF16, 0)   \
+    DG_TILE_SHAPES_M16(X, P_BF16, 1)   \
+    DG_TILE_SHAPES_M16(X, P_I8, 0)     \
+    DG_TILE_SHAPES_M16(X, P_I8, 1)
 
 // Skinny VALU streaming GEMM over a row-major 16-bit B:
 // X(path, MR, LPR): up to MR rows of A; LPR lanes span one row of B (8 columns each).
@@ -67,7 +78,7 @@ namespace dg {
 
 // Resource facts of the variants, used by the planner's constraints.
 struct TiledShape {
-    int path, b_kmajor, bm, bn, wm, wn, kr;
+    int path, b_kmajor, bm, bn, wm, wn, kr, ms;   // ms: MFMA block edge (32 or 16)
 };
 
 // Fewest direct-to-LDS loads any wave issues per stage when load i of an

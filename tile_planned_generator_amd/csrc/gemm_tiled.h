@@ -138,7 +138,7 @@ DG_DEV void static_for(F &&f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int PATH, int BKMAJ, int BM, int BN, int WM, int WN, int KR>
+template <int PATH, int BKMAJ, int BM, int BN, int WM, int WN, int KR, int MS = 32>
 __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 {
     constexpr int NW = WM * WN;
@@ -155,6 +155,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     static_assert(BKE == 2 * KSUB, "two substeps per region");
     static_assert(KR == 1 || PATH == P_F16 || PATH == P_BF16 || PATH == P_I8, "double K steps: 16-bit and int8");
     static_assert(KR == 1 || KR == 2, "one or two K regions per step");
+    // MFMA block: 32x32 (two MFMAs of KSUB k per region and block) or 16x16
+    // (one MFMA per 64-byte region and 16x16 block: v_mfma_i32_16x16x64_i8,
+    // v_mfma_f32_16x16x32_f16/_bf16).  The 16x16 MFMAs do the same work per
+    // clock and, on random operands, hold a higher clock under the power limit.
+    constexpr bool M16 = MS == 16;
+    static_assert(MS == 32 || MS == 16, "MFMA block size");
+    static_assert(!M16 || ((PATH == P_F16 || PATH == P_BF16 || PATH == P_I8) && WM * WN == 8 && KR == 1),
+                  "16x16 MFMAs: 16-bit and int8 operands, the eight-wave loop");
     constexpr int BKS = KR * BKE;                      // k elements per K step
     constexpr int NSUB = 2 * KR;                       // MFMA substeps per K step
     constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN, KR);
@@ -362,14 +370,21 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             if (part < 0 || (part == 0) == (i < A_LD)) load_one(j, i);
     };
 
-    using AccT = typename std::conditional<IS_I8, intx16, floatx16>::type;
-    AccT acc[FM][FN];
+    // Accumulators: per 32x32 block of the wave tile one 16-register tile, or
+    // (16x16 MFMAs) four 4-register tiles, q = 2 * (row half) + (column half).
+    using Acc32 = typename std::conditional<IS_I8, intx16, floatx16>::type;
+    using Acc16 = typename std::conditional<IS_I8, intx4, floatx4>::type;
+    using AccT = typename std::conditional<M16, Acc16, Acc32>::type;
+    constexpr int NQ = M16 ? 4 : 1, NV = M16 ? 4 : 16;
+    AccT acc[FM][FN][NQ];
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0;
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[mi][ni][q][v] = 0;
 
     // fragments of one k-substep: FM A blocks and FN B blocks (16 bytes per lane
     // each; MX: 32 bytes of fp8 A per lane, and the lane's scale bytes of its A
@@ -391,23 +406,30 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     //   The two reads of a block cover K rows kb.. and kb+4.. (b16) / kb+8.. (b8);
     //   row k and k + 4 (k + 8) share their swizzle, as do substeps 0 and 1, so
     //   those reads differ by immediate offsets.
+    //   16x16 MFMAs: A / K-major B row `row` (16 rows per block half), chunk
+    //   lane >> 4 (the MFMA takes a whole 64-byte region); row-major B: lane L of
+    //   group g supplies K row 8g + (L >> 2) at column 16 sn + 4 (L & 3) (b16), or
+    //   16g + (L >> 1) at column 16 sn + 8 (L & 1) (b8), sn the column half.
     const int grp16 = lane >> 4, L16 = lane & 15;
-    uint32_t boff[FN];
+    uint32_t boff[FN * (M16 ? 2 : 1)];
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
-        const int col0 = wn * WTN + ni * 32;
-        if constexpr (B_TR) {
-            if constexpr (!IS_I8) {
-                const int col = col0 + 16 * (grp16 & 1) + 4 * (L16 & 3);
-                const int k = 8 * (grp16 >> 1) + (L16 >> 2);
-                boff[ni] = A_ALL + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
-            } else {
-                const int col = col0 + 16 * (grp16 & 1) + 8 * (L16 & 1);
-                const int k = 16 * (grp16 >> 1) + (L16 >> 1);
-                boff[ni] = A_ALL + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
+#pragma unroll
+        for (int sn = 0; sn < (M16 ? 2 : 1); ++sn) {
+            const int col0 = wn * WTN + ni * 32 + 16 * sn;
+            uint32_t o = 0;
+            if constexpr (B_TR) {
+                if constexpr (!IS_I8) {
+                    const int col = col0 + (M16 ? 0 : 16 * (grp16 & 1)) + 4 * (L16 & 3);
+                    const int k = (M16 ? 8 * grp16 : 8 * (grp16 >> 1)) + (L16 >> 2);
+                    o = A_ALL + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
+                } else {
+                    const int col = col0 + (M16 ? 0 : 16 * (grp16 & 1)) + 8 * (L16 & 1);
+                    const int k = (M16 ? 16 * grp16 : 16 * (grp16 >> 1)) + (L16 >> 1);
+                    o = A_ALL + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
+                }
             }
-        } else {
-            boff[ni] = 0;
+            boff[ni * (M16 ? 2 : 1) + sn] = o;
         }
     }
 
@@ -433,6 +455,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
+        } else if constexpr (M16) {
+            // s is the block's row half; the lane reads chunk lane >> 4
+            const int r16 = wm * WTM + mi * 32 + 16 * s + L16;
+            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ ((r16 >> 2) & 3)) << 4));
         } else {
             f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + (s >> 1) * A_BYTES + row * 64 +
                                                         ((c ^ ((row >> 2) & 3)) << 4));
@@ -462,6 +488,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             } else {
                 f.b[ni] = u32x4{e2_next[ni], e2_sh[ni], 0u, 0u};
             }
+        } else if constexpr (BKMAJ && M16) {
+            // s is the block's column half; the lane reads chunk lane >> 4
+            const int row = col0 + 16 * s + L16;
+            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
         } else if constexpr (BKMAJ) {
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
@@ -470,14 +500,17 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             if constexpr (IS_MX)
                 f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
         } else {
-            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[ni];
+            // (16x16: s is the block's column half, its own lane offsets; the
+            // region's K rows start at 0)
+            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[M16 ? 2 * ni + s : ni];
+            constexpr int KO = M16 ? 0 : KSUB * s * RB;
             u32x2 lo, hi;
             if constexpr (!IS_I8) {
-                lo = lds_tr16<KSUB * s * RB>(a);
-                hi = lds_tr16<KSUB * s * RB + 4 * RB>(a);
+                lo = lds_tr16<KO>(a);
+                hi = lds_tr16<KO + 4 * RB>(a);
             } else {
-                lo = lds_tr8<KSUB * s * RB>(a);
-                hi = lds_tr8<KSUB * s * RB + 8 * RB>(a);
+                lo = lds_tr8<KO>(a);
+                hi = lds_tr8<KO + 8 * RB>(a);
             }
             f.b[ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
@@ -517,27 +550,57 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // the transposed product: lane l holds row lr of the block and, in registers
     // 4j .. 4j+3, its columns 8j + 4kg .. 8j + 4kg + 3.
     auto mfma1 = [&](const Frag &f, int mi, int ni) {
-        if constexpr (PATH == P_F16 || PATH == P_E2M1)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(half8, f.b[ni]), __builtin_bit_cast(half8, f.a[mi]), acc[mi][ni], 0, 0, 0);
+        if constexpr (M16)
+            return;   // (16x16 tiles go through mfmas16)
+        else if constexpr (PATH == P_F16 || PATH == P_E2M1)
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8, f.b[ni]), __builtin_bit_cast(half8, f.a[mi]), acc[mi][ni][0], 0, 0, 0);
         else if constexpr (PATH == P_BF16)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, f.b[ni]), __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, f.b[ni]), __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni][0], 0, 0, 0);
         else if constexpr (IS_MX)
             // first operand e2m1 (format 4, four registers used), second fp8 e4m3
             // (format 0); each scale is the low byte of its register
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 __builtin_bit_cast(intx8, u32x8{f.b[ni].x, f.b[ni].y, f.b[ni].z, f.b[ni].w, 0u, 0u, 0u, 0u}),
-                __builtin_bit_cast(intx8, f.a[mi]), acc[mi][ni], 4, 0, 0, (int)f.sb[ni], 0, (int)f.sa[mi]);
+                __builtin_bit_cast(intx8, f.a[mi]), acc[mi][ni][0], 4, 0, 0, (int)f.sb[ni], 0, (int)f.sa[mi]);
         else
-            acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                __builtin_bit_cast(intx4, f.b[ni]), __builtin_bit_cast(intx4, f.a[mi]), acc[mi][ni], 0, 0, 0);
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                __builtin_bit_cast(intx4, f.b[ni]), __builtin_bit_cast(intx4, f.a[mi]), acc[mi][ni][0], 0, 0, 0);
     };
     auto mfmas = [&](const Frag &f) {
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni) mfma1(f, mi, ni);
+    };
+    // 16x16 MFMAs of one region: fa / fb hold the row / column halves of the
+    // blocks (f0 the first, f1 the second); B goes in first as above, so lane l
+    // of a 16x16 tile holds row l & 15 and columns 4 (l >> 4) .. +3.
+    auto mfmas16 = [&](const Frag &h0, const Frag &h1) {
+        if constexpr (M16) {
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+            for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+                for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                    for (int sn = 0; sn < 2; ++sn) {
+                        const u32x4 a = sm ? h1.a[mi] : h0.a[mi];
+                        const u32x4 b = sn ? h1.b[ni] : h0.b[ni];
+                        AccT &c = acc[mi][ni][2 * sm + sn];
+                        if constexpr (PATH == P_F16)
+                            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b),
+                                                                       __builtin_bit_cast(half8, a), c, 0, 0, 0);
+                        else if constexpr (PATH == P_BF16)
+                            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                                        __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+                        else if constexpr (IS_I8)
+                            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(intx4, b),
+                                                                      __builtin_bit_cast(intx4, a), c, 0, 0, 0);
+                    }
+        }
     };
     // A final half step runs its second substep on zeroed fragments (0 x 0 adds
     // nothing): the fragments are ANDed with a uniform mask, so the loop body has
@@ -614,15 +677,29 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
             tie(f0);
             tie(f1);
-            if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
+            if constexpr (LAST) {
+                if constexpr (M16) {
+                    // a final half step: the lanes holding k past its first half
+                    // (chunks 2 and 3) contribute 0 x 0
+                    const bool keep = nfull == nsteps || grp16 < 2;
+                    keep_if(f0, keep);
+                    keep_if(f1, keep);
+                } else {
+                    keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
+                }
+            }
             bar();
             // compute phase, at raised wave priority so that the SIMD's other
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
-            decode_b(f0);
-            mfmas(f0);
-            decode_b(f1);
-            mfmas(f1);
+            if constexpr (M16) {
+                mfmas16(f0, f1);
+            } else {
+                decode_b(f0);
+                mfmas(f0);
+                decode_b(f1);
+                mfmas(f1);
+            }
             __builtin_amdgcn_s_setprio(0);
             bar();
         };
@@ -752,12 +829,22 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         for (int m = 0; m < FM; ++m) {
             if (m == mi) {
 #pragma unroll
-                for (int ni = 0; ni < FN; ++ni)
+                for (int ni = 0; ni < FN; ++ni) {
+                    if constexpr (M16) {
+                        // 16x16 tile q: row 16 (q >> 1) + (lane & 15), columns
+                        // 16 (q & 1) + 4 (lane >> 4) .. +3
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        *reinterpret_cast<Vec4 *>(sE + lr * RP + ni * 32 + 8 * j + 4 * kg) =
-                            Vec4{acc[m][ni][4 * j], acc[m][ni][4 * j + 1], acc[m][ni][4 * j + 2],
-                                 acc[m][ni][4 * j + 3]};
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<Vec4 *>(sE + (16 * (q >> 1) + L16) * RP + ni * 32 + 16 * (q & 1) +
+                                                      4 * grp16) = acc[m][ni][q];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<Vec4 *>(sE + lr * RP + ni * 32 + 8 * j + 4 * kg) =
+                                Vec4{acc[m][ni][0][4 * j], acc[m][ni][0][4 * j + 1], acc[m][ni][0][4 * j + 2],
+                                     acc[m][ni][0][4 * j + 3]};
+                    }
+                }
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -14,7 +14,7 @@ void *tiled_kernel_ptr_e2m1(int id);
 void *tiled_kernel_ptr_mx(int id);
 
 static const TiledShape k_shapes[] = {
-#define DG_TS(path, kmaj, bm, bn, wm, wn, kr) {path, kmaj, bm, bn, wm, wn, kr},
+#define DG_TS(path, kmaj, bm, bn, wm, wn, kr, ms) {path, kmaj, bm, bn, wm, wn, kr, ms},
     DG_TILED_CATALOGUE(DG_TS)
 #undef DG_TS
 };

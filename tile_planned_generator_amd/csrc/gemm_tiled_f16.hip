@@ -3,16 +3,16 @@
 
 namespace dg {
 
-template <int PATH, int KMAJ, int BM, int BN, int WM, int WN, int KR>
+template <int PATH, int KMAJ, int BM, int BN, int WM, int WN, int KR, int MS>
 static void *pick_f16()
 {
     if constexpr (PATH == P_F16)
-        return reinterpret_cast<void *>(gemm_tiled_kernel<PATH, KMAJ, BM, BN, WM, WN, KR>);
+        return reinterpret_cast<void *>(gemm_tiled_kernel<PATH, KMAJ, BM, BN, WM, WN, KR, MS>);
     else
         return nullptr;
 }
 
-#define DG_PICK(path, kmaj, bm, bn, wm, wn, kr) pick_f16<path, kmaj, bm, bn, wm, wn, kr>(),
+#define DG_PICK(path, kmaj, bm, bn, wm, wn, kr, ms) pick_f16<path, kmaj, bm, bn, wm, wn, kr, ms>(),
 
 // Kernel of catalogue entry id if it belongs to this path, else NULL.
 void *tiled_kernel_ptr_f16(int id)

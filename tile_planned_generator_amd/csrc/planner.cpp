@@ -44,7 +44,7 @@ constexpr int SKINNY_A_LDS = 32768;   // must match skinny.hip
 constexpr int E2M1_A_LDS = 32768;     // must match skinny.hip
 
 const TiledShape k_tiled_shapes[] = {
-#define DG_TS(path, kmaj, bm, bn, wm, wn, kr) {path, kmaj, bm, bn, wm, wn, kr},
+#define DG_TS(path, kmaj, bm, bn, wm, wn, kr, ms) {path, kmaj, bm, bn, wm, wn, kr, ms},
     DG_TILED_CATALOGUE(DG_TS)
 #undef DG_TS
 };
@@ -71,18 +71,18 @@ const int k_e2m1_mr[] = {
 // Registers, LDS and occupancy of the compiled variants, as the compiler
 // reported them when the library was built.
 struct ResRow {
-    int fam, a0, a1, a2, a3, a4, a5, a6, vgpr, agpr, lds, occ, spill;
+    int fam, a0, a1, a2, a3, a4, a5, a6, a7, vgpr, agpr, lds, occ, spill;
 };
 const ResRow k_res[] = {
 #include "resources.inc"
 };
 
 const ResRow *find_res(int fam, int a0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0,
-                       int a6 = 0)
+                       int a6 = 0, int a7 = 0)
 {
     for (const ResRow &r : k_res)
         if (r.fam == fam && r.a0 == a0 && r.a1 == a1 && r.a2 == a2 && r.a3 == a3 && r.a4 == a4 &&
-            r.a5 == a5 && r.a6 == a6)
+            r.a5 == a5 && r.a6 == a6 && r.a7 == a7)
             return &r;
     return nullptr;
 }
@@ -268,7 +268,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
         if (acc + other <= 256) { vgpr = acc + other; agpr = 0; }
         else { vgpr = other; agpr = acc; }
         int lds = tiled_lds_bytes(s.path, s.bm, s.bn, s.wm, s.wn, s.kr);
-        if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn, s.kr)) {
+        if (const ResRow *r = find_res(F_TILED, s.path, s.b_kmajor, s.bm, s.bn, s.wm, s.wn, s.kr, s.ms)) {
             vgpr = r->vgpr;
             agpr = r->agpr;
             lds = r->lds;
@@ -293,6 +293,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             else if (o.force_n_tile && o.force_n_tile != s.bn) why = "forced N tile";
             else if (o.force_k_tile && o.force_k_tile != BKE) why = "forced K tile";
             else if (o.force_waves && o.force_waves != waves) why = "forced wave count";
+            else if (o.force_mfma && o.force_mfma != s.ms) why = "forced MFMA block";
             else if (S_eff != S && !o.force_split_k) why = "split collapses";
             else if (over_ws_limit(pr, S_eff, o)) {
                 why = "workspace over the limit";
@@ -309,7 +310,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             c.family = F_TILED;
             c.kernel_id = id;
             c.unit = DG_UNIT_MFMA;
-            c.mfma_m = 32; c.mfma_n = 32; c.mfma_k = KSUB;
+            c.mfma_m = s.ms; c.mfma_n = s.ms; c.mfma_k = s.ms == 16 ? 2 * KSUB : KSUB;
             c.m_tile = s.bm; c.n_tile = s.bn; c.waves = waves;
             c.split_k = S_eff; c.k_slice = k_slice;
             schedule(k_slice, BKE, c.k_main, c.n_main, c.k_tail, c.n_tail);
@@ -329,8 +330,8 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
             // the published rate times the built-in fraction (catalogue.h).  The
             // LDS and L2 terms only matter for variants that are not MFMA-bound.
             char nm[64];
-            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d", path_name(pr.path),
-                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE);
+            std::snprintf(nm, sizeof nm, "tiled_%s_%s_%dx%d_w%dx%d_k%d%s", path_name(pr.path),
+                          pr.b_kmajor ? "k" : "n", s.bm, s.bn, s.wm, s.wn, BKE, s.ms == 16 ? "_m16" : "");
             const double step_ops = 2.0 * s.bm * s.bn * BKE;
             double t_mfma, round_us = -1;
             const auto hit = eff ? eff->eff.find(nm) : std::unordered_map<std::string, double>::const_iterator();
@@ -387,7 +388,7 @@ static void enum_tiled(const Problem &pr, const dg_device_desc &d, const dg_plan
 static void enum_skinny(const Problem &pr, const dg_device_desc &d, const dg_plan_opts &o,
                         std::vector<Candidate> &out, int &enumerated, int &pruned, int &ws_pruned)
 {
-    if (o.force_m_tile || o.force_k_tile || o.force_waves) return;  // tiled-only options
+    if (o.force_m_tile || o.force_k_tile || o.force_waves || o.force_mfma) return;  // tiled-only options
     // force_n_tile picks the streaming kernels' columns per workgroup
     auto n_ok = [&](int n_tile) { return o.force_n_tile == 0 || o.force_n_tile == n_tile; };
     const int lds_cap = std::min(d.lds_bytes_per_wg, o.lds_limit_bytes > 0 ? o.lds_limit_bytes : 1 << 30);
@@ -615,9 +616,9 @@ PlanResult plan_problem(const Problem &pr, const dg_device_desc &d, const dg_pla
         res.message = "conflicting compute units: the tiled path runs on MFMA, VALU was requested";
         return res;
     }
-    if (o.force_path == DG_PATH_SKINNY && (o.force_m_tile || o.force_k_tile || o.force_waves)) {
+    if (o.force_path == DG_PATH_SKINNY && (o.force_m_tile || o.force_k_tile || o.force_waves || o.force_mfma)) {
         res.status = DG_ERR_CONFLICT;
-        res.message = "forced M tile, K step and waves apply to the tiled path, the skinny path was forced";
+        res.message = "forced M tile, K step, waves and MFMA block apply to the tiled path, the skinny path was forced";
         return res;
     }
     if (want_tiled) enum_tiled(pr, d, o, eff, all, res.enumerated, res.pruned, res.ws_pruned);

@@ -50,7 +50,7 @@ class dg_plan_opts(C.Structure):
                 ("force_k_tile", C.c_int32), ("force_split_k", C.c_int32),
                 ("force_path", C.c_int32), ("unit", C.c_int32), ("lds_limit_bytes", C.c_int32),
                 ("target_occupancy", C.c_float), ("pad_k", C.c_int32),
-                ("force_waves", C.c_int32)]
+                ("force_waves", C.c_int32), ("force_mfma", C.c_int32)]
 
     def __init__(self, **kw):
         super().__init__()

@@ -59,11 +59,12 @@ MEASURED_DESC = ("hbm_gbps", "mfma_tflops_f16", "launch_us", "lds_conflict_strid
 
 # tiled variants of every path: (M tile, N tile, waves, K regions per step)
 VARIANTS = {
-    "f16": [(128, 256, 4, 1), (256, 256, 8, 1), (256, 128, 4, 1), (128, 128, 4, 1), (64, 64, 4, 1),
-            (256, 256, 4, 2), (128, 256, 4, 2), (256, 128, 4, 2), (128, 128, 4, 2), (64, 64, 4, 2)],
+    "f16": [(128, 256, 4, 1, 32), (256, 256, 8, 1, 32), (256, 128, 4, 1, 32), (128, 128, 4, 1, 32),
+            (64, 64, 4, 1, 32), (256, 256, 4, 2, 32), (128, 256, 4, 2, 32), (256, 128, 4, 2, 32),
+            (128, 128, 4, 2, 32), (64, 64, 4, 2, 32), (256, 256, 8, 1, 16)],
 }
 VARIANTS["bf16"] = VARIANTS["i8"] = VARIANTS["f16"]
-VARIANTS["e2m1"] = VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1]
+VARIANTS["e2m1"] = VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1 and v[4] == 32]
 REGION_K = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32, "mx": 128}
 
 
@@ -196,9 +197,10 @@ def calibrate(h, desc, dev, reps=40, rounds=3, paths=None, ks=(4096, 1024)):
             w, make, osz = _operands(name, dev, copies=copies, M=4096, N=4096, K=K)
             for kmaj in layouts:
                 calls = []
-                for bm, bn, nw, kr in VARIANTS[path]:
+                for bm, bn, nw, kr, ms in VARIANTS[path]:
                     o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=nw, force_split_k=1,
-                                        force_k_tile=REGION_K[path] * kr, force_path=dg.DG_PATH_TILED)
+                                        force_k_tile=REGION_K[path] * kr, force_path=dg.DG_PATH_TILED,
+                                        force_mfma=ms)
                     try:
                         calls.append(make(h, o, kmaj))
                     except dg.DGError:
