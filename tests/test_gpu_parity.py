@@ -334,8 +334,8 @@ def test_e2m1_odd_n(h, M, N, K, path):
 
 
 # compiled tiled variants: (M tile, N tile, waves, K regions per step, MFMA
-# block); the double K step and the 16x16 MFMAs exist for the 16-bit and int8
-# paths
+# block); the double K step exists for the 16-bit and int8 paths, the 16x16
+# MFMAs for those and e2m1
 TILED_VARIANTS = ((128, 256, 4, 1, 32), (256, 256, 8, 1, 32), (256, 128, 4, 1, 32), (128, 128, 4, 1, 32),
                   (64, 64, 4, 1, 32), (256, 256, 4, 2, 32), (128, 256, 4, 2, 32), (256, 128, 4, 2, 32),
                   (128, 128, 4, 2, 32), (64, 64, 4, 2, 32), (256, 256, 8, 1, 16))
@@ -355,7 +355,7 @@ def test_every_tiled_variant_on_a_ragged_problem(h):
                              ("e2m1", "e2m1_4096x4096x4096", True)):
         region = 64 if path == "i8" else 32
         for bm, bn, nw, kr, ms in TILED_VARIANTS:
-            if (kr > 1 or ms == 16) and path == "e2m1":
+            if kr > 1 and path == "e2m1":
                 continue
             if kr == 1:
                 ks = [8 * 32] if path == "e2m1" else [7 * region + region // 2]
@@ -572,7 +572,8 @@ def test_full_size_every_output(h, name, col_chunk):
 
 
 @pytest.mark.parametrize("name,ms", [("i8_4096x4096x4096", 16), ("i8_4096x4096x4096", 32),
-                                     ("f16_4096x4096x4096", 16), ("f16_4096x4096x4096", 32)])
+                                     ("f16_4096x4096x4096", 16), ("f16_4096x4096x4096", 32),
+                                     ("e2m1_4096x4096x4096", 16), ("e2m1_4096x4096x4096", 32)])
 def test_full_size_each_mfma_block(h, name, ms):
     # the 4096^3 workloads with the eight-wave 256x256 tile on each MFMA block
     # (32x32 and 16x16), every output against the oracle

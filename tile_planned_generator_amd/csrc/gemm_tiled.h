@@ -161,8 +161,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // clock and, on random operands, hold a higher clock under the power limit.
     constexpr bool M16 = MS == 16;
     static_assert(MS == 32 || MS == 16, "MFMA block size");
-    static_assert(!M16 || ((PATH == P_F16 || PATH == P_BF16 || PATH == P_I8) && WM * WN == 8 && KR == 1),
-                  "16x16 MFMAs: 16-bit and int8 operands, the eight-wave loop");
+    static_assert(!M16 || ((PATH == P_F16 || PATH == P_BF16 || PATH == P_I8 || PATH == P_E2M1) && WM * WN == 8 &&
+                           KR == 1),
+                  "16x16 MFMAs: 16-bit, int8 and e2m1 operands, the eight-wave loop");
     constexpr int BKS = KR * BKE;                      // k elements per K step
     constexpr int NSUB = 2 * KR;                       // MFMA substeps per K step
     constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN, KR);
@@ -469,7 +470,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const char *sB = smem + buf * STAGE + A_ALL;
         const int c = IS_MX ? 2 * s + kg : 2 * (s & 1) + kg;
         const int col0 = wn * WTN + ni * 32;
-        if constexpr (IS_E2M1) {
+        if constexpr (IS_E2M1 && M16) {
+            // 16x16: s is the block's column half; lane l takes code dword
+            // l >> 4 (k 8 (l >> 4) .. +7) of column l & 15 of that half, and the
+            // column's scale.  The 64 lanes of a read hit 64 distinct banks.
+            const int row = col0 + 16 * s + L16;
+            const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + 4 * grp16);
+            const unsigned sh = *reinterpret_cast<const unsigned short *>(sB + B_TILE + row * 2);
+            f.b[ni] = u32x4{codes, sh, 0u, 0u};
+        } else if constexpr (IS_E2M1) {
             // raw: the code word and the scale's bits; decode_b turns them into
             // the fp16 operand (in the MFMA phase, off the LDS-bound one).  Substep
             // 0 reads the column's whole 16-byte chunk (dword 2s + kg is substep
@@ -590,7 +599,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                         const u32x4 a = sm ? h1.a[mi] : h0.a[mi];
                         const u32x4 b = sn ? h1.b[ni] : h0.b[ni];
                         AccT &c = acc[mi][ni][2 * sm + sn];
-                        if constexpr (PATH == P_F16)
+                        if constexpr (PATH == P_F16 || PATH == P_E2M1)
                             c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b),
                                                                        __builtin_bit_cast(half8, a), c, 0, 0, 0);
                         else if constexpr (PATH == P_BF16)
@@ -693,6 +702,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
             if constexpr (M16) {
+                decode_b(f0);
+                decode_b(f1);
                 mfmas16(f0, f1);
             } else {
                 decode_b(f0);

@@ -64,7 +64,8 @@ VARIANTS = {
             (128, 128, 4, 2, 32), (64, 64, 4, 2, 32), (256, 256, 8, 1, 16)],
 }
 VARIANTS["bf16"] = VARIANTS["i8"] = VARIANTS["f16"]
-VARIANTS["e2m1"] = VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1 and v[4] == 32]
+VARIANTS["e2m1"] = [v for v in VARIANTS["f16"] if v[3] == 1]
+VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1 and v[4] == 32]
 REGION_K = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32, "mx": 128}
 
 
