@@ -169,11 +169,14 @@ def test_gemm_mx_small(h, M, N, K):
     run_mx(h, M, N, K)
 
 
-@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 256, 4), (256, 128, 4), (128, 128, 4),
-                                         (64, 64, 4)])
-def test_gemm_mx_every_variant(h, bm, bn, waves):
-    # a ragged problem with a half K step at the end
-    run_mx(h, 300, 330, 448, opts=dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=waves))
+@pytest.mark.parametrize("bm,bn,waves,ms", [(256, 256, 8, 32), (128, 256, 4, 32), (256, 128, 4, 32),
+                                            (128, 128, 4, 32), (64, 64, 4, 32), (256, 256, 8, 16)])
+def test_gemm_mx_every_variant(h, bm, bn, waves, ms):
+    # a ragged problem with a half K step at the end, unsplit and split in 3
+    for split in (1, 3):
+        info, _ = run_mx(h, 300, 330, 448, opts=dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_waves=waves,
+                                                                force_mfma=ms, force_split_k=split))
+        assert info.mfma_m == ms
 
 
 @pytest.mark.parametrize("split", [2, 3, 8])
@@ -231,6 +234,16 @@ def test_gemm_mx_full_size_every_output(h):
     checked on every output."""
     info, st = run_mx(h, 4096, 4096, 4096)
     assert info.split_k == 1 and st["n"] == 4096 * 4096
+
+
+@pytest.mark.parametrize("ms", [16, 32])
+def test_gemm_mx_full_size_each_mfma_block(h, ms):
+    """The 4096^3 workload with the eight-wave 256x256 tile on each MFMA block,
+    every output against the oracle."""
+    o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=256, force_n_tile=256, force_waves=8,
+                        force_mfma=ms)
+    info, st = run_mx(h, 4096, 4096, 4096, opts=o)
+    assert info.mfma_m == ms and st["n"] == 4096 * 4096
 
 
 def test_quant_then_gemm_end_to_end(h):

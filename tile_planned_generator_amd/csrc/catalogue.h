@@ -56,7 +56,8 @@ namespace dg {
     DG_TILE_SHAPES_M16(X, P_BF16, 1)   \
     DG_TILE_SHAPES_M16(X, P_I8, 0)     \
     DG_TILE_SHAPES_M16(X, P_I8, 1)     \
-    DG_TILE_SHAPES_M16(X, P_E2M1, 1)
+    DG_TILE_SHAPES_M16(X, P_E2M1, 1)   \
+    DG_TILE_SHAPES_M16(X, P_MX, 1)
 
 // Skinny VALU streaming GEMM over a row-major 16-bit B:
 // X(path, MR, LPR): up to MR rows of A; LPR lanes span one row of B (8 columns each).

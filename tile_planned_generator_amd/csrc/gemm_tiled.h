@@ -161,9 +161,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // clock and, on random operands, hold a higher clock under the power limit.
     constexpr bool M16 = MS == 16;
     static_assert(MS == 32 || MS == 16, "MFMA block size");
-    static_assert(!M16 || ((PATH == P_F16 || PATH == P_BF16 || PATH == P_I8 || PATH == P_E2M1) && WM * WN == 8 &&
-                           KR == 1),
-                  "16x16 MFMAs: 16-bit, int8 and e2m1 operands, the eight-wave loop");
+    static_assert(!M16 || (WM * WN == 8 && KR == 1), "16x16 MFMAs: the eight-wave loop");
     constexpr int BKS = KR * BKE;                      // k elements per K step
     constexpr int NSUB = 2 * KR;                       // MFMA substeps per K step
     constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN, KR);
@@ -442,7 +440,20 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const char *sA = smem + buf * STAGE;
         const int c = 2 * (s & 1) + kg;
         const int row = wm * WTM + mi * 32 + lr;
-        if constexpr (IS_MX) {
+        if constexpr (IS_MX && M16) {
+            // 16x16x128 block-scaled MFMA, s the block's row half: the 8-bit
+            // operand of lane group h holds k 16h .. +15 in its first four
+            // registers and k 64 + 16h .. +15 in its last four (probed on the GPU
+            // with one-hot operands), so the lane reads chunk h of both 64-byte
+            // regions of its row; the scale of lane group h applies to k 32h ..
+            // +31: byte `row` of the chunk of group h.
+            const int r16 = wm * WTM + mi * 32 + 16 * s + L16;
+            const int sw = (r16 >> 2) & 3;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(sA + A_BYTES + r16 * 64 + ((grp16 ^ sw) << 4));
+            f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + grp16 * 256 + r16);
+        } else if constexpr (IS_MX) {
             // Region s.  The 8-bit operand of the 32x32x64 block-scaled MFMA is
             // not 32 consecutive k per lane: lane group kg holds k 16kg .. +15 in
             // its first four registers and k 32 + 16kg .. +15 in its last four
@@ -497,6 +508,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             } else {
                 f.b[ni] = u32x4{e2_next[ni], e2_sh[ni], 0u, 0u};
             }
+        } else if constexpr (IS_MX && M16) {
+            // s is the block's column half; the 4-bit operand of lane group g
+            // holds k 32g .. +31 of the step: chunk g of the column's 64 bytes,
+            // and the column's scale byte of group g
+            const int row = col0 + 16 * s + L16;
+            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
+            f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + grp16 * 256 + row);
         } else if constexpr (BKMAJ && M16) {
             // s is the block's column half; the lane reads chunk lane >> 4
             const int row = col0 + 16 * s + L16;
@@ -596,10 +614,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
                     for (int sn = 0; sn < 2; ++sn) {
-                        const u32x4 a = sm ? h1.a[mi] : h0.a[mi];
+                        const AFrag a = sm ? h1.a[mi] : h0.a[mi];
                         const u32x4 b = sn ? h1.b[ni] : h0.b[ni];
                         AccT &c = acc[mi][ni][2 * sm + sn];
-                        if constexpr (PATH == P_F16 || PATH == P_E2M1)
+                        if constexpr (IS_MX)
+                            // first operand e2m1 (format 4, four registers), second fp8 e4m3
+                            c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                __builtin_bit_cast(intx8, u32x8{b.x, b.y, b.z, b.w, 0u, 0u, 0u, 0u}),
+                                __builtin_bit_cast(intx8, a), c, 4, 0, 0, (int)(sn ? h1.sb[ni] : h0.sb[ni]), 0,
+                                (int)(sm ? h1.sa[mi] : h0.sa[mi]));
+                        else if constexpr (PATH == P_F16 || PATH == P_E2M1)
                             c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b),
                                                                        __builtin_bit_cast(half8, a), c, 0, 0, 0);
                         else if constexpr (PATH == P_BF16)
@@ -687,7 +711,30 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             tie(f0);
             tie(f1);
             if constexpr (LAST) {
-                if constexpr (M16) {
+                if constexpr (M16 && IS_MX) {
+                    // a final half step (k 64 .. 127 past the end): the 4-bit
+                    // operands of lane groups 2 and 3 and the upper halves of the
+                    // 8-bit operands (k 64 + 16h ..) are zeroed, and the scales of
+                    // groups 2 and 3 set to 127 (a factor of one; a scale byte past
+                    // K may be the NaN code)
+                    if (nfull != nsteps) {
+                        const unsigned mb = grp16 < 2 ? ~0u : 0u;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            Frag &f = h ? f1 : f0;
+#pragma unroll
+                            for (int mi = 0; mi < FM; ++mi) {
+                                f.a[mi][4] = f.a[mi][5] = f.a[mi][6] = f.a[mi][7] = 0u;
+                                f.sa[mi] = (f.sa[mi] & mb) | (~mb & 127u);
+                            }
+#pragma unroll
+                            for (int ni = 0; ni < FN; ++ni) {
+                                f.b[ni] &= mb;
+                                f.sb[ni] = (f.sb[ni] & mb) | (~mb & 127u);
+                            }
+                        }
+                    }
+                } else if constexpr (M16) {
                     // a final half step: the lanes holding k past its first half
                     // (chunks 2 and 3) contribute 0 x 0
                     const bool keep = nfull == nsteps || grp16 < 2;

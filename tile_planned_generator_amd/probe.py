@@ -65,7 +65,7 @@ VARIANTS = {
 }
 VARIANTS["bf16"] = VARIANTS["i8"] = VARIANTS["f16"]
 VARIANTS["e2m1"] = [v for v in VARIANTS["f16"] if v[3] == 1]
-VARIANTS["mx"] = [v for v in VARIANTS["f16"] if v[3] == 1 and v[4] == 32]
+VARIANTS["mx"] = VARIANTS["e2m1"]
 REGION_K = {"f16": 32, "bf16": 32, "i8": 64, "e2m1": 32, "mx": 128}
 
 
