@@ -519,7 +519,9 @@ def test_mx_plans_satisfy_constraints(off, M, N, K):
         p = arr[i]
         name = p.kernel_name.decode()
         assert name.startswith("tiled_mx_k_"), name
-        assert p.mfma_m == 32 and p.mfma_n == 32 and p.mfma_k == 64
+        # 32x32x64 or 16x16x128 block-scaled MFMAs
+        assert (p.mfma_m, p.mfma_n, p.mfma_k) in ((32, 32, 64), (16, 16, 128))
+        assert name.endswith("_m16") == (p.mfma_m == 16)
         assert p.lds_bytes <= 163840 and p.vgpr_est <= 256 and p.agpr_est <= 256
         # K steps of 128 (two block-scaled MFMAs); slices start on whole steps
         assert p.k_main == 128 and p.k_tail in (0, 64)
