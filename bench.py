@@ -466,7 +466,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed launches first (the default, about 20 ms of the headline, runs past the "
+                         "dip of the power management after an idle start)")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--workloads", default="",
                     help="comma-separated subset of the other workloads to time")
