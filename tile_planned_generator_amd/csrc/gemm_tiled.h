@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // clock and, on random operands, hold a higher clock under the power limit.
     constexpr bool M16 = MS == 16;
     static_assert(MS == 32 || MS == 16, "MFMA block size");
-    static_assert(!M16 || (WM * WN == 8 && KR == 1), "16x16 MFMAs: the eight-wave loop");
+    static_assert(!M16 || (NW == 8 && KR == 1), "16x16 MFMAs: the eight-wave loop");
     constexpr int BKS = KR * BKE;                      // k elements per K step
     constexpr int NSUB = 2 * KR;                       // MFMA substeps per K step
     constexpr int NBUF = tiled_nbuf(PATH, BM, BN, WM, WN, KR);
@@ -440,20 +440,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const char *sA = smem + buf * STAGE;
         const int c = 2 * (s & 1) + kg;
         const int row = wm * WTM + mi * 32 + lr;
-        if constexpr (IS_MX && M16) {
-            // 16x16x128 block-scaled MFMA, s the block's row half: the 8-bit
-            // operand of lane group h holds k 16h .. +15 in its first four
-            // registers and k 64 + 16h .. +15 in its last four (probed on the GPU
-            // with one-hot operands), so the lane reads chunk h of both 64-byte
-            // regions of its row; the scale of lane group h applies to k 32h ..
-            // +31: byte `row` of the chunk of group h.
-            const int r16 = wm * WTM + mi * 32 + 16 * s + L16;
-            const int sw = (r16 >> 2) & 3;
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(sA + A_BYTES + r16 * 64 + ((grp16 ^ sw) << 4));
-            f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + grp16 * 256 + r16);
-        } else if constexpr (IS_MX) {
+        if constexpr (IS_MX) {
             // Region s.  The 8-bit operand of the 32x32x64 block-scaled MFMA is
             // not 32 consecutive k per lane: lane group kg holds k 16kg .. +15 in
             // its first four registers and k 32 + 16kg .. +15 in its last four
@@ -467,10 +454,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
-        } else if constexpr (M16) {
-            // s is the block's row half; the lane reads chunk lane >> 4
-            const int r16 = wm * WTM + mi * 32 + 16 * s + L16;
-            f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ ((r16 >> 2) & 3)) << 4));
         } else {
             f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + (s >> 1) * A_BYTES + row * 64 +
                                                         ((c ^ ((row >> 2) & 3)) << 4));
@@ -481,15 +464,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         const char *sB = smem + buf * STAGE + A_ALL;
         const int c = IS_MX ? 2 * s + kg : 2 * (s & 1) + kg;
         const int col0 = wn * WTN + ni * 32;
-        if constexpr (IS_E2M1 && M16) {
-            // 16x16: s is the block's column half; lane l takes code dword
-            // l >> 4 (k 8 (l >> 4) .. +7) of column l & 15 of that half, and the
-            // column's scale.  The 64 lanes of a read hit 64 distinct banks.
-            const int row = col0 + 16 * s + L16;
-            const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + 4 * grp16);
-            const unsigned sh = *reinterpret_cast<const unsigned short *>(sB + B_TILE + row * 2);
-            f.b[ni] = u32x4{codes, sh, 0u, 0u};
-        } else if constexpr (IS_E2M1) {
+        if constexpr (IS_E2M1) {
             // raw: the code word and the scale's bits; decode_b turns them into
             // the fp16 operand (in the MFMA phase, off the LDS-bound one).  Substep
             // 0 reads the column's whole 16-byte chunk (dword 2s + kg is substep
@@ -508,17 +483,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             } else {
                 f.b[ni] = u32x4{e2_next[ni], e2_sh[ni], 0u, 0u};
             }
-        } else if constexpr (IS_MX && M16) {
-            // s is the block's column half; the 4-bit operand of lane group g
-            // holds k 32g .. +31 of the step: chunk g of the column's 64 bytes,
-            // and the column's scale byte of group g
-            const int row = col0 + 16 * s + L16;
-            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
-            f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + grp16 * 256 + row);
-        } else if constexpr (BKMAJ && M16) {
-            // s is the block's column half; the lane reads chunk lane >> 4
-            const int row = col0 + 16 * s + L16;
-            f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
         } else if constexpr (BKMAJ) {
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
@@ -527,17 +491,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             if constexpr (IS_MX)
                 f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
         } else {
-            // (16x16: s is the block's column half, its own lane offsets; the
-            // region's K rows start at 0)
-            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[M16 ? 2 * ni + s : ni];
-            constexpr int KO = M16 ? 0 : KSUB * s * RB;
+            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[M16 ? 2 * ni : ni];
             u32x2 lo, hi;
             if constexpr (!IS_I8) {
-                lo = lds_tr16<KO>(a);
-                hi = lds_tr16<KO + 4 * RB>(a);
+                lo = lds_tr16<KSUB * s * RB>(a);
+                hi = lds_tr16<KSUB * s * RB + 4 * RB>(a);
             } else {
-                lo = lds_tr8<KO>(a);
-                hi = lds_tr8<KO + 8 * RB>(a);
+                lo = lds_tr8<KSUB * s * RB>(a);
+                hi = lds_tr8<KSUB * s * RB + 8 * RB>(a);
             }
             f.b[ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
@@ -601,39 +562,152 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni) mfma1(f, mi, ni);
     };
-    // 16x16 MFMAs of one region: fa / fb hold the row / column halves of the
-    // blocks (f0 the first, f1 the second); B goes in first as above, so lane l
-    // of a 16x16 tile holds row l & 15 and columns 4 (l >> 4) .. +3.
-    auto mfmas16 = [&](const Frag &h0, const Frag &h1) {
-        if constexpr (M16) {
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-            for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-                for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-                    for (int sn = 0; sn < 2; ++sn) {
-                        const AFrag a = sm ? h1.a[mi] : h0.a[mi];
-                        const u32x4 b = sn ? h1.b[ni] : h0.b[ni];
-                        AccT &c = acc[mi][ni][2 * sm + sn];
-                        if constexpr (IS_MX)
-                            // first operand e2m1 (format 4, four registers), second fp8 e4m3
-                            c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                __builtin_bit_cast(intx8, u32x8{b.x, b.y, b.z, b.w, 0u, 0u, 0u, 0u}),
-                                __builtin_bit_cast(intx8, a), c, 4, 0, 0, (int)(sn ? h1.sb[ni] : h0.sb[ni]), 0,
-                                (int)(sm ? h1.sa[mi] : h0.sa[mi]));
-                        else if constexpr (PATH == P_F16 || PATH == P_E2M1)
-                            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b),
-                                                                       __builtin_bit_cast(half8, a), c, 0, 0, 0);
-                        else if constexpr (PATH == P_BF16)
-                            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
-                                                                        __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
-                        else if constexpr (IS_I8)
-                            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(intx4, b),
-                                                                      __builtin_bit_cast(intx4, a), c, 0, 0, 0);
-                    }
+    // ---- 16x16 MFMAs: the fragments of one K region are both row halves of
+    // every 32-row A block and both column halves of every 32-column B block
+    // (16 rows / columns each).  A lane reads chunk lane >> 4 of row (column)
+    // lane & 15 of its half: the MFMA takes the whole 64-byte region.
+    struct Frag16 {
+        AFrag a[2][FM];
+        u32x4 b[2][FN];
+        unsigned sa[2][IS_MX ? FM : 1], sb[2][IS_MX ? FN : 1];
+    };
+    auto read_a16 = [&](int buf, int h, int mi, Frag16 &f) {
+        const char *sA = smem + buf * STAGE;
+        const int r16 = wm * WTM + mi * 32 + 16 * h + L16;
+        const int sw = (r16 >> 2) & 3;
+        if constexpr (IS_MX) {
+            // 16x16x128 block-scaled MFMA: the 8-bit operand of lane group g
+            // holds k 16g .. +15 in its first four registers and k 64 + 16g ..
+            // +15 in its last four (probed on the GPU with one-hot operands), so
+            // the lane reads chunk g of both 64-byte regions of its row; the
+            // scale of lane group g applies to k 32g .. +31: byte `r16` of the
+            // chunk of group g.
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(sA + A_BYTES + r16 * 64 + ((grp16 ^ sw) << 4));
+            f.a[h][mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            f.sa[h][mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + grp16 * 256 + r16);
+        } else {
+            f.a[h][mi] = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
         }
+    };
+    auto read_b16 = [&](int buf, int h, int ni, Frag16 &f) {
+        const char *sB = smem + buf * STAGE + A_ALL;
+        const int row = wn * WTN + ni * 32 + 16 * h + L16;   // column of the tile
+        if constexpr (IS_E2M1) {
+            // code dword g (k 8g .. +7) of the column and its scale; the 64
+            // lanes of a read hit 64 distinct banks
+            const unsigned codes = *reinterpret_cast<const unsigned *>(sB + row * 16 + 4 * grp16);
+            const unsigned sh = *reinterpret_cast<const unsigned short *>(sB + B_TILE + row * 2);
+            f.b[h][ni] = u32x4{codes, sh, 0u, 0u};
+        } else if constexpr (IS_MX) {
+            // the 4-bit operand of lane group g holds k 32g .. +31 of the step:
+            // chunk g of the column's 64 bytes, and the column's scale of group g
+            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
+            f.sb[h][ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + grp16 * 256 + row);
+        } else if constexpr (BKMAJ) {
+            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
+        } else {
+            // transposing reads, this half's own lane offsets; K rows from 0
+            const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[2 * ni + h];
+            u32x2 lo, hi;
+            if constexpr (!IS_I8) {
+                lo = lds_tr16<0>(a);
+                hi = lds_tr16<4 * RB>(a);
+            } else {
+                lo = lds_tr8<0>(a);
+                hi = lds_tr8<8 * RB>(a);
+            }
+            f.b[h][ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+    };
+    auto read_frag16 = [&](int buf, int h, Frag16 &f) {
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) read_a16(buf, h, mi, f);
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) read_b16(buf, h, ni, f);
+    };
+    // (as settle / tie for the 32x32 fragments)
+    auto tie16 = [&](Frag16 &f) {
+        if constexpr (B_TR) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(f.b[h][ni]) : : "memory");
+        }
+    };
+    auto settle16 = [&](Frag16 &f) {
+        if constexpr (B_TR) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            tie16(f);
+        }
+    };
+    auto decode_b16 = [&](Frag16 &f) {
+        if constexpr (IS_E2M1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int ni = 0; ni < FN; ++ni) {
+                    const unsigned codes = f.b[h][ni].x;
+                    const unsigned short sh = (unsigned short)f.b[h][ni].y;
+                    f.b[h][ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
+                }
+        }
+    };
+    // A final half step (keep false): the lanes holding k past its first half
+    // (lane groups 2 and 3; for MX the upper halves of the 8-bit operands and
+    // the 4-bit operands of lane groups 2 and 3, whose scales become 127, a
+    // factor of one, since a scale byte past K may be the NaN code) contribute
+    // 0 x 0.  Branch-free.
+    auto keep16 = [&](Frag16 &f, bool keep) {
+        const unsigned mb = (keep || grp16 < 2) ? ~0u : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi) {
+                if constexpr (IS_MX) {
+                    const unsigned mu = keep ? ~0u : 0u;
+#pragma unroll
+                    for (int e = 4; e < 8; ++e) f.a[h][mi][e] &= mu;
+                    f.sa[h][mi] = (f.sa[h][mi] & mb) | (~mb & 127u);
+                } else {
+                    f.a[h][mi] &= mb;
+                }
+            }
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni) {
+                f.b[h][ni] &= mb;
+                if constexpr (IS_MX) f.sb[h][ni] = (f.sb[h][ni] & mb) | (~mb & 127u);
+            }
+        }
+    };
+    // MFMA q of a region, q = ((mi * 2 + sm) * FN + ni) * 2 + sn; B goes in
+    // first as above, so lane l of a 16x16 tile holds row l & 15 and columns
+    // 4 (l >> 4) .. +3.
+    auto mfma16 = [&](const Frag16 &f, int q) {
+        if constexpr (M16) {
+            const int sn = q & 1, ni = (q >> 1) % FN, sm = (q / (2 * FN)) & 1, mi = q / (4 * FN);
+            const AFrag a = f.a[sm][mi];
+            const u32x4 b = f.b[sn][ni];
+            AccT &c = acc[mi][ni][2 * sm + sn];
+            if constexpr (IS_MX)
+                // first operand e2m1 (format 4, four registers), second fp8 e4m3
+                c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    __builtin_bit_cast(intx8, u32x8{b.x, b.y, b.z, b.w, 0u, 0u, 0u, 0u}),
+                    __builtin_bit_cast(intx8, a), c, 4, 0, 0, (int)f.sb[sn][ni], 0, (int)f.sa[sm][mi]);
+            else if constexpr (PATH == P_F16 || PATH == P_E2M1)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b), __builtin_bit_cast(half8, a),
+                                                           c, 0, 0, 0);
+            else if constexpr (PATH == P_BF16)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                            __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+            else
+                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(intx4, b), __builtin_bit_cast(intx4, a),
+                                                          c, 0, 0, 0);
+        }
+    };
+    auto mfmas16 = [&](const Frag16 &f) {
+#pragma unroll
+        for (int q = 0; q < 4 * FM * FN; ++q) mfma16(f, q);
     };
     // A final half step runs its second substep on zeroed fragments (0 x 0 adds
     // nothing): the fragments are ANDed with a uniform mask, so the loop body has
@@ -697,61 +771,38 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         if (lag) bar();
         // One step; the last one (LAST) issues no loads and masks its second
         // substep when it is a half step.
+        Frag16 fr;   // (16x16 MFMAs)
         auto step = [&](int st, auto last_tag) {
             constexpr bool LAST = decltype(last_tag)::value;
             const int buf = st % NBUF;
             // memory phase: the fragment reads of stage st, with the loads of
             // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
             // to different units)
-            read_frag(buf, S0{}, f0, g0 + st);
-            if constexpr (!LAST) load_stage(st + AHEAD, 0);
-            read_frag(buf, S1{}, f1, g0 + st);
-            if constexpr (!LAST) load_stage(st + AHEAD, 1);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
-            tie(f0);
-            tie(f1);
-            if constexpr (LAST) {
-                if constexpr (M16 && IS_MX) {
-                    // a final half step (k 64 .. 127 past the end): the 4-bit
-                    // operands of lane groups 2 and 3 and the upper halves of the
-                    // 8-bit operands (k 64 + 16h ..) are zeroed, and the scales of
-                    // groups 2 and 3 set to 127 (a factor of one; a scale byte past
-                    // K may be the NaN code)
-                    if (nfull != nsteps) {
-                        const unsigned mb = grp16 < 2 ? ~0u : 0u;
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            Frag &f = h ? f1 : f0;
-#pragma unroll
-                            for (int mi = 0; mi < FM; ++mi) {
-                                f.a[mi][4] = f.a[mi][5] = f.a[mi][6] = f.a[mi][7] = 0u;
-                                f.sa[mi] = (f.sa[mi] & mb) | (~mb & 127u);
-                            }
-#pragma unroll
-                            for (int ni = 0; ni < FN; ++ni) {
-                                f.b[ni] &= mb;
-                                f.sb[ni] = (f.sb[ni] & mb) | (~mb & 127u);
-                            }
-                        }
-                    }
-                } else if constexpr (M16) {
-                    // a final half step: the lanes holding k past its first half
-                    // (chunks 2 and 3) contribute 0 x 0
-                    const bool keep = nfull == nsteps || grp16 < 2;
-                    keep_if(f0, keep);
-                    keep_if(f1, keep);
-                } else {
-                    keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
-                }
+            if constexpr (M16) {
+                read_frag16(buf, 0, fr);
+                if constexpr (!LAST) load_stage(st + AHEAD, 0);
+                read_frag16(buf, 1, fr);
+                if constexpr (!LAST) load_stage(st + AHEAD, 1);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
+                tie16(fr);
+                if constexpr (LAST) keep16(fr, nfull == nsteps);
+            } else {
+                read_frag(buf, S0{}, f0, g0 + st);
+                if constexpr (!LAST) load_stage(st + AHEAD, 0);
+                read_frag(buf, S1{}, f1, g0 + st);
+                if constexpr (!LAST) load_stage(st + AHEAD, 1);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
+                tie(f0);
+                tie(f1);
+                if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
             }
             bar();
             // compute phase, at raised wave priority so that the SIMD's other
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
             if constexpr (M16) {
-                decode_b(f0);
-                decode_b(f1);
-                mfmas16(f0, f1);
+                decode_b16(fr);
+                mfmas16(fr);
             } else {
                 decode_b(f0);
                 mfmas(f0);
@@ -772,6 +823,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         // here keeps the rule that no transposing read is left in flight)
         settle(f0);
         settle(f1);
+        settle16(fr);
         if (!lag) bar();
     } else {
         // Four waves, one per SIMD: each wave hides its own LDS reads and buffer
