@@ -12,17 +12,22 @@ synthetic data drawn on the GPU and resident in HBM before any timing starts.
 Timing: HIP events on the stream the kernels run on (torch's current stream),
 bracketing K back-to-back steps after W warm-up steps; ms_per_step is the
 average and `value` the whole-job rate.  `repeats` times five more runs of K
-steps (median and minimum).  A step is one launch of the kernel, so the
-roofline's `achieved` divides the algorithmic work by the kernel's average
-duration over all 6K timed launches (a kernel trace of the same command
-averages to it; later launches run a little slower as the chip heats).
-`telemetry` records the engine clock and the package power over a 3 s loop of
-the headline kernel.  The roofline's `traffic` is the HBM
-bytes per launch recorded from rocprofv3 counters in profiles/hbm_traffic.txt,
-reported only while the kernel sources still hash to the recorded value.  Small HBM-bound workloads rotate through copies of B (>= 576 MB in
-all, twice the L2 + MALL) so that every step reads HBM, and are also reported
-warm; workloads whose kernels are shorter than the host's launch cost are
-replayed from a captured HIP graph (checked against an eager run).
+steps (each run's time, the median and the minimum) and the median of 100
+launches each bracketed by its own event pair (an isolated launch with its
+overhead).  A step is one launch of the kernel, so the roofline's `achieved`
+divides the algorithmic work by the kernel's average duration over the K timed
+launches (in a kernel trace of the same command, the mean of those launches).
+After an idle start the power management settles over about 10 ms, during which
+launches run slower; the default warm-up runs past it, and runs that start
+inside it (short warm-ups) show it in `repeats`.  `telemetry` records the engine clock
+and the package power over a 3 s loop of the headline kernel, `plan` the
+headline plan's shape and compiled resources.  The roofline's `traffic` is the
+HBM bytes per launch recorded from rocprofv3 counters in
+profiles/hbm_traffic.txt, reported only while the kernel sources still hash to
+the recorded value.  Small HBM-bound workloads rotate through copies of B
+(>= 576 MB in all, twice the L2 + MALL) so that every step reads HBM, and are
+also reported warm; workloads whose kernels are shorter than the host's launch
+cost are replayed from a captured HIP graph (checked against an eager run).
 
 The CPU baseline is the oracle (plain C, binary64 / int64) timed on a bounded
 sample of the headline workload on this host's cores.
@@ -287,6 +292,42 @@ def report(p, ms):
             "tile": f"{i.m_tile}x{i.n_tile}", "algorithmic_bytes": byts, "ops": ops}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def launch_pairs(p, n=100):
+    """Median milliseconds of one launch bracketed by its own event pair (n
+    launches): the kernel plus the overhead of an isolated launch."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        p.launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+
+
+def plan_record(info):
+    """The headline plan's shape and resources: the compiler's register and LDS
+    counts of the chosen kernel and the waves it runs per SIMD."""
+    return {"kernel": info.kernel_name.decode(), "tile": [info.m_tile, info.n_tile],
+            "mfma": [info.mfma_m, info.mfma_n, info.mfma_k], "waves_per_wg": info.waves_per_wg,
+            "waves_per_simd": info.waves_per_simd, "vgpr": info.vgpr_est, "agpr": info.agpr_est,
+            "lds_bytes": info.lds_bytes, "k_main": info.k_main, "n_main": info.n_main, "k_tail": info.k_tail,
+            "split_k": info.split_k, "est_us": round(info.est_us, 2)}
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle on leading rows of the int8 4096^3 workload; rows grow until
     about `budget_s` seconds of CPU work."""
@@ -306,7 +347,7 @@ def cpu_baseline(budget_s=12.0):
         spent += dt
     ops = 2.0 * rows * w.N * w.K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"rows 0..{rows - 1} of the int8 4096x4096x4096 GEMM "
                       f"({rows}x4096x4096 multiply-adds, int64 accumulation), {dt:.2f} s"}
 
@@ -502,20 +543,21 @@ def main():
     p = Prepared(h, HEADLINE, dev, rotate=False)
     ms, steps = time_steps(p, args.steps, args.warmup, use_graph=False)
     head = report(p, ms)
+    plan_info = p.info
     ops, _ = algorithmic(p.w)
     achieved_job = ops / (ms * 1e-3) / 1e12
     rep = repeats(p, steps)
+    rep["launch_pair_ms_median"] = round(launch_pairs(p), 6)
     rep["TOP/s_median"] = round(ops / (rep["ms_median"] * 1e-3) / 1e12, 2)
     rep["TOP/s_best"] = round(ops / (rep["ms_min"] * 1e-3) / 1e12, 2)
-    # the kernel's average duration over every timed launch (the timed steps and
-    # the repeats; one launch per step), the figure a kernel trace of this
-    # command averages to
-    kernel_ms = (ms * steps + sum(rep["all_ms"]) * steps) / (steps * (1 + rep["n"]))
+    # the kernel's average duration over the timed region (one launch per step,
+    # launched back to back): the mean of those launches in a kernel trace of
+    # this command
+    kernel_ms = ms
     achieved = ops / (kernel_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["i8"],
                 "unit": "TOP/s", "frac": round(achieved / PEAK["i8"], 4),
-                "traffic": recorded_traffic(HEADLINE), "kernel_ms": round(kernel_ms, 6),
-                "launches": steps * (1 + rep["n"])}
+                "traffic": recorded_traffic(HEADLINE), "kernel_ms": round(kernel_ms, 6), "launches": steps}
     stages = stage_breakdown(h, p)
     telem = None if args.no_telemetry else telemetry(p, ms)
     del p
@@ -552,6 +594,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "repeats": rep,
+        "plan": plan_record(plan_info),
         "telemetry": telem,
         "stages": stages,
         "device": {"name": props.name, "cus": props.multi_processor_count},
