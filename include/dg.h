@@ -154,8 +154,8 @@ typedef struct {
                                  K is DG_ERR_ALIGNMENT. */
     int32_t force_waves;      /* waves per workgroup of the tiled path (0 = free)    */
     int32_t force_mfma;       /* MFMA output block of the tiled path: 32 (32x32) or 16
-                                 (16x16; 16-bit and int8 paths, eight-wave tiles)
-                                 (0 = free) */
+                                 (16x16; every path, eight-wave tiles) (0 = free);
+                                 other values are DG_ERR_INVALID_ARG */
 } dg_plan_opts;
 
 /* Description of the device the planner plans for.  dg_create fills it from

@@ -241,6 +241,32 @@ def test_conflicting_compute_units(off):
     assert _status(off.plan, 1, 256, 256, opts=o)[0] == dg.DG_ERR_CONFLICT
 
 
+def test_mfma_block_option(off):
+    # force_mfma picks the MFMA block of the tiled path: 16x16 exists for the
+    # eight-wave 256x256 tile of every path, 32x32 for every tile
+    probs = ((4096, 4096, 4096, "i8", "i8", "i32", dg.DG_ROW_MAJOR), (4096, 4096, 4096, "f16", "f16", "f16",
+             dg.DG_COL_MAJOR), (2048, 2048, 8192, "bf16", "bf16", "bf16", dg.DG_ROW_MAJOR),
+             (4096, 4096, 4096, "f16", "e2m1", "f16", dg.DG_COL_MAJOR))
+    for M, N, K, a, b, c, lay in probs:
+        for ms in (16, 32):
+            p = off.plan(M, N, K, a, b, c, lay, opts=dg.dg_plan_opts(force_mfma=ms, force_path=dg.DG_PATH_TILED))
+            assert p.mfma_m == p.mfma_n == ms and p.kernel_name.decode().endswith("_m16") == (ms == 16)
+            if ms == 16:
+                assert (p.m_tile, p.n_tile, p.waves_per_wg) == (256, 256, 8)
+                assert p.mfma_k == {"i8": 64}.get(a, 32)
+        # a 16x16 four-wave tile is not compiled
+        o = dg.dg_plan_opts(force_mfma=16, force_waves=4)
+        assert _status(off.plan, M, N, K, a, b, c, lay, opts=o)[0] == dg.DG_ERR_NO_CANDIDATE
+    # only 16 and 32 are MFMA blocks; the option belongs to the tiled path
+    o = dg.dg_plan_opts(force_mfma=8)
+    assert _status(off.plan, 256, 256, 256, opts=o)[0] == dg.DG_ERR_INVALID_ARG
+    o = dg.dg_plan_opts(force_mfma=16, force_path=dg.DG_PATH_SKINNY)
+    assert _status(off.plan, 1, 4096, 4096, opts=o)[0] == dg.DG_ERR_CONFLICT
+    # a streaming-shaped problem with the option set plans on the tiled path
+    p = off.plan(1, 4096, 8192, "bf16", "bf16", "bf16", opts=dg.dg_plan_opts(force_mfma=32))
+    assert p.path == dg.DG_PATH_TILED and p.mfma_m == 32
+
+
 def test_forced_columns_pick_the_streaming_variant(off):
     # force_n_tile alone selects the streaming kernels' columns per workgroup
     for nt in (256, 512, 1024, 2048):

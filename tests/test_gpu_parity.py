@@ -504,6 +504,11 @@ def test_pad_k(h):
     run(h, w, opts=o, pad=16, b_colmajor=True)
     # fp16 with alpha, beta * D and only a tail (K < 16)
     run(h, synth.make("f16_256x256x256_alpha_beta_d", M=64, N=72, K=7), opts=o, pad=8)
+    # the 16x16 MFMA tile with a half step, then the tail (fp16 and int8)
+    o16 = dg.dg_plan_opts(pad_k=1, force_path=dg.DG_PATH_TILED, force_m_tile=256, force_n_tile=256,
+                          force_waves=8, force_mfma=16)
+    run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=300, N=264, K=7 * 32 + 16 + 8), opts=o16, pad=8)
+    run(h, synth.make("i8_4096x4096x4096", M=300, N=200, K=5 * 64 + 32 + 4), opts=o16, pad=16)
 
 
 def test_k_zero_and_empty(h):
@@ -512,10 +517,11 @@ def test_k_zero_and_empty(h):
     run(h, synth.make("f16_2048x2048x8192_bias_gelu", M=40, N=64, K=0))
     # every loop shape with an empty K range (eight-wave and four-wave tiles)
     # (the K step: regions of 32 k for 16-bit operands, 64 k for int8)
-    for bm, bn, nw, kr in ((256, 256, 8, 1), (128, 256, 4, 1), (128, 128, 4, 1), (256, 256, 4, 2)):
+    for bm, bn, nw, kr, ms in ((256, 256, 8, 1, 32), (128, 256, 4, 1, 32), (128, 128, 4, 1, 32),
+                               (256, 256, 4, 2, 32), (256, 256, 8, 1, 16)):
         for name, region in (("f16_256x256x256_alpha_beta_d", 32), ("i8_4096x4096x4096", 64)):
             o = dg.dg_plan_opts(force_m_tile=bm, force_n_tile=bn, force_path=dg.DG_PATH_TILED,
-                                force_waves=nw, force_k_tile=region * kr)
+                                force_waves=nw, force_k_tile=region * kr, force_mfma=ms)
             run(h, synth.make(name, M=300, N=260, K=0), opts=o)
     # M = 0 or N = 0: nothing to do, nothing launched
     Ce = torch.empty(0, 64, dtype=torch.float16, device=DEV)

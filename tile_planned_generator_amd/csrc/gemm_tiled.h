@@ -46,9 +46,13 @@
 //     chunk of scales (the scale arrays are group-major, so each chunk is one
 //     contiguous load).  The scale register of lane group kg covers k 32kg .. +31
 //     of one MFMA.
-//   - Accumulators stay in registers for the whole K range (32x32 blocks:
-//     v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8,
-//     v_mfma_scale_f32_32x32x64_f8f6f4).
+//   - Accumulators stay in registers for the whole K range.  MFMA blocks
+//     (MS): 32x32 (v_mfma_f32_32x32x16_f16/_bf16, v_mfma_i32_32x32x32_i8,
+//     v_mfma_scale_f32_32x32x64_f8f6f4; two per 64-byte region) or, on the
+//     eight-wave tile, 16x16 (v_mfma_f32_16x16x32_f16/_bf16,
+//     v_mfma_i32_16x16x64_i8, v_mfma_scale_f32_16x16x128_f8f6f4; one per
+//     region and 16x16 block): the same work per clock, and on random operands
+//     the 16x16 ones run at a higher clock under the power limit.
 //   - The K schedule is n_main full steps then at most one shorter step of
 //     1 .. 2KR-1 substeps for the tail (the pages' variable K step, [generator]
 //     DeepGEMM article, kwkr.cn, section 2.2, first layer).
