@@ -415,8 +415,11 @@ def test_skinny_mfma(h, M):
 
 @pytest.mark.parametrize("M", [1, 2, 4, 7])
 def test_skinny_e2m1(h, M):
-    # one slice holds at most 32 KB of A (K * rows * 2 bytes): M > 4 needs two
-    for K, S in ((4096, 1 if M <= 4 else 2), (4096, 4), (1056, 0)):
+    # one slice holds at most 32 KB of A (K * rows * 2 bytes): M > 4 needs two.
+    # The longest slice each row count allows (16384 / MR, MR the rows the
+    # kernel stages) takes the staging loops past their first batch.
+    longest = {1: 16384, 2: 8192, 4: 4096, 7: 2048}[M]
+    for K, S in ((4096, 1 if M <= 4 else 2), (4096, 4), (1056, 0), (longest, 1)):
         w = synth.make("e2m1_1x4096x4096", M=M, N=300, K=K)
         run(h, w, opts=dg.dg_plan_opts(force_path=dg.DG_PATH_SKINNY, force_split_k=S))
 

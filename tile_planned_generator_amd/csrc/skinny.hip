@@ -259,9 +259,9 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
 // (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then v_dot2_f32_f16), and the
 // scale applied to the group sum.  A's slice and the slice's scales of the
 // workgroup's 16 columns (one 32-byte piece per group row of the group-major
-// scale array, fetched as dwords) are staged in LDS once per workgroup, after
-// the first codes are requested; groups are taken GU at a time, all their loads
-// issued before any arithmetic; the 16 lanes of a column are summed in a fixed
+// scale array, fetched as dwords) are staged in LDS once per workgroup, their
+// loads issued with the first codes; groups are taken GU at a time, all their
+// loads issued before any arithmetic; the 16 lanes of a column are summed in a fixed
 // order at the end.
 constexpr int E2M1_COLS_PER_WG = 16;
 constexpr int E2M1_A_LDS = 32768;   // bytes of A staged per workgroup
@@ -300,30 +300,58 @@ __global__ void __launch_bounds__(256) skinny_e2m1_kernel(SkinnyArgs p)
             c[u] = ld16_nt(Bc + (int64_t)gcs[u] * 16);
         }
     };
-    if (gbeg + q < gend) load_groups(gbeg + q);
 
-    // stage the slice's scales of the workgroup's columns: group g, columns
-    // n0 .. n0+15 are 32 contiguous bytes (8 dwords) of the group-major array
-    // (rows of ld_scale fp16, ld_scale even); buffer loads return 0 past the
-    // array's end, and columns past N are never used
-    {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void *>(p.scale), (short)0, (int)((int64_t)(p.K / 32) * p.ld_scale * 2), 0x00020000);
-        unsigned *sSw = reinterpret_cast<unsigned *>(sS);
-        for (int idx = tid; idx < (gend - gbeg) * 8; idx += 256) {
-            const int gr = idx >> 3, d = idx & 7;
-            const int off = (int)(((int64_t)(gbeg + gr) * p.ld_scale + n0) * 2 + 4 * d);
-            sSw[idx] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-        }
-    }
-
-    // stage A[0:M][kbeg:kend] (16-byte chunks; rows past M are zero)
-    for (int idx = tid; idx < MR * L / 8; idx += 256) {
-        const int m = idx / (L / 8), k8 = idx - m * (L / 8);
+    // Staging of the slice's scales of the workgroup's columns (group g,
+    // columns n0 .. n0+15: 32 contiguous bytes, 8 dwords, of the group-major
+    // array, rows of ld_scale fp16, ld_scale even) and of A[0:M][kbeg:kend]
+    // (16-byte chunks; rows past M are zero).  The first SB dwords and AB
+    // chunks per thread are requested together with the first codes, so that
+    // one memory round trip serves all three; longer slices stage the rest
+    // afterwards.  Buffer loads return 0 past the scale array's end; columns
+    // past N are never used.
+    constexpr int SB = 4, AB = 2 * MR;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(p.scale), (short)0, (int)((int64_t)(p.K / 32) * p.ld_scale * 2), 0x00020000);
+    unsigned *sSw = reinterpret_cast<unsigned *>(sS);
+    const int ns = (gend - gbeg) * 8, L8 = L / 8, na = MR * L8;
+    auto scale_off = [&](int idx) {
+        return (int)(((int64_t)(gbeg + (idx >> 3)) * p.ld_scale + n0) * 2 + 4 * (idx & 7));
+    };
+    auto a_chunk = [&](int idx) {
+        const int m = idx / L8, k8 = idx - m * L8;
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (m < M) v = ld16(A + (int64_t)m * p.lda + kbeg + 8 * k8);
-        *reinterpret_cast<u32x4 *>(sA + m * L + 8 * k8) = v;
+        return v;
+    };
+    unsigned sv[SB];
+    u32x4 av[AB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int idx = tid + 256 * j;
+        sv[j] = idx < ns ? __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off(idx), 0, 0) : 0u;
     }
+#pragma unroll
+    for (int j = 0; j < AB; ++j) {
+        const int idx = tid + 256 * j;
+        av[j] = idx < na ? a_chunk(idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // unconditional (lanes past the slice's groups load group gbeg, unused), so
+    // that the staging writes below wait only for the staging loads
+    load_groups(gbeg + q);
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int idx = tid + 256 * j;
+        if (idx < ns) sSw[idx] = sv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < AB; ++j) {
+        const int idx = tid + 256 * j;
+        if (idx < na) *reinterpret_cast<u32x4 *>(sA + 8 * idx) = av[j];
+    }
+    for (int idx = tid + 256 * SB; idx < ns; idx += 256)
+        sSw[idx] = __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off(idx), 0, 0);
+    for (int idx = tid + 256 * AB; idx < na; idx += 256)
+        *reinterpret_cast<u32x4 *>(sA + 8 * idx) = a_chunk(idx);
     __syncthreads();
 
     float acc[MR];
@@ -421,9 +449,12 @@ hipError_t launch_skinny_mfma(int id, const SkinnyArgs &a, int gx, int gy, hipSt
 }
 hipError_t launch_skinny_e2m1(int id, const SkinnyArgs &a, int gx, int gy, hipStream_t s)
 {
-    // the A slice must fit the kernel's LDS staging area, in whole 32-k groups
+    // the A slice must fit the kernel's LDS staging area, in whole 32-k groups,
+    // and every slice must start before K (the kernel reads a slice's first
+    // group without a check)
     if (id >= 0 && id < skinny_e2m1_count() &&
-        ((int64_t)a.k_slice * k_e2m1_mr[id] * 2 > E2M1_A_LDS || a.k_slice % 32))
+        ((int64_t)a.k_slice * k_e2m1_mr[id] * 2 > E2M1_A_LDS || a.k_slice % 32 || a.k_slice <= 0 ||
+         a.K <= 0 || (int64_t)(gy - 1) * a.k_slice >= a.K))
         return hipErrorInvalidValue;
     return launch_entry(k_e2m1, skinny_e2m1_count(), id, a, gx, gy, s);
 }
