@@ -555,11 +555,13 @@ __global__ void __launch_bounds__(256) reduce4_kernel(ReduceArgs a)
 // Many slices and N a multiple of 4: R = lanes runs of slices per group of four
 // consecutive outputs.  A workgroup holds 256 / R groups; thread (run r, group
 // g) sums slices [r*C, (r+1)*C) of its four outputs in ascending order, with
-// 16-byte loads that are contiguous across the threads of a run, and the R run
+// 16-byte loads that are contiguous across the threads of a run (up to 16 in
+// flight per thread), and the R run
 // sums are then added in run order through LDS.  The order of every addition is
 // fixed, so the result does not depend on timing.
 __global__ void __launch_bounds__(256) reduce_runs_kernel(ReduceArgs a)
 {
+    constexpr int RU = 16;   // loads in flight per thread: one round trip for runs of up to 16 slices
     const int R = a.lanes, G = 256 / R;
     const int t = threadIdx.x, g = t % G, r = t / G;
     const int64_t MN = (int64_t)a.M * a.N;
@@ -572,15 +574,15 @@ __global__ void __launch_bounds__(256) reduce_runs_kernel(ReduceArgs a)
     if (a.is_int) {
         const int32_t *w = reinterpret_cast<const int32_t *>(a.ws) + (ok ? o4 : 0);
         intx4 acc = intx4{0, 0, 0, 0};
-        for (int s = s0; s < s1; s += 8) {
-            intx4 v[8];
+        for (int s = s0; s < s1; s += RU) {
+            intx4 v[RU];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < RU; ++u)
                 v[u] = (ok && s + u < s1)
                            ? __builtin_nontemporal_load(reinterpret_cast<const intx4 *>(w + (int64_t)(s + u) * MN))
                            : intx4{0, 0, 0, 0};
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < RU; ++u)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[c] = (int)((uint32_t)acc[c] + (uint32_t)v[u][c]);
         }
@@ -602,15 +604,15 @@ __global__ void __launch_bounds__(256) reduce_runs_kernel(ReduceArgs a)
     } else {
         const float *w = reinterpret_cast<const float *>(a.ws) + (ok ? o4 : 0);
         floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int s = s0; s < s1; s += 8) {
-            floatx4 v[8];
+        for (int s = s0; s < s1; s += RU) {
+            floatx4 v[RU];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < RU; ++u)
                 v[u] = (ok && s + u < s1)
                            ? __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(w + (int64_t)(s + u) * MN))
                            : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += v[u];
+            for (int u = 0; u < RU; ++u) acc += v[u];
         }
         part[t] = acc;
         __syncthreads();
