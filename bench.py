@@ -375,11 +375,13 @@ def stage_breakdown(h, p, launches=5):
     s["unit"] = "s_memtime ticks per workgroup"
     # The s_memtime counter runs at the MFMA clock (a 32x32x32 int8 MFMA issues
     # every 32 ticks back to back), and its rate over the K loop's real time is
-    # the clock the loop ran at.  MFMA cycles one SIMD owes per K step: the
-    # tile's 32x32 blocks times the step's MFMA depths times the cycles of one
-    # MFMA (32 for int8 32x32x32), over the CU's 4 SIMDs.
+    # the clock the loop ran at.  MFMA cycles each SIMD owes per K step: the
+    # step's multiply-adds (tile x K step) over the CU's dense rate per clock
+    # (the published peak over 256 CUs at 2.4 GHz: 4096 int8 multiply-adds,
+    # whichever MFMA block the kernel uses).
     i = p.info
-    per_step = (i.m_tile // 32) * (i.n_tile // 32) * (i.k_main // i.mfma_k) * 32 / 4
+    macs_per_clk = PEAK[p.w.path] * 1e12 / 2 / 256 / 2.4e9
+    per_step = i.m_tile * i.n_tile * i.k_main / macs_per_clk
     if s["k_loop"]["median"] > 0:
         s["k_loop_mfma_busy"] = round(per_step * s["k_steps"] / s["k_loop"]["median"], 4)
     if s.get("tick_ghz"):

@@ -15,9 +15,8 @@ namespace dg {
 //   b_kmajor  1: B stored N x K (K contiguous); 0: K x N (N contiguous)
 //   BM x BN   workgroup tile; WM x WN wave grid (each wave BM/WM x BN/WN)
 //   KR        64-byte K regions per K step: the K step (K_tile) is KR x 32 k
-//             (16-bit), KR x 64 k (int8)
+//             (16-bit), KR x 64 k (int8); e2m1 and MX take KR = 1
 //   MS        MFMA output block: 32 (32x32) or 16 (16x16)
-//             for 16-bit operands and KR x 64 k for int8 (e2m1 and MX: KR = 1)
 #define DG_TILE_SHAPES(X, path, kmaj)  \
     X(path, kmaj, 128, 256, 2, 2, 1, 32)   \
     X(path, kmaj, 256, 256, 2, 4, 1, 32)   \
