@@ -488,6 +488,34 @@ def test_int_alpha_beta_d(h):
     run(h, w, alpha=3, beta=-2)
 
 
+@pytest.mark.parametrize("path,name,colm", [("f16", "f16_2048x2048x8192_bias_gelu", False),
+                                            ("f16", "f16_2048x2048x8192_bias_gelu", True),
+                                            ("bf16", "bf16_16x4096x131072", False),
+                                            ("i8", "i8_4096x4096x4096", False),
+                                            ("i8", "i8_4096x4096x4096", True),
+                                            ("e2m1", "e2m1_4096x4096x4096", True)])
+def test_small_tiles_with_beta_d(h, path, name, colm):
+    # beta * D on every 64x64 tile (both K steps; the planner takes them for small
+    # problems such as 256^3 with D), unsplit, with ragged M: N = 70 on padded
+    # rows (the last, partial column group of a row goes element by element) and
+    # N = 64 on tight ones.
+    M, K = 100, 512
+    region = 64 if path == "i8" else 32
+    for kr in ((1,) if path == "e2m1" else (1, 2)):
+        for N, pad in ((70, 2), (64, 0)):
+            w = synth.make(name, M=M, N=N, K=K)
+            if path == "i8":
+                w.tensors["D"] = synth.int8_uniform(11, M * N).view(M, N).to(torch.int32) * 1000
+                alpha, beta = 3, -2
+            else:
+                w.tensors["D"] = synth.to_storage(synth.uniform(7, M * N, -1, 1), TORCH_OUT[w.out]).view(M, N)
+                alpha, beta = 1.25, 0.5
+            o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=64, force_n_tile=64, force_waves=4,
+                                force_k_tile=region * kr, force_split_k=1)
+            info, st = run(h, w, opts=o, b_colmajor=colm, pad=pad, alpha=alpha, beta=beta)
+            assert info.m_tile == 64 and info.n_tile == 64 and info.split_k == 1 and st["n"] == M * N
+
+
 def test_pad_k(h):
     # K not a multiple of the MFMA depth: the aligned part runs as planned, a tail
     # kernel adds the rest as one more partial slice, the reduction applies the
