@@ -100,15 +100,28 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
             }
         }
     };
-    // two register buffers: batch it+1 streams in while batch it is consumed
+    // two register buffers: batch it+1 streams in while batch it is consumed.
+    // The loop issues both of its loads unconditionally (the last batches are
+    // peeled off below): a load under a branch makes the compiler's wait before
+    // the following batch assume the branch not taken, so that it also waits
+    // for the batch just issued.
     int it = 0;
-    for (; it + 1 < nmain; it += 2) {
+    for (; it + 2 < nmain; it += 2) {
         load_batch(it + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
         fma_batch(it, b0);
-        if (it + 2 < nmain) load_batch(it + 2, b0);
+        load_batch(it + 2, b0);
+        __builtin_amdgcn_sched_barrier(0);
         fma_batch(it + 1, b1);
     }
-    if (it < nmain) fma_batch(it, b0);
+    if (it + 1 < nmain) {
+        load_batch(it + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_batch(it, b0);
+        fma_batch(it + 1, b1);
+    } else if (it < nmain) {
+        fma_batch(it, b0);
+    }
     // the rows after the last full batch (fewer than U per lane): all loaded at
     // once, then added in ascending row order
     {
@@ -216,17 +229,30 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
     };
 
     // two register buffers: step it+1 streams in while step it is consumed
+    // (unconditional loads in the loop, the last steps peeled off, as in the
+    // VALU kernel)
     const int nfull = (kend - kbeg) / 32;
     Tile t0, t1;
     if (nfull > 0) load(kbeg, false, t0);
+    // (sched_barrier: the compiler would otherwise sink each load below the
+    // step before it, and the loop would drain every iteration)
     int it = 0;
-    for (; it + 1 < nfull; it += 2) {
+    for (; it + 2 < nfull; it += 2) {
         load(kbeg + (it + 1) * 32, false, t1);
+        __builtin_amdgcn_sched_barrier(0);
         compute(t0);
-        if (it + 2 < nfull) load(kbeg + (it + 2) * 32, false, t0);
+        load(kbeg + (it + 2) * 32, false, t0);
+        __builtin_amdgcn_sched_barrier(0);
         compute(t1);
     }
-    if (it < nfull) compute(t0);
+    if (it + 1 < nfull) {
+        load(kbeg + (it + 1) * 32, false, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t0);
+        compute(t1);
+    } else if (it < nfull) {
+        compute(t0);
+    }
     const int k0 = kbeg + nfull * 32;
     if (k0 < kend) {   // tail step: rows past the slice are zero
         load(k0, true, t1);
