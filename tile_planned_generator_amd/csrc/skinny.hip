@@ -37,8 +37,10 @@ DG_DEV float elt16(int path, unsigned short h)
 
 // ----------------------------------------------------------------- VALU path
 // Four waves per workgroup, each on its own LPR*8 columns; within a wave,
-// 64/LPR row groups interleave over the K slice and are summed by lane
-// shuffles at the end.  A's slice (MR rows) is staged in LDS.
+// 64/LPR row groups take the K slice's rows U consecutive rows at a time (row
+// group g: rows U*g .. U*g+U-1 of each batch of U*64/LPR rows; the rows after
+// the last full batch interleave) and are summed by lane shuffles at the end.
+// A's slice (MR rows) is staged in LDS.
 constexpr int SKINNY_A_LDS = 32768;   // bytes of A staged per workgroup
 
 template <int PATH, int MR, int LPR>
@@ -61,12 +63,12 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
     const char *Bb = reinterpret_cast<const char *>(p.B) + (int64_t)(col < p.N ? col : 0) * 2 +
                      (int64_t)kbeg * p.ldb * 2;
     const int64_t ldb_b = p.ldb * 2;
-    // batches of U rows per lane (U * RPI rows per wave), then single rows
+    // batches of U consecutive rows per lane (U * RPI rows per wave), then single rows
     const int nmain = L / (U * RPI);
     auto load_batch = [&](int it, u32x4 (&b)[U]) {
-        const int r = g + it * U * RPI;
+        const int r = U * g + it * U * RPI;
 #pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = ld16_nt(Bb + (int64_t)(r + u * RPI) * ldb_b);
+        for (int u = 0; u < U; ++u) b[u] = ld16_nt(Bb + (int64_t)(r + u) * ldb_b);
     };
     // the first batch of B is in flight while A is staged
     u32x4 b0[U], b1[U];
@@ -87,14 +89,14 @@ __global__ void __launch_bounds__(256) skinny_valu_kernel(SkinnyArgs p)
         for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
 
     auto fma_batch = [&](int it, const u32x4 (&b)[U]) {
-        const int r = g + it * U * RPI;
+        const int r = U * g + it * U * RPI;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float w[8];
             unpack8(PATH, b[u], w);
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
-                const float a = elt16(PATH, sA[m * L + r + u * RPI]);
+                const float a = elt16(PATH, sA[m * L + r + u]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[m][e] += a * w[e];
             }
