@@ -205,11 +205,17 @@ __global__ void __launch_bounds__(256) skinny_mfma_kernel(SkinnyArgs p)
     };
     auto load = [&](int k0, bool partial, Tile &t) {
         const int kr = k0 + 8 * kg;
+        // one 64-bit row address per step, then the uniform row pitch per row
+        // (a product per row costs three quarter-rate multiplies per load)
+        const char *rp = Bb + (int64_t)kr * ldb_b;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int k = partial ? min(kr + r, kend - 1) : kr + r;
-            t.b[r] = ld16_nt(Bb + (int64_t)k * ldb_b);
-            if (partial && kr + r >= kend) t.b[r] = u32x4{0, 0, 0, 0};
+            if (partial) {
+                t.b[r] = ld16_nt(Bb + (int64_t)min(kr + r, kend - 1) * ldb_b);
+                if (kr + r >= kend) t.b[r] = u32x4{0, 0, 0, 0};
+            } else {
+                t.b[r] = ld16_nt(rp + r * ldb_b);
+            }
         }
         t.a = ld16(Ab + (int64_t)(partial ? min(kr, kend - 8) : kr) * 2);
         if (partial && kr >= kend) t.a = u32x4{0, 0, 0, 0};
