@@ -608,6 +608,21 @@ def test_full_size_every_output(h, name, col_chunk):
     assert st["n"] == w.M * w.N
 
 
+@pytest.mark.parametrize("name,region", [("i8_4096x4096x4096", 64), ("f16_2048x2048x8192_bias_gelu", 32),
+                                         ("bf16_16x4096x131072", 32)])
+def test_short_k_on_the_16x16_tile(h, name, region):
+    # The eight-wave 16x16 tile over a row-major B reads the next stage's B
+    # fragments during the MFMAs: slices of one, two and three K steps (and a
+    # split whose slices have one step each) take its prologue, its last step
+    # and the steps in between, against the oracle.
+    for steps, split in ((1, 1), (2, 1), (3, 1), (4, 4), (5, 1)):
+        w = synth.make(name, M=300, N=264, K=steps * region)
+        o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=256, force_n_tile=256, force_waves=8,
+                            force_mfma=16, force_split_k=split)
+        info, st = run(h, w, opts=o, pad=8)
+        assert info.mfma_m == 16 and info.split_k == split and st["n"] == w.M * w.N
+
+
 @pytest.mark.parametrize("name,ms", [("i8_4096x4096x4096", 16), ("i8_4096x4096x4096", 32),
                                      ("f16_4096x4096x4096", 16), ("f16_4096x4096x4096", 32),
                                      ("e2m1_4096x4096x4096", 16), ("e2m1_4096x4096x4096", 32)])
