@@ -17,9 +17,11 @@
 //     its LDS reads; the workgroup fence of __syncthreads would wait for every
 //     load.
 //   - A (and a K-contiguous B) is kept as rows of 64 bytes per K region (four
-//     16-byte chunks) whose chunk index is XORed with (row >> 2) & 3, so the 16 rows a
-//     16-lane phase of a fragment read touches hit 16 distinct 16-byte bank
-//     groups of gfx950's 64-bank LDS.
+//     16-byte chunks) whose chunk index is XORed with (row >> 2) & 3 for the
+//     32x32 fragment reads and with (row >> 1) & 3 for the 16x16 ones: with
+//     gfx950's LDS conflict counters, each is free of bank conflicts for its own
+//     read (32 rows x one chunk, or 16 rows x four chunks, per instruction) and
+//     costs the other twice the LDS cycles.
 //   - A row-major B (N contiguous) is kept as it is in memory, K rows of BN
 //     columns, and read with the transposing LDS reads of gfx950
 //     (ds_read_b64_tr_b16 / ds_read_b64_tr_b8): within each group of 16 lanes,
@@ -28,7 +30,10 @@
 //     ..., a+14), so lanes that address 4 (8) consecutive K rows of 4 (8)
 //     neighbouring columns hand every lane the consecutive K values of one
 //     column - the MFMA B operand.  The 16-byte chunks of row k are XORed with
-//     4*(k & 3) (b16) or 2*(k & 7) (b8) so those rows fall into distinct banks.
+//     4*(k & 3) (b16) or 2*(k & 7) (b8) so those rows fall into distinct banks;
+//     the 16x16 reads, whose two half-waves read K rows 8 (b16) or 16 (b8)
+//     apart, also take bit 3 (b16, as 2) or bit 4 (b8, as 1) of k, without which
+//     the half-waves collide (measured: twice the LDS cycles).
 //     These reads are issued from inline assembly: the compiler treats its own
 //     transposing-read builtins as possibly aliasing every in-flight
 //     direct-to-LDS load and would wait for all of them before each read.  Their
@@ -185,6 +190,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int STAGE = A_ALL + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
     constexpr int CPR = RB / 16;               // 16-byte chunks per such row
+    // chunk swizzles (see the header): 64-byte rows of A and of a K-major B,
+    // and K rows of a row-major B
+    auto rsw = [](int r) { return M16 ? (r >> 1) & 3 : (r >> 2) & 3; };
+    auto ksw = [](int k) {
+        return IS_I8 ? ((2 * (k & 7)) | (M16 ? (k >> 4) & 1 : 0)) % CPR
+                     : ((4 * (k & 3)) | (M16 ? 2 * ((k >> 3) & 1) : 0)) % CPR;
+    };
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     constexpr int LDS_BYTES = tiled_lds_bytes(PATH, BM, BN, WM, WN, KR);
     static_assert(STAGE == tiled_stage_bytes(PATH, BM, BN, KR), "stage size");
@@ -291,7 +303,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     for (int i = 0; i < A_LD; ++i) {
         const int pc0 = (i * NW + wave) * 64 + lane;
         const int reg = pc0 / (BM * 4), pc = pc0 % (BM * 4);
-        const int r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
+        const int r = pc >> 2, c = (pc & 3) ^ rsw(r);
         oa[i] = reg * 64 + r * lda_b + c * 16;
     }
     uint32_t ob[B_LD];
@@ -302,12 +314,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             ob[i] = pc * ldb_b;
         } else if constexpr (BKMAJ) {       // as A, rows are columns of B (region reg: k + 64 bytes * reg)
             const int reg = pc / (BN * 4), q = pc % (BN * 4);
-            const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+            const int r = q >> 2, c = (q & 3) ^ rsw(r);
             ob[i] = reg * 64 + r * ldb_b + c * 16;
         } else {                            // K rows of BN columns
             const int k = pc / CPR, pcol = pc % CPR;
-            const int sw = IS_I8 ? (2 * (k & 7)) % CPR : (4 * (k & 3)) % CPR;
-            ob[i] = k * ldb_b + (pcol ^ sw) * 16;
+            ob[i] = k * ldb_b + (pcol ^ ksw(k)) * 16;
         }
     }
     const int swave = NW - 1 - wave;        // scale loads go from the last wave down
@@ -425,11 +436,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 if constexpr (!IS_I8) {
                     const int col = col0 + (M16 ? 0 : 16 * (grp16 & 1)) + 4 * (L16 & 3);
                     const int k = (M16 ? 8 * grp16 : 8 * (grp16 >> 1)) + (L16 >> 2);
-                    o = A_ALL + k * RB + (((col >> 3) ^ ((4 * (k & 3)) % CPR)) << 4) + (col & 7) * 2;
+                    o = A_ALL + k * RB + (((col >> 3) ^ ksw(k)) << 4) + (col & 7) * 2;
                 } else {
                     const int col = col0 + (M16 ? 0 : 16 * (grp16 & 1)) + 8 * (L16 & 1);
                     const int k = (M16 ? 16 * grp16 : 16 * (grp16 >> 1)) + (L16 >> 1);
-                    o = A_ALL + k * RB + (((col >> 4) ^ ((2 * (k & 7)) % CPR)) << 4) + (col & 15);
+                    o = A_ALL + k * RB + (((col >> 4) ^ ksw(k)) << 4) + (col & 15);
                 }
             }
             boff[ni * (M16 ? 2 : 1) + sn] = o;
@@ -453,14 +464,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // GPU with one-hot operands).  So the lane reads chunks kg and kg+2.
             // The lane's scale is byte `row` of the chunk of group 2s + kg.
             const char *rA = sA + s * A_BYTES + row * 64;
-            const int sw = (row >> 2) & 3;
+            const int sw = rsw(row);
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(rA + ((kg ^ sw) << 4));
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
         } else {
             f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + (s >> 1) * A_BYTES + row * 64 +
-                                                        ((c ^ ((row >> 2) & 3)) << 4));
+                                                        ((c ^ rsw(row)) << 4));
         }
     };
     auto read_b = [&](int buf, auto s_tag, int ni, Frag &f, int g) {
@@ -491,7 +502,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // (MX: chunk 2s + kg holds the 32 codes of k 64s + 32kg .. +31)
             const int row = col0 + lr;
             f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + (IS_MX ? 0 : (s >> 1) * B_REG) + row * 64 +
-                                                        ((c ^ ((row >> 2) & 3)) << 4));
+                                                        ((c ^ rsw(row)) << 4));
             if constexpr (IS_MX)
                 f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
         } else {
@@ -578,7 +589,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     auto read_a16 = [&](int buf, int h, int mi, Frag16 &f) {
         const char *sA = smem + buf * STAGE;
         const int r16 = wm * WTM + mi * 32 + 16 * h + L16;
-        const int sw = (r16 >> 2) & 3;
+        const int sw = rsw(r16);
         if constexpr (IS_MX) {
             // 16x16x128 block-scaled MFMA: the 8-bit operand of lane group g
             // holds k 16g .. +15 in its first four registers and k 64 + 16g ..
@@ -606,10 +617,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         } else if constexpr (IS_MX) {
             // the 4-bit operand of lane group g holds k 32g .. +31 of the step:
             // chunk g of the column's 64 bytes, and the column's scale of group g
-            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
+            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ rsw(row)) << 4));
             f.sb[h][ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + grp16 * 256 + row);
         } else if constexpr (BKMAJ) {
-            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ ((row >> 2) & 3)) << 4));
+            f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ rsw(row)) << 4));
         } else {
             // transposing reads, this half's own lane offsets; K rows from 0
             const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[2 * ni + h];
