@@ -124,7 +124,7 @@ constexpr double tiled_step_efficiency(int path, int bm, int bn, int waves, int 
 // chunk per operand and group of the step).
 constexpr int tiled_stage_bytes(int path, int bm, int bn, int kr = 1)
 {
-    return path == 4 ? bm * 128 + bn * 64 + 2048
+    return path == 4 ? bm * 128 + bn * 64 + 2304
          : (path == 3 ? bm * 64 + bn * 16 + (bn * 2 + 255) / 256 * 256 : kr * (bm * 64 + bn * 64));
 }
 // LDS stages: five for the eight-wave variants when they fit gfx950's 160 KB

@@ -184,8 +184,12 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     constexpr int B_TILE = KR * B_REG;
     // scales: e2m1 one fp16 per column (whole 256-byte loads); MX, per operand
     // and group of the step, one byte per row of A (column of B) in a 256-byte
-    // chunk: [A g0..g3][B g0..g3]
-    constexpr int S_BYTES = IS_E2M1 ? (BN * 2 + 255) / 256 * 256 : (IS_MX ? 2048 : 0);
+    // chunk: [A g0..g3][B g0..g3], the chunks SBS bytes apart.  The 16x16
+    // reads take the four groups' chunks at once (one per lane group): 256
+    // bytes apart, their bytes of one row share a bank; 272 apart they do not
+    // (measured with the LDS conflict counters).
+    constexpr int SBS = IS_MX && M16 ? 272 : 256;
+    constexpr int S_BYTES = IS_E2M1 ? (BN * 2 + 255) / 256 * 256 : (IS_MX ? 2304 : 0);
     static_assert(!IS_MX || (BM <= 256 && BN <= 256), "MX scale chunks hold 256 rows");
     constexpr int STAGE = A_ALL + B_TILE + S_BYTES;
     constexpr int RB = BN * ESZ;               // bytes per K row of a row-major B tile
@@ -204,8 +208,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     // direct-to-LDS loads: a 16-byte load fills 1 KB (64 lanes), a dword load 256 B.
     // Load i of an operand is issued by wave i % NW (the scale loads from the
     // last wave down, to even out the per-wave counts).
-    constexpr int A_NL = A_ALL / 1024, B_NL = B_TILE / 1024, S_NL = S_BYTES / 256;
-    static_assert(A_NL * 1024 == A_ALL && B_NL * 1024 == B_TILE && S_NL * 256 == S_BYTES,
+    constexpr int A_NL = A_ALL / 1024, B_NL = B_TILE / 1024, S_NL = IS_MX ? 8 : S_BYTES / 256;
+    static_assert(A_NL * 1024 == A_ALL && B_NL * 1024 == B_TILE &&
+                      (IS_MX ? (S_NL - 1) * SBS + 256 <= S_BYTES : S_NL * 256 == S_BYTES),
                   "tile not whole loads");
     constexpr int A_LD = (A_NL + NW - 1) / NW, B_LD = (B_NL + NW - 1) / NW, S_LD = (S_NL + NW - 1) / NW;
     constexpr int LPS = tiled_min_loads_per_wave(A_NL, B_NL, S_NL, NW);   // fewest loads a wave issues per stage
@@ -366,7 +371,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 const __amdgpu_buffer_rsrc_t rS =
                     make_rsrc(rows ? SAbase : Sbase, real ? (rows ? sa_bytes : s_bytes) : 0u);
                 buf_ld4_lds(rS, os[q] + (uint32_t)(k0 >> 5) * (uint32_t)(rows ? p.ld_scale_a : p.ld_scale),
-                            sb + A_ALL + B_TILE + (q * NW + swave) * 256);
+                            sb + A_ALL + B_TILE + (q * NW + swave) * SBS);
             }
         } else if constexpr (IS_E2M1) {
             const int q = i - A_LD - B_LD;
@@ -468,7 +473,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(rA + ((kg ^ sw) << 4));
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(rA + (((kg + 2) ^ sw) << 4));
             f.a[mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * 256 + row);
+            f.sa[mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + (2 * s + kg) * SBS + row);
         } else {
             f.a[mi] = *reinterpret_cast<const u32x4 *>(sA + (s >> 1) * A_BYTES + row * 64 +
                                                         ((c ^ rsw(row)) << 4));
@@ -504,7 +509,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             f.b[ni] = *reinterpret_cast<const u32x4 *>(sB + (IS_MX ? 0 : (s >> 1) * B_REG) + row * 64 +
                                                         ((c ^ rsw(row)) << 4));
             if constexpr (IS_MX)
-                f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + (2 * s + kg) * 256 + row);
+                f.sb[ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 4 * SBS + (2 * s + kg) * SBS + row);
         } else {
             const uint32_t a = lds0 + (uint32_t)buf * STAGE + boff[M16 ? 2 * ni : ni];
             u32x2 lo, hi;
@@ -600,7 +605,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(sA + A_BYTES + r16 * 64 + ((grp16 ^ sw) << 4));
             f.a[h][mi] = AFrag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            f.sa[h][mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + grp16 * 256 + r16);
+            f.sa[h][mi] = *reinterpret_cast<const unsigned char *>(sA + A_ALL + B_TILE + grp16 * SBS + r16);
         } else {
             f.a[h][mi] = *reinterpret_cast<const u32x4 *>(sA + r16 * 64 + ((grp16 ^ sw) << 4));
         }
@@ -618,7 +623,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // the 4-bit operand of lane group g holds k 32g .. +31 of the step:
             // chunk g of the column's 64 bytes, and the column's scale of group g
             f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ rsw(row)) << 4));
-            f.sb[h][ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 1024 + grp16 * 256 + row);
+            f.sb[h][ni] = *reinterpret_cast<const unsigned char *>(sB + B_TILE + 4 * SBS + grp16 * SBS + row);
         } else if constexpr (BKMAJ) {
             f.b[h][ni] = *reinterpret_cast<const u32x4 *>(sB + row * 64 + ((grp16 ^ rsw(row)) << 4));
         } else {
