@@ -784,166 +784,67 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             }
         };
         constexpr int AHEAD = NBUF - 1;   // stages issued before the loop
-        // 16x16 MFMAs over a row-major B (transposing reads, the slower LDS
-        // reads) with at least four stages: the B fragments of stage st+1 are
-        // read during the compute phase of step st, between its MFMAs, into a
-        // second set of B registers (copied in at the next memory phase), so
-        // that the memory phase reads only A.  Stage st+1 must then have landed
-        // for every wave by the barrier before that compute phase: the memory
-        // phase of step st waits for this wave's loads of stage st+2 (not st+1),
-        // leaving NBUF-3 stages in flight, and the waits of the second group,
-        // one phase behind, still come before that barrier.  (Where B's reads
-        // are plain 16-byte or e2m1 code reads, the stage of lookahead this
-        // costs outweighs what it saves.)
-        constexpr bool EARLY_B = M16 && NBUF >= 4 && B_TR;
-        if constexpr (EARLY_B) {
 #pragma unroll
-            for (int j = 0; j < AHEAD; ++j) load_stage(j);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 2) * LPS, 15));   // stages 0 and 1
-            bar();
-            if (lag) bar();
-            constexpr int NM = 4 * FM * FN;   // MFMAs per step
-            Frag16 fr;
-            u32x4 nb[2][FN];   // the B fragments of the next stage
-            auto read_next_b = [&](int buf, int h, int ni) {
-                Frag16 tmp;
-                read_b16(buf, h, ni, tmp);
-                nb[h][ni] = tmp.b[h][ni];
-            };
-            // the transposing reads are assembly, invisible to the compiler's
-            // waits: wait for them before anything touches nb
-            auto tie_next_b = [&] {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int ni = 0; ni < FN; ++ni) asm volatile("" : "+v"(nb[h][ni]) : : "memory");
-            };
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int ni = 0; ni < FN; ++ni) read_next_b(0, h, ni);
-            tie_next_b();
-            auto estep = [&](int st, auto last_tag) {
-                constexpr bool LAST = decltype(last_tag)::value;
-                const int buf = st % NBUF;
-                // memory phase: the A fragments of stage st, the loads of stage
-                // st+NBUF-1 between them, B from the registers read ahead
-#pragma unroll
-                for (int mi = 0; mi < FM; ++mi) read_a16(buf, 0, mi, fr);
+        for (int j = 0; j < AHEAD; ++j) load_stage(j);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
+        bar();
+        if (lag) bar();
+        // One step; the last one (LAST) issues no loads and masks its second
+        // substep when it is a half step.
+        Frag16 fr;   // (16x16 MFMAs)
+        auto step = [&](int st, auto last_tag) {
+            constexpr bool LAST = decltype(last_tag)::value;
+            const int buf = st % NBUF;
+            // memory phase: the fragment reads of stage st, with the loads of
+            // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
+            // to different units)
+            if constexpr (M16) {
+                read_frag16(buf, 0, fr);
                 if constexpr (!LAST) load_stage(st + AHEAD, 0);
-#pragma unroll
-                for (int mi = 0; mi < FM; ++mi) read_a16(buf, 1, mi, fr);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int ni = 0; ni < FN; ++ni) fr.b[h][ni] = nb[h][ni];
-                if constexpr (!LAST) {
-                    load_stage(st + AHEAD, 1);
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 2) * LPS, 0));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-                    keep16(fr, nfull == nsteps);
-                }
-                bar();
-                // compute phase: the MFMAs of stage st; after MFMAs 0, 2, 4, ...
-                // one B fragment of stage st+1 (both transposing reads)
-                __builtin_amdgcn_s_setprio(1);
-                const int nbuf = (st + 1) % NBUF;
-#pragma unroll
-                for (int q = 0; q < NM; ++q) {
-                    mfma16(fr, q);
-                    // (the order is fixed: the reads early, their wait last)
-                    __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (!LAST) {
-                        if (q % 2 == 0 && q / 2 < 2 * FN) read_next_b(nbuf, (q / 2) / FN, (q / 2) % FN);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if constexpr (!LAST) {
-                    // the A fragments stay allocated to the end of the phase, so
-                    // that no transposing read (whose late register write the
-                    // compiler does not see) lands in an MFMA operand
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int mi = 0; mi < FM; ++mi) asm volatile("" : : "v"(fr.a[h][mi]));
-                    tie_next_b();
-                }
-                __builtin_amdgcn_s_setprio(0);
-                bar();
-            };
-            if (clk_on) {
-                ck1 = __builtin_amdgcn_s_memtime();
-                rt1 = __builtin_amdgcn_s_memrealtime();
+                read_frag16(buf, 1, fr);
+                if constexpr (!LAST) load_stage(st + AHEAD, 1);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
+                tie16(fr);
+                if constexpr (LAST) keep16(fr, nfull == nsteps);
+            } else {
+                read_frag(buf, S0{}, f0, g0 + st);
+                if constexpr (!LAST) load_stage(st + AHEAD, 0);
+                read_frag(buf, S1{}, f1, g0 + st);
+                if constexpr (!LAST) load_stage(st + AHEAD, 1);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
+                tie(f0);
+                tie(f1);
+                if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
             }
-            for (int st = 0; st < nsteps - 1; ++st) estep(st, std::false_type{});
-            estep(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
-            if (!lag) bar();
-        } else {
-            constexpr int AHEAD = NBUF - 1;   // stages issued before the loop
-    #pragma unroll
-            for (int j = 0; j < AHEAD; ++j) load_stage(j);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
             bar();
-            if (lag) bar();
-            // One step; the last one (LAST) issues no loads and masks its second
-            // substep when it is a half step.
-            Frag16 fr;   // (16x16 MFMAs)
-            auto step = [&](int st, auto last_tag) {
-                constexpr bool LAST = decltype(last_tag)::value;
-                const int buf = st % NBUF;
-                // memory phase: the fragment reads of stage st, with the loads of
-                // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
-                // to different units)
-                if constexpr (M16) {
-                    read_frag16(buf, 0, fr);
-                    if constexpr (!LAST) load_stage(st + AHEAD, 0);
-                    read_frag16(buf, 1, fr);
-                    if constexpr (!LAST) load_stage(st + AHEAD, 1);
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
-                    tie16(fr);
-                    if constexpr (LAST) keep16(fr, nfull == nsteps);
-                } else {
-                    read_frag(buf, S0{}, f0, g0 + st);
-                    if constexpr (!LAST) load_stage(st + AHEAD, 0);
-                    read_frag(buf, S1{}, f1, g0 + st);
-                    if constexpr (!LAST) load_stage(st + AHEAD, 1);
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
-                    tie(f0);
-                    tie(f1);
-                    if constexpr (LAST) keep_if(f1, nfull == nsteps);   // a final half step adds 0 x 0
-                }
-                bar();
-                // compute phase, at raised wave priority so that the SIMD's other
-                // wave (in its memory phase) does not delay the MFMA issue
-                __builtin_amdgcn_s_setprio(1);
-                if constexpr (M16) {
-                    decode_b16(fr);
-                    mfmas16(fr);
-                } else {
-                    decode_b(f0);
-                    mfmas(f0);
-                    decode_b(f1);
-                    mfmas(f1);
-                }
-                __builtin_amdgcn_s_setprio(0);
-                bar();
-            };
-            if (clk_on) {
-                ck1 = __builtin_amdgcn_s_memtime();
-                rt1 = __builtin_amdgcn_s_memrealtime();
+            // compute phase, at raised wave priority so that the SIMD's other
+            // wave (in its memory phase) does not delay the MFMA issue
+            __builtin_amdgcn_s_setprio(1);
+            if constexpr (M16) {
+                decode_b16(fr);
+                mfmas16(fr);
+            } else {
+                decode_b(f0);
+                mfmas(f0);
+                decode_b(f1);
+                mfmas(f1);
             }
-            for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
-            // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
-            step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
-            // (every fragment read in this loop is consumed in its own step; settling
-            // here keeps the rule that no transposing read is left in flight)
-            settle(f0);
-            settle(f1);
-            settle16(fr);
-            if (!lag) bar();
+            __builtin_amdgcn_s_setprio(0);
+            bar();
+        };
+        if (clk_on) {
+            ck1 = __builtin_amdgcn_s_memtime();
+            rt1 = __builtin_amdgcn_s_memrealtime();
         }
+        for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
+        // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
+        step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
+        // (every fragment read in this loop is consumed in its own step; settling
+        // here keeps the rule that no transposing read is left in flight)
+        settle(f0);
+        settle(f1);
+        settle16(fr);
+        if (!lag) bar();
     } else {
         // Four waves, one per SIMD: each wave hides its own LDS reads and buffer
         // loads behind its MFMAs, so the instruction order is fixed by hand
