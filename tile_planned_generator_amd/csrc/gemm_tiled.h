@@ -944,6 +944,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     const int col = n0 + wn * WTN + ec;
     const bool vec_col = vec_ok && col + 3 < N;
     const int mode = p.split_k > 1 ? 0 : (p.epi.d_read || p.epi.kind != E_NONE ? 2 : 1);
+    // A plain 16-bit C (alpha * acc; no D, bias or activation) goes eight
+    // columns per lane, one 16-byte store each, rather than four (8 bytes).
+    constexpr int LPR8 = WTN / 8, RPI8 = 64 / LPR8, NIT8 = 32 / RPI8;
+    constexpr int EB8 = NIT8 < 4 ? NIT8 : 4;
+    static_assert(LPR8 * 8 == WTN && RPI8 * LPR8 == 64 && NIT8 * RPI8 == 32, "eight-column rows");
+    const int er8 = lane / LPR8, ec8 = (lane % LPR8) * 8;
+    const int col8 = n0 + wn * WTN + ec8;
+    const bool wide16 = !IS_I8 && mode == 1 && p.epi.out_type != T_F32;
+    const bool vec8 = aligned_to(p.epi.C, 16) && (p.epi.ldc & 7) == 0 && col8 + 7 < N;
     floatx4 bias4 = floatx4{0.f, 0.f, 0.f, 0.f};
     if (vec_col && p.split_k == 1) {
         if constexpr (IS_I8) bias4 = epi_bias4_i(p.epi, col);
@@ -1069,11 +1078,43 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 }
             }
         };
+        bool done = false;
+        if constexpr (!IS_I8) {
+            if (wide16) {
 #pragma unroll 1
-        for (int it0 = 0; it0 < NIT; it0 += EB) {
-            if (mode == 0) batch(std::integral_constant<int, 0>{}, it0);
-            else if (mode == 1) batch(std::integral_constant<int, 1>{}, it0);
-            else batch(std::integral_constant<int, 2>{}, it0);
+                for (int it0 = 0; it0 < NIT8; it0 += EB8) {
+                    floatx4 x[EB8][2];
+#pragma unroll
+                    for (int u = 0; u < EB8; ++u) {
+                        const float *src = sE + ((it0 + u) * RPI8 + er8) * RP + ec8;
+                        x[u][0] = *reinterpret_cast<const floatx4 *>(src);
+                        x[u][1] = *reinterpret_cast<const floatx4 *>(src + 4);
+                    }
+#pragma unroll
+                    for (int u = 0; u < EB8; ++u) {
+                        const int row = row0 + (it0 + u) * RPI8 + er8;
+                        if (row >= M) continue;
+                        const floatx4 lo = p.epi.alpha * x[u][0], hi = p.epi.alpha * x[u][1];
+                        const int64_t c0 = (int64_t)row * p.epi.ldc + col8;
+                        if (vec8) {
+                            store8_f16x(p.epi.C, p.epi.out_type, c0, lo, hi);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (col8 + e < N) store_f32(p.epi.C, p.epi.out_type, c0 + e, e < 4 ? lo[e] : hi[e - 4]);
+                        }
+                    }
+                }
+                done = true;
+            }
+        }
+        if (!done) {
+#pragma unroll 1
+            for (int it0 = 0; it0 < NIT; it0 += EB) {
+                if (mode == 0) batch(std::integral_constant<int, 0>{}, it0);
+                else if (mode == 1) batch(std::integral_constant<int, 1>{}, it0);
+                else batch(std::integral_constant<int, 2>{}, it0);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

@@ -192,6 +192,21 @@ DG_DEV void store4_f32(void *p, int type, int64_t idx, floatx4 v)
         __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(p) + idx));
 }
 
+// Eight values to a 16-bit output (type T_F16 or T_BF16), nearest even, as one
+// 16-byte store: idx a multiple of 8, p 16-byte aligned.
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+DG_DEV void store8_f16x(void *p, int type, int64_t idx, floatx4 lo, floatx4 hi)
+{
+    if (type == T_F16)
+        __builtin_nontemporal_store(half8{(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                                          (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w},
+                                    reinterpret_cast<half8 *>(reinterpret_cast<_Float16 *>(p) + idx));
+    else
+        __builtin_nontemporal_store(bf16x8v{(__bf16)lo.x, (__bf16)lo.y, (__bf16)lo.z, (__bf16)lo.w,
+                                            (__bf16)hi.x, (__bf16)hi.y, (__bf16)hi.z, (__bf16)hi.w},
+                                    reinterpret_cast<bf16x8v *>(reinterpret_cast<__bf16 *>(p) + idx));
+}
+
 // epi_store_f on four consecutive columns j .. j+3 (the same arithmetic per
 // element), on values already loaded: d holds D's four values (used when D is
 // read), b the bias's four values (used by the bias kinds).
