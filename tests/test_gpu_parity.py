@@ -74,11 +74,14 @@ def _chunks(n, size):
 
 
 def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, rows=None,
-        cols=None, requant_scale=1.0, rq_bias=None, alpha=None, beta=None, col_chunk=0):
+        cols=None, requant_scale=1.0, rq_bias=None, alpha=None, beta=None, col_chunk=0,
+        c_ld=None, c_off=0):
     """Run workload ``w`` through dg_gemm and check it against the oracle on
     rows x cols (all by default; the oracle runs on column blocks of
     ``col_chunk`` columns when it is given, which bounds its binary64 copy of B).
     The output's row padding and a few rows past M are checked untouched.
+    c_ld / c_off: C's leading dimension and its first element's offset (in
+    elements) in its buffer, whose elements before C must stay untouched too.
     Returns (plan info, error stats)."""
     t = w.tensors
     M, N, K = w.M, w.N, w.K
@@ -100,7 +103,14 @@ def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, ro
     else:
         Bd = to_dev(t["B"], pad)
         layout = dg.DG_ROW_MAJOR
-    Cd, Cbuf = guarded_out(M, N, TORCH_OUT[out], pad)
+    if c_ld is None and not c_off:
+        Cd, Cbuf = guarded_out(M, N, TORCH_OUT[out], pad)
+        head = None
+    else:
+        ld = c_ld or N
+        flat = torch.full((c_off + (M + GUARD_ROWS) * ld,), SENTINEL, dtype=TORCH_OUT[out], device=DEV)
+        Cbuf = flat[c_off:].view(M + GUARD_ROWS, ld)
+        Cd, head = Cbuf[:M, :N], flat[:c_off]
     D = to_dev(t["D"], pad) if "D" in t and beta != 0 else None
     bias = t.get("bias")
     if epilogue in ("requant_i8", "requant_f16"):
@@ -111,6 +121,8 @@ def run(h, w, *, b_colmajor=False, pad=0, opts=None, out=None, epilogue=None, ro
     torch.cuda.synchronize()
     say(f"       plan {info.kernel_name.decode()} S={info.split_k} tile={info.m_tile}x{info.n_tile}")
     check_guards(Cbuf, M, N)
+    if head is not None:
+        assert bool((head.cpu() == SENTINEL).all()), "elements before C were written"
     del A, Bd, scale
 
     r_idx = torch.arange(M) if rows is None else torch.as_tensor(rows)
@@ -294,6 +306,22 @@ def test_f16_alpha_beta_d_full_size(h):
 def test_f16_alpha_beta_d_ragged(h, M, N, K, pad):
     # pad makes the row pitch a multiple of 8 elements (16 bytes)
     run(h, synth.make("f16_256x256x256_alpha_beta_d", M=M, N=N, K=K), pad=pad)
+
+
+@pytest.mark.parametrize("name", ["f16_4096x4096x4096", "bf16_16x4096x131072"])
+@pytest.mark.parametrize("tile", [(256, 256, 8, 16), (64, 64, 4, 32)])
+@pytest.mark.parametrize("c_ld,c_off", [(268, 0), (264, 4), (265, 1)])
+def test_16bit_c_pitch_and_alignment(h, name, tile, c_ld, c_off):
+    # A plain 16-bit C goes eight columns per 16-byte store when its pitch is a
+    # multiple of 8 elements and it is 16-byte aligned; a pitch of 4 mod 8, a
+    # C 8 bytes past a 16-byte boundary, and an odd pitch with a 2-byte
+    # aligned C take the element-wise stores (N = 264 is a whole number of
+    # 8-column pieces, so only the pitch or the alignment decides)
+    bm, bn, waves, ms = tile
+    w = synth.make(name, M=300, N=264, K=512)
+    o = dg.dg_plan_opts(force_path=dg.DG_PATH_TILED, force_m_tile=bm, force_n_tile=bn, force_waves=waves,
+                        force_mfma=ms, force_split_k=1)
+    run(h, w, opts=o, alpha=0.75, c_ld=c_ld, c_off=c_off)
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 640), (300, 200, 96), (129, 257, 4160)])
