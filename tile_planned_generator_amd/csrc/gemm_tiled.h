@@ -661,18 +661,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             tie16(f);
         }
     };
-    auto decode_b16 = [&](Frag16 &f) {
-        if constexpr (IS_E2M1) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int ni = 0; ni < FN; ++ni) {
-                    const unsigned codes = f.b[h][ni].x;
-                    const unsigned short sh = (unsigned short)f.b[h][ni].y;
-                    f.b[h][ni] = __builtin_bit_cast(u32x4, decode_e2m1x8(codes, __builtin_bit_cast(_Float16, sh)));
-                }
-        }
-    };
     // A final half step (keep false): the lanes holding k past its first half
     // (lane groups 2 and 3; for MX the upper halves of the 8-bit operands and
     // the 4-bit operands of lane groups 2 and 3, whose scales become 127, a
@@ -728,6 +716,53 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
     auto mfmas16 = [&](const Frag16 &f) {
 #pragma unroll
         for (int q = 0; q < 4 * FM * FN; ++q) mfma16(f, q);
+    };
+    // e2m1: the compute phase decodes the B blocks one at a time, in four
+    // pieces of two instructions (two conversions, or two fp16 products with
+    // the scale: the arithmetic of decode_e2m1x8), each piece of block b+1
+    // after one of block b's MFMAs.  Only block 0's decode precedes the first
+    // MFMA; written as one run of decodes, all of them did.
+    auto mfmas16_e2m1 = [&](Frag16 &f) {
+        constexpr int NB = 2 * FN, NA = 2 * FM;
+        half2v hv[4];
+        half2v s2;
+        auto piece = [&](auto b_tag, auto k_tag) {
+            constexpr int b = decltype(b_tag)::value, k = decltype(k_tag)::value;
+            constexpr int sn = b & 1, ni = b >> 1;
+            const unsigned codes = f.b[sn][ni].x;
+            if constexpr (k == 0) {
+                const _Float16 sc = __builtin_bit_cast(_Float16, (unsigned short)f.b[sn][ni].y);
+                s2 = half2v{sc, sc};
+                hv[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+                hv[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+            } else if constexpr (k == 1) {
+                hv[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+                hv[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+            } else if constexpr (k == 2) {
+                hv[0] = hv[0] * s2;
+                hv[1] = hv[1] * s2;
+            } else {
+                hv[2] = hv[2] * s2;
+                hv[3] = hv[3] * s2;
+                f.b[sn][ni] = u32x4{__builtin_bit_cast(unsigned, hv[0]), __builtin_bit_cast(unsigned, hv[1]),
+                                    __builtin_bit_cast(unsigned, hv[2]), __builtin_bit_cast(unsigned, hv[3])};
+            }
+        };
+        static_for<4>([&](auto k_tag) { piece(std::integral_constant<int, 0>{}, k_tag); });
+        static_for<NB>([&](auto b_tag) {
+            constexpr int b = decltype(b_tag)::value;
+            static_for<NA>([&](auto a_tag) {
+                constexpr int a = decltype(a_tag)::value;
+                constexpr int sm = a & 1, mi = a >> 1, sn = b & 1, ni = b >> 1;
+                __builtin_amdgcn_sched_barrier(0);
+                mfma16(f, ((mi * 2 + sm) * FN + ni) * 2 + sn);
+                if constexpr (b + 1 < NB && a < 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    piece(std::integral_constant<int, b + 1>{}, a_tag);
+                }
+            });
+        });
+        __builtin_amdgcn_sched_barrier(0);
     };
     // A final half step runs its second substep on zeroed fragments (0 x 0 adds
     // nothing): the fragments are ANDed with a uniform mask, so the loop body has
@@ -820,8 +855,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // compute phase, at raised wave priority so that the SIMD's other
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
-            if constexpr (M16) {
-                decode_b16(fr);
+            if constexpr (M16 && IS_E2M1) {
+                mfmas16_e2m1(fr);
+            } else if constexpr (M16) {
                 mfmas16(fr);
             } else {
                 decode_b(f0);
