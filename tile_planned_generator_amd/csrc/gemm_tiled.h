@@ -838,9 +838,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                 if constexpr (!LAST) load_stage(st + AHEAD, 0);
                 read_frag16(buf, 1, fr);
                 if constexpr (!LAST) load_stage(st + AHEAD, 1);
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 0));
-                tie16(fr);
-                if constexpr (LAST) keep16(fr, nfull == nsteps);
+                // only the direct loads are waited for before the barrier: the
+                // fragment reads land while the other group's last MFMAs run,
+                // and are waited for at the start of the compute phase (stage
+                // st's buffer is refilled only after the next barrier)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
             } else {
                 read_frag(buf, S0{}, f0, g0 + st);
                 if constexpr (!LAST) load_stage(st + AHEAD, 0);
@@ -855,6 +857,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // compute phase, at raised wave priority so that the SIMD's other
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
+            if constexpr (M16) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+                tie16(fr);
+                if constexpr (LAST) keep16(fr, nfull == nsteps);
+            }
             if constexpr (M16 && IS_E2M1) {
                 mfmas16_e2m1(fr);
             } else if constexpr (M16) {
