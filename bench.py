@@ -268,11 +268,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def tiled_source_hash():
+    """Hash of the tiled kernel's code: its sources with comments and
+    whitespace runs removed, so that a comment edit keeps the recorded
+    counters while any change to the code drops them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TILED_SOURCES:
-        with open(os.path.join(ROOT, "tile_planned_generator_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tile_planned_generator_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

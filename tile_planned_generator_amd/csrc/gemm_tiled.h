@@ -41,8 +41,9 @@
 //   - e2m1 codes are staged packed (two per byte), 16 bytes per column and step,
 //     with the column's fp16 group scale (the step's scales are contiguous in
 //     the group-major scale array: whole-dword loads), and decoded to fp16
-//     when the fragment is read (v_cvt_scalef32_pk_f16_fp4 with a unit scale,
-//     then a packed fp16 multiply by the group scale).
+//     (v_cvt_scalef32_pk_f16_fp4 with a unit scale, then a packed fp16 multiply
+//     by the group scale) before the MFMAs that take them: per substep with
+//     32x32 blocks, and block by block between the MFMAs with 16x16 ones.
 //   - MX (fp8 e4m3 A, e2m1 B, one e8m0 scale per 32 k on each): the operands
 //     go to the block-scaled MFMA as stored, without decoding.  A step is 128 k:
 //     two 64-byte fp8 rows per tile row (k 0-63 and 64-127 of the step, each
@@ -63,8 +64,9 @@
 //     DeepGEMM article, kwkr.cn, section 2.2, first layer).
 //   - The epilogue (alpha, beta*D, bias, GELU, requantise, conversion) runs once
 //     per output element after the K loop, four columns per lane with vector
-//     loads and stores; with a K split the raw fp32 / int32 partials go to the
-//     workspace and a reduce kernel applies the epilogue.
+//     loads and stores (eight, one 16-byte store, for a plain 16-bit C); with a
+//     K split the raw fp32 / int32 partials go to the workspace and a reduce
+//     kernel applies the epilogue.
 // Tiles are visited in a grouped order and every XCD gets a contiguous run of
 // them, so tiles that share rows of A or columns of B share an L2.
 #pragma once
