@@ -755,7 +755,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             constexpr int b = decltype(b_tag)::value;
             static_for<NA>([&](auto a_tag) {
                 constexpr int a = decltype(a_tag)::value;
-                constexpr int sm = a & 1, mi = a >> 1, sn = b & 1, ni = b >> 1;
+                constexpr int sm = a / FM, mi = a % FM, sn = b & 1, ni = b >> 1;   // A rows of half 0 first
                 __builtin_amdgcn_sched_barrier(0);
                 mfma16(f, ((mi * 2 + sm) * FN + ni) * 2 + sn);
                 if constexpr (b + 1 < NB && a < 4) {
@@ -835,7 +835,21 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // memory phase: the fragment reads of stage st, with the loads of
             // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
             // to different units)
-            if constexpr (M16) {
+            if constexpr (M16 && IS_E2M1) {
+                // the code words and scales first: block 0's decode and the
+                // first MFMAs need them before the later A rows
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ni = 0; ni < FN; ++ni) read_b16(buf, h, ni, fr);
+#pragma unroll
+                for (int mi = 0; mi < FM; ++mi) read_a16(buf, 0, mi, fr);
+                if constexpr (!LAST) load_stage(st + AHEAD, 0);
+#pragma unroll
+                for (int mi = 0; mi < FM; ++mi) read_a16(buf, 1, mi, fr);
+                if constexpr (!LAST) load_stage(st + AHEAD, 1);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
+            } else if constexpr (M16) {
                 read_frag16(buf, 0, fr);
                 if constexpr (!LAST) load_stage(st + AHEAD, 0);
                 read_frag16(buf, 1, fr);
@@ -860,7 +874,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
             if constexpr (M16) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+                // (reads the compiler cannot see, the transposing ones, are
+                // waited for here; it waits for its own ones where they are used)
+                if constexpr (B_TR) __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
                 tie16(fr);
                 if constexpr (LAST) keep16(fr, nfull == nsteps);
             }
@@ -881,6 +897,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             ck1 = __builtin_amdgcn_s_memtime();
             rt1 = __builtin_amdgcn_s_memrealtime();
         }
+        // no scalar memory result pending at the first step: such results return
+        // out of order, and one in flight would make every wait for a fragment
+        // read in the step a wait for all of them
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
         for (int st = 0; st < nsteps - 1; ++st) step(st, std::false_type{});
         // (with an empty K slice, stage 0 holds the zeros of out-of-range loads)
         step(nsteps > 0 ? nsteps - 1 : 0, std::true_type{});
