@@ -95,33 +95,56 @@ def _regs(operands):
 
 def _check_transposing_reads(src):
     """The tiled kernel issues its transposing LDS reads from inline assembly,
-    which the compiler's wait insertion does not see: until an lgkmcnt(0) wait,
-    the destination registers of such a read are still being written.  Scan the
-    device assembly of `src` and return every instruction that touches one of
-    those registers before that wait (an instruction that would read a value not
-    yet landed, or write a register the read will overwrite)."""
+    which the compiler's wait insertion does not see: until a wait covers such a
+    read, its destination registers are still being written.  LDS operations
+    complete in order, so while a read is in flight so is every later LDS
+    operation, and the counter (which also counts scalar memory reads) is above
+    their number: an lgkmcnt(N) wait covers every read followed by at least N
+    later LDS operations.  Scan the device assembly of `src` in program order and return every
+    instruction that touches a register of a read not yet covered (one that
+    would read a value not yet landed, or write a register the read will
+    overwrite)."""
     path = os.path.join(CSRC, src)
     cmd = [HIPCC, *DEVICE, *COMMON, "-x", "hip", "--cuda-device-only", "-S", path, "-o", "-"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"assembling {src} failed:\n{r.stderr}")
-    bad, pend, kernel = [], set(), None
-    for line in r.stdout.splitlines():
+    return scan_transposing_reads(r.stdout)
+
+
+def scan_transposing_reads(asm):
+    """The scan of _check_transposing_reads over device assembly text."""
+    bad, kernel = [], None
+    pend = []           # [registers, LDS operations issued after the read]
+    for line in asm.splitlines():
         if re.match(r"^_ZN\w+:", line):
-            kernel, pend = line.split(":")[0], set()
+            kernel, pend = line.split(":")[0], []
             continue
         t = line.strip()
         if not t or t.startswith((";", ".")) or kernel is None:
             continue
         op = t.split()[0]
-        if op == "s_waitcnt" and "lgkmcnt(0)" in t:
-            pend = set()
+        if op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", t)
+            if m:
+                n = int(m.group(1))
+                pend = [e for e in pend if e[1] < n]
             continue
         operands = t.split(";")[0][len(op):]
+        regs = set().union(*(e[0] for e in pend)) if pend else set()
         if op.startswith("ds_read_b64_tr"):
-            pend |= _regs(operands.split(",")[0])
-        elif pend & _regs(operands):
+            dst = _regs(operands.split(",")[0])
+            if regs & _regs(operands):
+                bad.append(f"{kernel}: {t}")
+            for e in pend:
+                e[1] += 1
+            pend.append([dst, 0])
+            continue
+        if regs & _regs(operands):
             bad.append(f"{kernel}: {t}")
+        if op.startswith("ds_"):
+            for e in pend:
+                e[1] += 1
     return bad
 
 

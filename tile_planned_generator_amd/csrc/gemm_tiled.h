@@ -715,9 +715,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
                                                           c, 0, 0, 0);
         }
     };
+    // (A rows of half 0 first, in their read order)
     auto mfmas16 = [&](const Frag16 &f) {
 #pragma unroll
-        for (int q = 0; q < 4 * FM * FN; ++q) mfma16(f, q);
+        for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+                for (int b = 0; b < 2 * FN; ++b) mfma16(f, ((mi * 2 + sm) * FN + (b >> 1)) * 2 + (b & 1));
     };
     // e2m1: the compute phase decodes the B blocks one at a time, in four
     // pieces of two instructions (two conversions, or two fp16 products with
@@ -835,9 +840,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // memory phase: the fragment reads of stage st, with the loads of
             // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
             // to different units)
-            if constexpr (M16 && IS_E2M1) {
-                // the code words and scales first: block 0's decode and the
-                // first MFMAs need them before the later A rows
+            if constexpr (M16 && (IS_E2M1 || B_TR)) {
+                // the B reads first (e2m1: code words and scales, which block
+                // 0's decode needs; row-major B: the transposing reads, which one
+                // wait then covers), then the A rows of half 0 and of half 1, in
+                // the order of the MFMAs that take them
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -874,9 +881,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // wave (in its memory phase) does not delay the MFMA issue
             __builtin_amdgcn_s_setprio(1);
             if constexpr (M16) {
-                // (reads the compiler cannot see, the transposing ones, are
-                // waited for here; it waits for its own ones where they are used)
-                if constexpr (B_TR) __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+                // (reads the compiler cannot see, the transposing ones, issued
+                // before the 2 FM A reads, are waited for here; it waits for its
+                // own ones where they are used)
+                if constexpr (B_TR) __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 2 * FM));
                 tie16(fr);
                 if constexpr (LAST) keep16(fr, nfull == nsteps);
             }
