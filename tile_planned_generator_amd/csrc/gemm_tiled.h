@@ -642,12 +642,6 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             f.b[h][ni] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
     };
-    auto read_frag16 = [&](int buf, int h, Frag16 &f) {
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi) read_a16(buf, h, mi, f);
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) read_b16(buf, h, ni, f);
-    };
     // (as settle / tie for the 32x32 fragments)
     auto tie16 = [&](Frag16 &f) {
         if constexpr (B_TR) {
@@ -840,7 +834,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
             // memory phase: the fragment reads of stage st, with the loads of
             // stage st+NBUF-1 issued between them (LDS reads and buffer loads go
             // to different units)
-            if constexpr (M16 && (IS_E2M1 || B_TR)) {
+            if constexpr (M16) {
                 // the B reads first (e2m1: code words and scales, which block
                 // 0's decode needs; row-major B: the transposing reads, which one
                 // wait then covers), then the A rows of half 0 and of half 1, in
@@ -855,16 +849,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
 #pragma unroll
                 for (int mi = 0; mi < FM; ++mi) read_a16(buf, 1, mi, fr);
                 if constexpr (!LAST) load_stage(st + AHEAD, 1);
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
-            } else if constexpr (M16) {
-                read_frag16(buf, 0, fr);
-                if constexpr (!LAST) load_stage(st + AHEAD, 0);
-                read_frag16(buf, 1, fr);
-                if constexpr (!LAST) load_stage(st + AHEAD, 1);
                 // only the direct loads are waited for before the barrier: the
                 // fragment reads land while the other group's last MFMAs run,
-                // and are waited for at the start of the compute phase (stage
-                // st's buffer is refilled only after the next barrier)
+                // and are waited for in the compute phase (stage st's buffer is
+                // refilled only after the next barrier)
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm((AHEAD - 1) * LPS, 15));
             } else {
                 read_frag(buf, S0{}, f0, g0 + st);
