@@ -806,7 +806,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) gemm_tiled_kernel(TiledArgs p)
         // may be refilled by any phase that starts at or after barrier 2st+3.
         // The memory phase of step st issues the loads of stage st+NBUF-1, into
         // the buffer of stage st-1, and its wait leaves the NBUF-2 stages after
-        // stage st+1 in flight.
+        // stage st+1 in flight.  With 16x16 MFMAs that wait is for the direct
+        // loads only: the phase's fragment reads (B, then the A rows of each
+        // half) are waited for in the compute phase, each before the first
+        // MFMA that takes it.
         const bool lag = wave >= 4;
         auto bar = [] {
             __builtin_amdgcn_sched_barrier(0);
