@@ -267,20 +267,27 @@ TILED_SOURCES = ["gemm_tiled.h", "gemm_tiled_i8.hip", "kcommon.h", "catalogue.h"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
-def tiled_source_hash():
-    """Hash of the tiled kernel's code: its sources with comments and
-    whitespace runs removed, so that a comment edit keeps the recorded
-    counters while any change to the code drops them."""
+def code_hash(texts):
+    """Hash of source texts with comments and whitespace runs removed: a
+    comment edit keeps it, any change to the code changes it."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in TILED_SOURCES:
-        with open(os.path.join(ROOT, "tile_planned_generator_amd", "csrc", f), encoding="utf-8") as fh:
-            text = fh.read()
+    for text in texts:
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def tiled_source_hash():
+    """code_hash of the tiled kernel's sources: the recorded HBM counters stay
+    valid while it matches."""
+    texts = []
+    for f in TILED_SOURCES:
+        with open(os.path.join(ROOT, "tile_planned_generator_amd", "csrc", f), encoding="utf-8") as fh:
+            texts.append(fh.read())
+    return code_hash(texts)
 
 
 def recorded_traffic(workload):
